@@ -1,0 +1,331 @@
+/*
+ * oracle.c -- plain FP64 CPU reference for block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the GPU library: every decoder below is
+ * written out from the closed forms of the element formats.
+ *
+ * What it computes (the plain definition of the method):
+ *
+ *     D[m,n] = sum_k  a(m,k) * b(n,k)
+ *
+ * where a and b are the dequantized operands.  Block scaling is only an
+ * encoding of a and b; the method ("Add FlyDSL grouped groupwise FP8 GEMM for
+ * ROCm", section "Architecture support"; "PyTorch on AMD GPUs gains a FlyDSL
+ * backend", section "Interpretation") reaches this same sum with FP32
+ * accumulation on matrix cores.  Here every dequantized value and every
+ * product is formed in FP64 and summed in FP64 in plain k order, with no
+ * blocking and no reordering.
+ *
+ * Element formats (OCP Microscaling Formats MX v1.0; external to the pages,
+ * which only name the formats -- "Experimental FlyDSL GEMM backend for TE
+ * PyTorch", section "Supported Data Types"; "PyTorch on AMD GPUs gains a
+ * FlyDSL backend", section "Interpretation"):
+ *   E4M3: bias 7, no infinities, S.1111.111 is NaN, max 448.
+ *   E5M2: bias 15, IEEE-like: exponent 31 is Inf (m=0) or NaN.
+ *   E2M1: bias 1, no Inf/NaN, values {0,.5,1,1.5,2,3,4,6}.
+ *   E8M0: 2^(c-127); c=255 is NaN.
+ *
+ * Parity status: every function here is pinned by CPU tests (closed forms,
+ * an independent library decoder, exact rational brute force, one-hot and
+ * identity inputs, exact scale doubling, reduction to a library matmul).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+/* Element-format selectors for this file (the oracle's own numbering). */
+#define ORC_E4M3 0
+#define ORC_E5M2 1
+#define ORC_E2M1 4
+
+/* Scale kinds. */
+#define ORC_SCALE_MX     0   /* one E8M0 byte per 32 consecutive K values   */
+#define ORC_SCALE_TENSOR 1   /* one FP32 dequant multiplier for the tensor  */
+
+/* ---- element decoders (closed forms) ---------------------------------- */
+
+double oracle_decode_e4m3(unsigned c)
+{
+    unsigned s = (c >> 7) & 1u, e = (c >> 3) & 15u, m = c & 7u;
+    double v;
+    if (e == 15u && m == 7u) return NAN;           /* the only NaN pattern */
+    if (e == 0u) v = ldexp((double)m, -9);          /* subnormal: m * 2^-9  */
+    else v = ldexp((double)(8u + m), (int)e - 10);  /* (1+m/8) * 2^(e-7)    */
+    return s ? -v : v;
+}
+
+double oracle_decode_e5m2(unsigned c)
+{
+    unsigned s = (c >> 7) & 1u, e = (c >> 2) & 31u, m = c & 3u;
+    double v;
+    if (e == 31u) {
+        if (m == 0u) return s ? -INFINITY : INFINITY;
+        return NAN;
+    }
+    if (e == 0u) v = ldexp((double)m, -16);         /* m * 2^-16            */
+    else v = ldexp((double)(4u + m), (int)e - 17);  /* (1+m/4) * 2^(e-15)   */
+    return s ? -v : v;
+}
+
+double oracle_decode_e2m1(unsigned nib)
+{
+    unsigned s = (nib >> 3) & 1u, e = (nib >> 1) & 3u, m = nib & 1u;
+    double v;
+    if (e == 0u) v = 0.5 * (double)m;               /* subnormal: m * 2^-1  */
+    else v = ldexp((double)(2u + m), (int)e - 2);   /* (1+m/2) * 2^(e-1)    */
+    return s ? -v : v;
+}
+
+double oracle_decode_e8m0(unsigned c)
+{
+    c &= 255u;
+    if (c == 255u) return NAN;
+    return ldexp(1.0, (int)c - 127);
+}
+
+double oracle_decode(int fmt, unsigned code)
+{
+    switch (fmt) {
+    case ORC_E4M3: return oracle_decode_e4m3(code & 255u);
+    case ORC_E5M2: return oracle_decode_e5m2(code & 255u);
+    case ORC_E2M1: return oracle_decode_e2m1(code & 15u);
+    default: return NAN;
+    }
+}
+
+/* ---- operand element access -------------------------------------------
+ *
+ * An operand is a logical [rows, K] matrix (rows = M for A, N for B).
+ * Storage:
+ *   transposed == 0 : codes row-major [rows, K]   (K contiguous)
+ *   transposed == 1 : codes row-major [K, rows]   (rows contiguous)
+ * For E2M1, two codes share a byte along the contiguous dimension; the
+ * element with the even index sits in the low nibble (bits 3:0).
+ * MX scales are always blocked along K and stored [rows, K/32] row-major,
+ * whatever the code layout ("[gfx1250] Add MXFP4 GEMM support to FlyDSL
+ * backend", review thread: rowwise and columnwise copies each carry their
+ * own K-blocked scales).  Tensor scales are one float.
+ */
+typedef struct {
+    int fmt;             /* ORC_E4M3 / ORC_E5M2 / ORC_E2M1 */
+    int scale_kind;      /* ORC_SCALE_MX / ORC_SCALE_TENSOR */
+    int transposed;
+    const uint8_t *codes;
+    const void *scales;
+    int64_t rows, K;
+} orc_operand;
+
+static unsigned orc_code(const orc_operand *op, int64_t r, int64_t k)
+{
+    int64_t idx, ld;
+    if (!op->transposed) { idx = r * op->K + k; ld = idx; }
+    else { idx = k * op->rows + r; ld = idx; }
+    if (op->fmt == ORC_E2M1) {
+        uint8_t byte = op->codes[ld / 2];
+        return (ld & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
+    }
+    return op->codes[ld];
+}
+
+static double orc_scale(const orc_operand *op, int64_t r, int64_t k)
+{
+    if (op->scale_kind == ORC_SCALE_TENSOR)
+        return (double)*(const float *)op->scales;
+    return oracle_decode_e8m0(((const uint8_t *)op->scales)[r * (op->K / 32) + k / 32]);
+}
+
+/* Dequantized value a(r,k) = decode(code) * scale. */
+static double orc_value(const orc_operand *op, int64_t r, int64_t k)
+{
+    return oracle_decode(op->fmt, orc_code(op, r, k)) * orc_scale(op, r, k);
+}
+
+/* Dequantize a whole operand into a row-major [rows, K] FP64 matrix. */
+int oracle_dequant(int fmt, int scale_kind, int transposed,
+                   const uint8_t *codes, const void *scales,
+                   int64_t rows, int64_t K, double *out)
+{
+    orc_operand op = {fmt, scale_kind, transposed, codes, scales, rows, K};
+    int64_t r;
+    if (scale_kind == ORC_SCALE_MX && K % 32 != 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = orc_value(&op, r, k);
+    return 0;
+}
+
+/* ---- dense GEMM: D = sum_k a(m,k) b(n,k) --------------------------------
+ * A is [M,K]-logical, B is [N,K]-logical (each possibly stored transposed).
+ * Dequantize both, then the textbook triple loop in FP64.  D is FP64 [M,N].
+ * Scratch: caller passes workspace of (M+N)*K doubles.
+ */
+int oracle_gemm(int fmtA, int skA, int trA, const uint8_t *A, const void *sA,
+                int fmtB, int skB, int trB, const uint8_t *B, const void *sB,
+                int64_t M, int64_t N, int64_t K, double *work, double *D)
+{
+    double *a = work, *b = work + M * K;
+    int64_t m;
+    if (oracle_dequant(fmtA, skA, trA, A, sA, M, K, a)) return -1;
+    if (oracle_dequant(fmtB, skB, trB, B, sB, N, K, b)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            const double *ar = a + m * K, *br = b + n * K;
+            for (int64_t k = 0; k < K; ++k) acc += ar[k] * br[k];
+            D[m * N + n] = acc;
+        }
+    }
+    return 0;
+}
+
+/* Selected entries D[idx_m[i], idx_n[i]], each a direct sum over k with the
+ * operands decoded on the fly.  For spot checks at sizes where the full
+ * product is out of reach. */
+int oracle_gemm_entries(int fmtA, int skA, int trA, const uint8_t *A, const void *sA,
+                        int fmtB, int skB, int trB, const uint8_t *B, const void *sB,
+                        int64_t M, int64_t N, int64_t K,
+                        const int64_t *idx_m, const int64_t *idx_n, int64_t count,
+                        double *out)
+{
+    orc_operand a = {fmtA, skA, trA, A, sA, M, K};
+    orc_operand b = {fmtB, skB, trB, B, sB, N, K};
+    int64_t i;
+    if ((skA == ORC_SCALE_MX || skB == ORC_SCALE_MX) && K % 32 != 0) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += orc_value(&a, idx_m[i], k) * orc_value(&b, idx_n[i], k);
+        out[i] = acc;
+    }
+    return 0;
+}
+
+/* ---- grouped groupwise GEMM ---------------------------------------------
+ * "Add FlyDSL grouped groupwise FP8 GEMM for ROCm" (PR body; commit on the
+ * activation-scale layout):
+ *   - G groups of rows, sizes m_sizes[g]; group g owns rows
+ *     [start_g, start_g + m_sizes[g]) with start_g = sum_{h<g} m_sizes[h].
+ *   - XQ is E4M3 [totM, K]; WQ is E4M3 [G, N, K] (plain row-major).
+ *   - Activation scales: one FP32 per row per 128-K block, stored in the
+ *     per-group block layout: group g's block begins at start_g * (K/128)
+ *     and holds (local row i, k-block kb) at offset i + kb * m_sizes[g].
+ *   - Weight scales: one FP32 per 128x128 block of W[g], stored
+ *     [G, N/128, K/128] row-major (the pages give the granularity only).
+ *   - N and K must be multiples of 128.
+ * a(r,k) = dec(XQ[r,k]) * xs(r,k),  b_g(n,k) = dec(WQ[g,n,k]) * ws[g,n/128,k/128]
+ * D[r,n] = sum_k a(r,k) * b_g(n,k) for r in group g.  Rows that belong to no
+ * group are not written.
+ */
+static double orc_xs(const float *xs, int64_t start, int64_t mg, int64_t K,
+                     int64_t local, int64_t kb)
+{
+    return (double)xs[start * (K / 128) + local + kb * mg];
+}
+
+int oracle_grouped_gemm(int G, const int64_t *m_sizes,
+                        const uint8_t *XQ, const float *xs,
+                        const uint8_t *WQ, const float *ws,
+                        int64_t totM, int64_t N, int64_t K, double *D)
+{
+    int64_t start = 0;
+    if (N % 128 != 0 || K % 128 != 0) return -1;
+    for (int g = 0; g < G; ++g) {
+        int64_t mg = m_sizes[g], i;
+        if (mg < 0 || start + mg > totM) return -2;
+        const uint8_t *W = WQ + (int64_t)g * N * K;
+        const float *wsg = ws + (int64_t)g * (N / 128) * (K / 128);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (i = 0; i < mg; ++i) {
+            int64_t r = start + i;
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double av = oracle_decode_e4m3(XQ[r * K + k]) * orc_xs(xs, start, mg, K, i, k / 128);
+                    double bv = oracle_decode_e4m3(W[n * K + k]) * (double)wsg[(n / 128) * (K / 128) + k / 128];
+                    acc += av * bv;
+                }
+                D[r * N + n] = acc;
+            }
+        }
+        start += mg;
+    }
+    return 0;
+}
+
+/* Selected entries of the grouped product.  Row r's group is found by
+ * walking m_sizes; a row in no group yields NaN. */
+int oracle_grouped_entries(int G, const int64_t *m_sizes,
+                           const uint8_t *XQ, const float *xs,
+                           const uint8_t *WQ, const float *ws,
+                           int64_t totM, int64_t N, int64_t K,
+                           const int64_t *idx_m, const int64_t *idx_n, int64_t count,
+                           double *out)
+{
+    int64_t i;
+    if (N % 128 != 0 || K % 128 != 0) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        int64_t r = idx_m[i], n = idx_n[i], start = 0, mg = 0;
+        int g, found = -1;
+        for (g = 0; g < G; ++g) {
+            mg = m_sizes[g];
+            if (r >= start && r < start + mg) { found = g; break; }
+            start += mg;
+        }
+        if (found < 0 || r >= totM) { out[i] = NAN; continue; }
+        const uint8_t *W = WQ + (int64_t)found * N * K;
+        const float *wsg = ws + (int64_t)found * (N / 128) * (K / 128);
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double av = oracle_decode_e4m3(XQ[r * K + k]) * orc_xs(xs, start, mg, K, r - start, k / 128);
+            double bv = oracle_decode_e4m3(W[n * K + k]) * (double)wsg[(n / 128) * (K / 128) + k / 128];
+            acc += av * bv;
+        }
+        out[i] = acc;
+    }
+    return 0;
+}
+
+/* ---- BF16 round-to-nearest-even of an FP64 value ------------------------
+ * BF16 keeps 8 significant bits (1 implicit + 7 stored), exponent range as
+ * FP32.  Rounds the exact FP64 value once (no intermediate FP32 step).
+ * Overflow goes to +-Inf; NaN maps to the canonical quiet NaN 0x7FC0.
+ */
+uint16_t oracle_bf16_rne(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    double ax = fabs(x);
+    int e;
+    if (isnan(x)) return 0x7FC0u;
+    if (ax == 0.0) return sign;
+    if (isinf(x)) return (uint16_t)(sign | 0x7F80u);
+    frexp(ax, &e);                     /* ax = f * 2^e, f in [0.5, 1)      */
+    /* unit in the last place of a BF16 number with this exponent: normal
+     * numbers have 8 significant bits -> ulp = 2^(e-8); below 2^-126 the
+     * spacing is fixed at 2^-133 (subnormal). */
+    int ulp_exp = e - 8;
+    if (ulp_exp < -133) ulp_exp = -133;
+    double q = ldexp(ax, -ulp_exp);    /* exact scaling by a power of two   */
+    double fl = floor(q), rem = q - fl;
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = ldexp(fl, ulp_exp);
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+    /* encode r (exactly representable in BF16) */
+    {
+        float f = (float)r;            /* exact: r has <= 8 significant bits */
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        return (uint16_t)(sign | ((u >> 16) & 0x7FFFu));
+    }
+}
+
+void oracle_bf16_rne_array(const double *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(x[i]);
+}
