@@ -1,0 +1,317 @@
+// C ABI of the gfx950 block-scaled GEMM library: argument validation, tile
+// and grid selection from static shapes, and kernel launch.  The host never
+// reads device memory; every call enqueues exactly one kernel on the caller's
+// stream or returns an error before enqueueing anything.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/mxgemm.h"
+#include "dense.hpp"
+#include "grouped.hpp"
+#include "preshuffle.hpp"
+
+using namespace mxg;
+
+namespace {
+
+struct FmtInfo {
+  bool ok;
+  bool mx;      // E8M0 block scales (else one FP32 per tensor)
+  int elem;     // F_E4M3 / F_E5M2 / F_E2M1
+};
+
+FmtInfo fmt_info(int f) {
+  switch (f) {
+    case MXG_MXFP8_E4M3: return {true, true, F_E4M3};
+    case MXG_MXFP8_E5M2: return {true, true, F_E5M2};
+    case MXG_MXFP4_E2M1: return {true, true, F_E2M1};
+    case MXG_FP8_E4M3_TENSOR: return {true, false, F_E4M3};
+    case MXG_FP8_E5M2_TENSOR: return {true, false, F_E5M2};
+    default: return {false, false, 0};
+  }
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Largest operand extents the 32-bit in-kernel offsets support.
+constexpr int64_t MAX_ROW_BYTES = 1ll << 22;   // bytes of K per row (256 rows < 2^30)
+constexpr int64_t MAX_DIM = 1ll << 31;
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MXG_OK : MXG_ERR_HIP;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" const char *mxgemm_status_string(int s) {
+  switch (s) {
+    case MXG_OK: return "ok";
+    case MXG_ERR_INVALID_ARG: return "invalid argument";
+    case MXG_ERR_UNSUPPORTED: return "unsupported format, layout or shape";
+    case MXG_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case MXG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int mxgemm_init(void) {
+  // Touch the device so the code object is loaded before any graph capture.
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXG_ERR_HIP;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, (const void *)dense_kernel<F_E4M3, F_E4M3, SM_MX, false, false, false>) != hipSuccess)
+    return MXG_ERR_HIP;
+  return MXG_OK;
+}
+
+extern "C" int mxgemm_validate(int fmtA, int fmtB, int layout, const void *A, const void *sA,
+                    const void *B, const void *sB, const void *D, int64_t M, int64_t N,
+                    int64_t K) {
+  const bool psb = (fmtB & MXG_PRESHUFFLED) != 0;
+  const FmtInfo fa = fmt_info(fmtA), fb = fmt_info(fmtB & ~MXG_PRESHUFFLED);
+  if (!fa.ok || !fb.ok) return MXG_ERR_INVALID_ARG;
+  if (layout != MXG_NT && layout != MXG_NN && layout != MXG_TN) return MXG_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (M >= MAX_DIM || N >= MAX_DIM) return MXG_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return MXG_OK;
+  if (!D) return MXG_ERR_INVALID_ARG;
+  if (!aligned(D, 16)) return MXG_ERR_MISALIGNED;
+  if (K == 0) return MXG_OK;
+  if (!A || !B || !sA || !sB) return MXG_ERR_INVALID_ARG;
+  if (fa.mx != fb.mx) return MXG_ERR_UNSUPPORTED;
+  if ((fa.elem == F_E2M1) != (fb.elem == F_E2M1)) return MXG_ERR_UNSUPPORTED;
+  const bool fp4 = fa.elem == F_E2M1;
+  if (fp4 && layout != MXG_NT) return MXG_ERR_UNSUPPORTED;
+  if (psb && layout != MXG_NT) return MXG_ERR_UNSUPPORTED;
+  if (K % (fp4 ? 256 : 128) != 0) return MXG_ERR_UNSUPPORTED;
+  const int64_t kb = fp4 ? K / 2 : K;
+  if (kb > MAX_ROW_BYTES) return MXG_ERR_UNSUPPORTED;
+  if (layout == MXG_TN && (M % 16 != 0 || M * 128 >= (1ll << 31))) return MXG_ERR_UNSUPPORTED;
+  if ((layout == MXG_TN || layout == MXG_NN) && (N % 16 != 0 || N * 128 >= (1ll << 31)))
+    return MXG_ERR_UNSUPPORTED;
+  if (fa.mx && (M * (K / 32) >= (1ll << 31) || cdiv(N, 16) * 16 * (K / 32) >= (1ll << 31)))
+    return MXG_ERR_UNSUPPORTED;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, fa.mx ? 16 : 4) || !aligned(sB, fb.mx ? 16 : 4))
+    return MXG_ERR_MISALIGNED;
+  return MXG_OK;
+}
+
+namespace {
+// Kernel selection for the dense path.
+typedef void (*dense_fn)(DenseArgs);
+
+template <int FA, int FB>
+dense_fn pick_layout(bool mx, int layout, bool psb) {
+  if (mx) {
+    if (layout != MXG_NT) return nullptr;
+    return psb ? dense_kernel<FA, FB, SM_MX, false, false, true>
+               : dense_kernel<FA, FB, SM_MX, false, false, false>;
+  }
+  if constexpr (FA == F_E2M1 || FB == F_E2M1) {
+    return nullptr;
+  } else {
+    switch (layout) {
+      case MXG_NT:
+        return psb ? dense_kernel<FA, FB, SM_TENSOR, false, false, true>
+                   : dense_kernel<FA, FB, SM_TENSOR, false, false, false>;
+      case MXG_NN: return dense_kernel<FA, FB, SM_TENSOR, false, true, false>;
+      case MXG_TN: return dense_kernel<FA, FB, SM_TENSOR, true, true, false>;
+      default: return nullptr;
+    }
+  }
+}
+
+dense_fn pick_dense(int ea, int eb, bool mx, int layout, bool psb) {
+  if (ea == F_E2M1 && eb == F_E2M1) return mx ? pick_layout<F_E2M1, F_E2M1>(true, layout, psb) : nullptr;
+  if (ea == F_E4M3 && eb == F_E4M3) return pick_layout<F_E4M3, F_E4M3>(mx, layout, psb);
+  if (ea == F_E4M3 && eb == F_E5M2) return pick_layout<F_E4M3, F_E5M2>(mx, layout, psb);
+  if (ea == F_E5M2 && eb == F_E4M3) return pick_layout<F_E5M2, F_E4M3>(mx, layout, psb);
+  if (ea == F_E5M2 && eb == F_E5M2) return pick_layout<F_E5M2, F_E5M2>(mx, layout, psb);
+  return nullptr;
+}
+
+__global__ void zero_bf16_kernel(uint16_t *D, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) D[i] = 0;
+}
+}  // namespace
+
+extern "C" int mxgemm_run(int fmtA, int fmtB, int layout, const void *A, const void *sA, const void *B,
+               const void *sB, void *D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int v = mxgemm_validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K);
+  if (v != MXG_OK) return v;
+  if (M == 0 || N == 0) return MXG_OK;
+  if (K == 0) {
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(zero_bf16_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
+                       (uint16_t *)D, n);
+    return launch_status();
+  }
+  const bool psb = (fmtB & MXG_PRESHUFFLED) != 0;
+  const FmtInfo fa = fmt_info(fmtA), fb = fmt_info(fmtB & ~MXG_PRESHUFFLED);
+  dense_fn fn = pick_dense(fa.elem, fb.elem, fa.mx, layout, psb);
+  if (!fn) return MXG_ERR_UNSUPPORTED;
+  const bool fp4 = fa.elem == F_E2M1;
+  DenseArgs a;
+  a.A = (const uint8_t *)A;
+  a.B = (const uint8_t *)B;
+  a.sA = sA;
+  a.sB = sB;
+  a.D = (uint16_t *)D;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.a_bytes = fp4 ? M * K / 2 : M * K;
+  a.b_bytes = psb ? mxgemm_preshuffle_b_bytes(fmtB & ~MXG_PRESHUFFLED, N, K) : (fp4 ? N * K / 2 : N * K);
+  a.sa_bytes = fa.mx ? M * (K / 32) : 4;
+  a.sb_bytes = fb.mx ? (psb ? mxgemm_preshuffle_scales_bytes(N, K) : N * (K / 32)) : 4;
+  a.tiles_m = (int)cdiv(M, DBM);
+  a.tiles_n = (int)cdiv(N, DBN);
+  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return launch_status();
+}
+
+extern "C" int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
+                              const void *WQ, const float *w_scale, const void *D, int64_t totM,
+                              int64_t N, int64_t K, int b_preshuffled) {
+  (void)b_preshuffled;
+  if (G < 1 || G > MXG_GROUPED_MAX_G) return MXG_ERR_UNSUPPORTED;
+  if (totM < 0 || N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (!m_sizes) return MXG_ERR_INVALID_ARG;
+  if (N % 128 != 0 || K % 128 != 0) return MXG_ERR_UNSUPPORTED;
+  if (totM >= MAX_DIM || N >= MAX_DIM || K > MAX_ROW_BYTES) return MXG_ERR_UNSUPPORTED;
+  if (totM * (K / 128) * 4 >= (1ll << 31)) return MXG_ERR_UNSUPPORTED;
+  if (totM == 0 || N == 0) return MXG_OK;
+  if (!D) return MXG_ERR_INVALID_ARG;
+  if (!aligned(D, 16) || !aligned(m_sizes, 8)) return MXG_ERR_MISALIGNED;
+  if (K == 0) return MXG_OK;
+  if (!XQ || !x_scale || !WQ || !w_scale) return MXG_ERR_INVALID_ARG;
+  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4))
+    return MXG_ERR_MISALIGNED;
+  return MXG_OK;
+}
+
+namespace {
+__global__ void grouped_zero_kernel(const int64_t *m_sizes, int G, uint16_t *D, int64_t totM,
+                                    int64_t N) {
+  // K == 0: every row that belongs to a group becomes zero.
+  int64_t covered = 0;
+  for (int g = 0; g < G; ++g) {
+    int64_t s = m_sizes[g];
+    const int64_t room = totM - covered;
+    covered += s < 0 ? 0 : (s > room ? room : s);
+  }
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < covered * N) D[i] = 0;
+}
+}  // namespace
+
+extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
+                         const void *WQ, const float *w_scale, void *D, int64_t totM, int64_t N,
+                         int64_t K, int b_preshuffled, hipStream_t stream) {
+  const int v = grouped_fp8_gemm_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K,
+                                          b_preshuffled);
+  if (v != MXG_OK) return v;
+  if (totM == 0 || N == 0) return MXG_OK;
+  if (K == 0) {
+    hipLaunchKernelGGL(grouped_zero_kernel, dim3((unsigned)cdiv(totM * N, 256)), dim3(256), 0,
+                       stream, m_sizes, G, (uint16_t *)D, totM, N);
+    return launch_status();
+  }
+  constexpr int BM = 128, BN = 128;
+  GroupedArgs a;
+  a.m_sizes = m_sizes;
+  a.XQ = (const uint8_t *)XQ;
+  a.WQ = (const uint8_t *)WQ;
+  a.xs = x_scale;
+  a.ws = w_scale;
+  a.D = (uint16_t *)D;
+  a.totM = totM;
+  a.N = N;
+  a.K = K;
+  a.G = G;
+  a.tiles_n = (int)(N / BN);
+  const int64_t tiles_m = cdiv(totM, BM) + G - 1;
+  const int64_t blocks = tiles_m * a.tiles_n;
+  if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  if (b_preshuffled)
+    hipLaunchKernelGGL((grouped_kernel<BM, BN, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((grouped_kernel<BM, BN, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return launch_status();
+}
+
+extern "C" int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K) {
+  const FmtInfo f = fmt_info(fmtB & ~MXG_PRESHUFFLED);
+  if (!f.ok || N < 0 || K < 0 || K % 128 != 0) return -1;
+  const int64_t nt = cdiv(N, 16), nks = K / 128;
+  return nt * nks * (f.elem == F_E2M1 ? 1024 : 2048);
+}
+
+extern "C" int mxgemm_preshuffle_b(int fmtB, int layout, const void *B, void *B_out, int64_t N, int64_t K,
+                        hipStream_t stream) {
+  const FmtInfo f = fmt_info(fmtB & ~MXG_PRESHUFFLED);
+  if (!f.ok || N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (layout != MXG_NT && layout != MXG_NN && layout != MXG_TN) return MXG_ERR_INVALID_ARG;
+  const bool fp4 = f.elem == F_E2M1;
+  const bool tb = layout != MXG_NT;   // B stored [K, N]
+  if (K % (fp4 ? 256 : 128) != 0) return MXG_ERR_UNSUPPORTED;
+  if (fp4 && tb) return MXG_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return MXG_OK;
+  if (!B || !B_out) return MXG_ERR_INVALID_ARG;
+  if (!aligned(B, 16) || !aligned(B_out, 16)) return MXG_ERR_MISALIGNED;
+  const int64_t chunks = mxgemm_preshuffle_b_bytes(fmtB, N, K) / 16;
+  const unsigned grid = (unsigned)cdiv(chunks, 256);
+  if (fp4)
+    hipLaunchKernelGGL((preshuffle_b_kernel<true, false>), dim3(grid), dim3(256), 0, stream,
+                       (const uint8_t *)B, (uint8_t *)B_out, N, K, chunks);
+  else if (tb)
+    hipLaunchKernelGGL((preshuffle_b_kernel<false, true>), dim3(grid), dim3(256), 0, stream,
+                       (const uint8_t *)B, (uint8_t *)B_out, N, K, chunks);
+  else
+    hipLaunchKernelGGL((preshuffle_b_kernel<false, false>), dim3(grid), dim3(256), 0, stream,
+                       (const uint8_t *)B, (uint8_t *)B_out, N, K, chunks);
+  return launch_status();
+}
+
+extern "C" int64_t mxgemm_preshuffle_scales_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || K % 32 != 0) return -1;
+  return cdiv(rows, 16) * cdiv(K, 512) * 256;
+}
+
+extern "C" int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K,
+                             hipStream_t stream) {
+  if (rows < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MXG_ERR_UNSUPPORTED;
+  if (rows == 0 || K == 0) return MXG_OK;
+  if (!s || !s_out) return MXG_ERR_INVALID_ARG;
+  if (!aligned(s, 4) || !aligned(s_out, 16)) return MXG_ERR_MISALIGNED;
+  const int64_t words = mxgemm_preshuffle_scales_bytes(rows, K) / 4;
+  hipLaunchKernelGGL(preshuffle_scales_kernel, dim3((unsigned)cdiv(words, 256)), dim3(256), 0,
+                     stream, (const uint8_t *)s, (uint32_t *)s_out, rows, K, words);
+  return launch_status();
+}
+
+extern "C" int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out, int64_t N, int64_t K,
+                             hipStream_t stream) {
+  if (G < 1 || G > MXG_GROUPED_MAX_G || N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (N % 128 != 0 || K % 128 != 0) return MXG_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return MXG_OK;
+  if (!WQ || !WQ_out) return MXG_ERR_INVALID_ARG;
+  if (!aligned(WQ, 16) || !aligned(WQ_out, 16)) return MXG_ERR_MISALIGNED;
+  // Each group's [N, K] block maps to a same-size preshuffled block; the
+  // whole [G*N, K] stack is one B operand whose 16-row tiles never straddle
+  // two groups (N % 16 == 0).
+  const int64_t chunks = (int64_t)G * N * K / 16;
+  hipLaunchKernelGGL((preshuffle_b_kernel<false, false>), dim3((unsigned)cdiv(chunks, 256)),
+                     dim3(256), 0, stream, (const uint8_t *)WQ, (uint8_t *)WQ_out,
+                     (int64_t)G * N, K, chunks);
+  return launch_status();
+}
+

@@ -1,0 +1,83 @@
+// Device-side building blocks shared by the gfx950 GEMM kernels: vector
+// types, buffer resources, LDS DMA, the scaled matrix-core instruction and
+// BF16 rounding.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
+// Element-format codes understood by the scaled MFMA's cbsz/blgp fields.
+enum : int { F_E4M3 = 0, F_E5M2 = 1, F_E2M1 = 4 };
+
+// Neutral E8M0 scale (2^0) in every byte.
+constexpr int E8M0_ONE_X4 = 0x7F7F7F7F;
+
+// Buffer resource over [base, base + nbytes): loads past nbytes return 0
+// (checked per dword), stores past it are dropped.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)nbytes, 0x00020000);
+}
+
+__device__ inline uint32_t clamp_records(int64_t remaining) {
+  if (remaining <= 0) return 0;
+  return remaining > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)remaining;
+}
+
+// 16 bytes per lane from global (via the buffer resource) straight into LDS:
+// lane L's data lands at lds_base + 16*L.  lds_base must be wave-uniform.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, (int)voff, 0, 0, 0);
+}
+
+// 4 bytes per lane into LDS at lds_base + 4*L.
+__device__ inline void dma4(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 4, (int)voff, 0, 0, 0);
+}
+
+__device__ inline uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+
+__device__ inline v4i lds_read16(const void *p) {
+  return *(const lds_v4i *)(const __attribute__((address_space(3))) char *)(uintptr_t)(p);
+}
+
+__device__ inline v2i lds_read_tr8(const void *p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_v2i *)((__attribute__((address_space(3))) char *)(uintptr_t)(p)));
+}
+
+// D += sum over a 16x16x128 block: first operand rows = output rows.
+template <int FX, int FY>
+__device__ inline v4f mfma_scaled(const v8i &x, const v8i &y, const v4f &c, int sx, int sy) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, sx, 0, sy);
+}
+
+// FP32 -> BF16 bits, round to nearest even; NaN -> quiet NaN.
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Wait for this wave's outstanding vector-memory loads (including LDS DMA).
+// s_waitcnt simm16 on gfx9: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8];
+// 0x0F70 = vmcnt(0) with expcnt/lgkmcnt left at their maxima.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+}  // namespace mxg

@@ -1,0 +1,142 @@
+"""Thin ctypes binding of libmxgemm.so (C ABI in include/mxgemm.h).
+
+Argument marshalling only: torch tensors are passed as raw device pointers
+plus sizes, and the current HIP stream of torch.  Every step of the GEMM runs
+in the library's kernels; there is no fallback path.  Importing this module
+raises if the library has not been built.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
+
+# Values mirror include/mxgemm.h.
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, -1, -2, -3, -4
+MXFP8_E4M3, MXFP8_E5M2, MXFP4_E2M1 = 0, 1, 4
+FP8_E4M3_TENSOR, FP8_E5M2_TENSOR = 16, 17
+PRESHUFFLED = 0x100
+NT, NN, TN = 0, 1, 2
+GROUPED_MAX_G = 1024
+
+EXPORTS = (
+    "mxgemm_init", "mxgemm_status_string", "mxgemm_run", "mxgemm_validate",
+    "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate",
+    "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
+    "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
+    "grouped_fp8_preshuffle_b",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmxgemm.so is not built (run __graft_entry__.build() or "
+                      "python -m block_scaled_precision_03_amd.csrc.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i, _i64, _p = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+_lib.mxgemm_init.restype = _i
+_lib.mxgemm_init.argtypes = []
+_lib.mxgemm_status_string.restype = ctypes.c_char_p
+_lib.mxgemm_status_string.argtypes = [_i]
+_lib.mxgemm_run.restype = _i
+_lib.mxgemm_run.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]
+_lib.mxgemm_validate.restype = _i
+_lib.mxgemm_validate.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64]
+_lib.grouped_fp8_gemm_run.restype = _i
+_lib.grouped_fp8_gemm_run.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p]
+_lib.grouped_fp8_gemm_validate.restype = _i
+_lib.grouped_fp8_gemm_validate.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i]
+_lib.mxgemm_preshuffle_b_bytes.restype = _i64
+_lib.mxgemm_preshuffle_b_bytes.argtypes = [_i, _i64, _i64]
+_lib.mxgemm_preshuffle_b.restype = _i
+_lib.mxgemm_preshuffle_b.argtypes = [_i, _i, _p, _p, _i64, _i64, _p]
+_lib.mxgemm_preshuffle_scales_bytes.restype = _i64
+_lib.mxgemm_preshuffle_scales_bytes.argtypes = [_i64, _i64]
+_lib.mxgemm_preshuffle_scales.restype = _i
+_lib.mxgemm_preshuffle_scales.argtypes = [_p, _p, _i64, _i64, _p]
+_lib.grouped_fp8_preshuffle_b.restype = _i
+_lib.grouped_fp8_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
+
+
+class MxgemmError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s: %s (%d)" % (what, status_string(status), status))
+        self.status = status
+
+
+def lib():
+    return _lib
+
+
+def status_string(s):
+    return _lib.mxgemm_status_string(int(s)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise MxgemmError(rc, what)
+
+
+def init():
+    _check(_lib.mxgemm_init(), "mxgemm_init")
+
+
+def run(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, stream=None):
+    """D[M,N] (bf16) = sum_k a(m,k) b(n,k); see include/mxgemm.h."""
+    _check(_lib.mxgemm_run(fmtA, fmtB, layout, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(D),
+                           M, N, K, _stream(stream)), "mxgemm_run")
+
+
+def validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K):
+    return _lib.mxgemm_validate(fmtA, fmtB, layout, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB),
+                                _ptr(D), M, N, K)
+
+
+def grouped_run(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_preshuffled=False,
+                stream=None):
+    _check(_lib.grouped_fp8_gemm_run(G, _ptr(m_sizes), _ptr(XQ), _ptr(x_scale), _ptr(WQ),
+                                     _ptr(w_scale), _ptr(D), totM, N, K, int(bool(b_preshuffled)),
+                                     _stream(stream)), "grouped_fp8_gemm_run")
+
+
+def grouped_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_preshuffled=False):
+    return _lib.grouped_fp8_gemm_validate(G, _ptr(m_sizes), _ptr(XQ), _ptr(x_scale), _ptr(WQ),
+                                          _ptr(w_scale), _ptr(D), totM, N, K,
+                                          int(bool(b_preshuffled)))
+
+
+def preshuffle_b_bytes(fmtB, N, K):
+    return _lib.mxgemm_preshuffle_b_bytes(fmtB, N, K)
+
+
+def preshuffle_b(fmtB, layout, B, B_out, N, K, stream=None):
+    _check(_lib.mxgemm_preshuffle_b(fmtB, layout, _ptr(B), _ptr(B_out), N, K, _stream(stream)),
+           "mxgemm_preshuffle_b")
+
+
+def preshuffle_scales_bytes(rows, K):
+    return _lib.mxgemm_preshuffle_scales_bytes(rows, K)
+
+
+def preshuffle_scales(s, s_out, rows, K, stream=None):
+    _check(_lib.mxgemm_preshuffle_scales(_ptr(s), _ptr(s_out), rows, K, _stream(stream)),
+           "mxgemm_preshuffle_scales")
+
+
+def grouped_preshuffle_b(G, WQ, WQ_out, N, K, stream=None):
+    _check(_lib.grouped_fp8_preshuffle_b(G, _ptr(WQ), _ptr(WQ_out), N, K, _stream(stream)),
+           "grouped_fp8_preshuffle_b")

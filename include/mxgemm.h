@@ -1,0 +1,193 @@
+/*
+ * mxgemm.h -- C ABI of the MI355X (gfx950) block-scaled GEMM library.
+ *
+ * One operation, three scale families:
+ *
+ *     D[m,n] = sum_k a(m,k) * b(n,k)        (FP32 accumulation, BF16 output)
+ *
+ * with a, b the dequantized operands:
+ *   MX          a = dec(qA[m,k]) * 2^(eA[m,k/32]-127)       (E8M0 per 32 K)
+ *   tensor-wise a = dec(qA[m,k]) * sA                        (one FP32)
+ *   groupwise   a = dec(XQ[r,k]) * xs(r,k/128), b = dec(WQ[g,n,k]) * ws[g,n/128,k/128]
+ *
+ * Sources: "Experimental FlyDSL GEMM backend for TE PyTorch
+ * (BF16/FP16/FP32/FP8/MXFP8)" (Summary; Supported Data Types; Validation: the
+ * TN/NN/NT layouts, mixed E4M3/E5M2, MXFP8); "Add FlyDSL grouped groupwise
+ * FP8 GEMM for ROCm" (PR body: plain and preshuffled [G,N,K] weights, N and K
+ * multiples of 128, activation scales in the per-group block layout; Tile
+ * selection: grid from static shapes only, no host read of tensor contents,
+ * one kernel per call; Architecture support: wide scaled MFMA with a neutral
+ * E8M0 scale and FP32 scales applied in software); "[gfx1250] Add MXFP4 GEMM
+ * support to FlyDSL backend" (Description: plain scales in, shuffled inside);
+ * "PyTorch on AMD GPUs gains a FlyDSL backend" (Interpretation: FP8 or packed
+ * FP4 operands, one E8M0 scale per 32 values along K, NT scaled GEMM).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains caller memory and uses no workspace.
+ *  - Calls are stream-ordered and asynchronous: exactly one kernel is
+ *    enqueued on `stream` (0 = the null stream) per successful call.
+ *  - All argument checks are synchronous and happen before anything is
+ *    enqueued; on error nothing is enqueued and outputs are untouched.
+ *  - No C++ exception crosses this ABI.  Returns MXG_OK (0) or a negative
+ *    mxg_status; mxgemm_status_string() names it.
+ *  - The host never reads device data, so calls are safe to capture into a
+ *    HIP graph after mxgemm_init().
+ *  - Sizes are int64.  M, N (or totM) == 0 is a no-op returning MXG_OK;
+ *    K == 0 writes zeros.
+ *  - Layout names are row-major, first letter for A, second for B:
+ *      A 'N' = [M,K] (K contiguous)   A 'T' = [K,M] (M contiguous)
+ *      B 'T' = [N,K] (K contiguous)   B 'N' = [K,N] (N contiguous)
+ *    so NT is D = A * B^T with both operands K-contiguous.
+ *  - D is BF16 (raw uint16 bits), row-major [M,N], rounded to nearest even.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXG_OK = 0,
+  MXG_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum          */
+  MXG_ERR_UNSUPPORTED = -2,   /* combination or divisibility not built          */
+  MXG_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned               */
+  MXG_ERR_HIP = -4            /* the HIP runtime reported an error              */
+} mxg_status;
+
+/* Operand format = element encoding + scale kind (one per operand). */
+enum {
+  MXG_MXFP8_E4M3 = 0,         /* E4M3 codes + E8M0 scale per 32 along K          */
+  MXG_MXFP8_E5M2 = 1,         /* E5M2 codes + E8M0 scale per 32 along K          */
+  MXG_MXFP4_E2M1 = 4,         /* E2M1 codes two per byte (element 2j in bits 3:0,
+                                 2j+1 in bits 7:4) + E8M0 scale per 32 along K  */
+  MXG_FP8_E4M3_TENSOR = 16,   /* E4M3 codes + one FP32 dequant multiplier        */
+  MXG_FP8_E5M2_TENSOR = 17    /* E5M2 codes + one FP32 dequant multiplier        */
+};
+
+/* OR into fmtB: B's codes (and, for MX, sB) were produced by
+ * mxgemm_preshuffle_b / mxgemm_preshuffle_scales. */
+#define MXG_PRESHUFFLED 0x100
+
+enum { MXG_NT = 0, MXG_NN = 1, MXG_TN = 2 };
+
+/* Largest G accepted by grouped_fp8_gemm_run. */
+#define MXG_GROUPED_MAX_G 1024
+
+/*
+ * mxgemm_init -- load the library's code objects on the current device.
+ * Call once per device before capturing calls into a HIP graph.  Idempotent.
+ */
+int mxgemm_init(void);
+
+/* Static description of a status code; never freed. */
+const char *mxgemm_status_string(int status);
+
+/*
+ * mxgemm_run -- dense block-scaled GEMM D[M,N] = sum_k a(m,k) b(n,k).
+ *
+ * fmtA, fmtB  operand formats (MXG_MXFP8_*, MXG_MXFP4_E2M1, MXG_FP8_*_TENSOR);
+ *             both MX or both tensor-wise; E2M1 only with E2M1.  fmtB may
+ *             carry MXG_PRESHUFFLED (NT only).
+ * layout      MXG_NT, MXG_NN or MXG_TN (see the header comment).
+ * A, B        codes: uint8, row-major in the layout's storage shape.  E2M1 is
+ *             packed two per byte along K (NT only).
+ * sA, sB      MX: uint8 E8M0 [rows, K/32] row-major (rows = M for A, N for B),
+ *             always blocked along K whatever the code layout; a preshuffled
+ *             sB has the size given by mxgemm_preshuffle_scales_bytes(N, K).
+ *             Tensor-wise: pointer to one float (device), the dequant
+ *             multiplier (value = code value * s).
+ * D           BF16 [M,N] row-major, written in full.
+ * Divisibility: MX needs K % 128 == 0 (E2M1: K % 256 == 0); NN/TN need the
+ *             contiguous dimension of each transposed operand (M for A 'T',
+ *             N for B 'N') to be a multiple of 16.  Otherwise
+ *             MXG_ERR_UNSUPPORTED.  A, B, sA, sB and D must be 16-byte
+ *             aligned (MXG_ERR_MISALIGNED).
+ * Edge rows/columns (M, N not multiples of the tile) are masked.
+ */
+int mxgemm_run(int fmtA, int fmtB, int layout,
+               const void *A, const void *sA, const void *B, const void *sB,
+               void *D, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* Host-only check of mxgemm_run's arguments (no device call).  Returns the
+ * status mxgemm_run would return before enqueueing anything. */
+int mxgemm_validate(int fmtA, int fmtB, int layout,
+                    const void *A, const void *sA, const void *B, const void *sB,
+                    const void *D, int64_t M, int64_t N, int64_t K);
+
+/*
+ * grouped_fp8_gemm_run -- grouped groupwise FP8 GEMM (one GEMM per group of
+ * rows, e.g. per expert).
+ *
+ * G           number of groups, 1 <= G <= MXG_GROUPED_MAX_G.
+ * m_sizes     device int64[G]: rows per group, in order.  Group g owns rows
+ *             [start_g, start_g + m_sizes[g]) with start_g the prefix sum.
+ *             Caller precondition (not checked: the host reads no device
+ *             data): m_sizes[g] >= 0 and sum = totM.  The kernel clamps every
+ *             group to [0, totM), so a violated precondition can leave rows
+ *             unwritten but never touches memory outside D.
+ * XQ          E4M3 [totM, K] row-major.
+ * x_scale     FP32, totM*K/128 values in the per-group block layout: group
+ *             g's block begins at start_g*(K/128) and holds (local row i,
+ *             k-block kb) at i + kb*m_sizes[g].
+ * WQ          E4M3 weights [G, N, K] row-major, or (b_preshuffled != 0) the
+ *             output of grouped_fp8_preshuffle_b.
+ * w_scale     FP32 [G, N/128, K/128] row-major (one per 128x128 block).
+ * D           BF16 [totM, N] row-major; rows of empty groups do not exist,
+ *             rows outside every group are left untouched.
+ * N and K must be multiples of 128 (MXG_ERR_UNSUPPORTED).
+ */
+int grouped_fp8_gemm_run(int G, const int64_t *m_sizes,
+                         const void *XQ, const float *x_scale,
+                         const void *WQ, const float *w_scale,
+                         void *D, int64_t totM, int64_t N, int64_t K,
+                         int b_preshuffled, hipStream_t stream);
+
+int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
+                              const void *XQ, const float *x_scale,
+                              const void *WQ, const float *w_scale,
+                              const void *D, int64_t totM, int64_t N, int64_t K,
+                              int b_preshuffled);
+
+/*
+ * Preshuffle: one-time re-layout of a B operand (weights) into the order in
+ * which the matrix-core K-loop consumes it ("Add FlyDSL grouped groupwise FP8
+ * GEMM for ROCm", PR body: callers shuffle once at load time).
+ *
+ * mxgemm_preshuffle_b: B codes of format fmtB (E4M3/E5M2/E2M1, MX or tensor)
+ * stored per `layout`'s B ('T' = [N,K], 'N' = [K,N]; E2M1 only [N,K]) ->
+ * B_out of mxgemm_preshuffle_b_bytes(fmtB, N, K) bytes, consumable by
+ * mxgemm_run with fmtB | MXG_PRESHUFFLED and layout MXG_NT.  Padding beyond N
+ * is zero-filled.  K must satisfy mxgemm_run's divisibility rule.
+ */
+int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K);
+int mxgemm_preshuffle_b(int fmtB, int layout, const void *B, void *B_out,
+                        int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * mxgemm_preshuffle_scales: E8M0 scales [rows, K/32] -> s_out of
+ * mxgemm_preshuffle_scales_bytes(rows, K) bytes, in per-lane order (one
+ * 32-bit word per lane covers four consecutive 128-K steps).  Padding is
+ * filled with 127 (scale 1).
+ */
+int64_t mxgemm_preshuffle_scales_bytes(int64_t rows, int64_t K);
+int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K,
+                             hipStream_t stream);
+
+/*
+ * grouped_fp8_preshuffle_b: plain E4M3 weights [G, N, K] -> WQ_out of the
+ * same byte size, consumable by grouped_fp8_gemm_run with b_preshuffled = 1.
+ * N and K must be multiples of 128.
+ */
+int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out,
+                             int64_t N, int64_t K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

@@ -1,0 +1,126 @@
+"""GPU parity of grouped_fp8_gemm_run (plain and preshuffled weights) against
+the FP64 oracle.  Rows of D outside every group are prefilled with a
+sentinel and must keep it bit for bit; empty groups own no rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_precision_03_amd import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_BITS = 0x7F7F   # a large finite BF16 value no GEMM row here produces
+
+
+def _inputs(seed, m_sizes, N, K, totM=None):
+    m_sizes = np.asarray(m_sizes, np.int64)
+    G = len(m_sizes)
+    cover = int(m_sizes.sum())
+    totM = cover if totM is None else totM
+    x = synth.normal(seed, (totM, K))
+    w = synth.normal(seed + 1, (G, N, K), 0.02)
+    XQ, xs = synth.quant_group_act(x[:cover], m_sizes)
+    if totM > cover:   # rows beyond every group: any codes, unit scales
+        XQ = np.concatenate([XQ, np.full((totM - cover, K), 0x38, np.uint8)])
+        xs = np.concatenate([xs, np.ones((totM - cover) * (K // 128), np.float32)])
+    WQ, ws = synth.quant_group_weight(w)
+    return m_sizes, XQ, xs, WQ, ws, totM
+
+
+def _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled):
+    from block_scaled_precision_03_amd import mxgemm
+    G = len(m_sizes)
+    D = torch.full((totM, N), 0, dtype=torch.int16, device=H.DEV)
+    D.fill_(SENTINEL_BITS)
+    W = H.dev(WQ)
+    if preshuffled:
+        Wp = torch.empty_like(W)
+        mxgemm.grouped_preshuffle_b(G, W, Wp, N, K)
+        W = Wp
+    mxgemm.grouped_run(G, H.dev(m_sizes), H.dev(XQ), H.dev(xs), W, H.dev(ws), D, totM, N, K,
+                       b_preshuffled=preshuffled)
+    torch.cuda.synchronize()
+    return D
+
+
+SPLITS = [
+    [37, 0, 150, 3, 64, 1, 99, 30],    # uneven, one empty, not tile aligned
+    [0, 0, 300, 0],                    # all rows in one group
+    [0, 70, 129, 41],                  # first empty
+    [200, 56, 0],                      # last empty
+    [128, 128, 256],                   # tile aligned
+    [1, 1, 1, 1, 1],                   # single rows
+]
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+@pytest.mark.parametrize("split", SPLITS)
+def test_grouped_splits(split, preshuffled):
+    N, K = 256, 640              # G > 1, K > 128: per-group scale addressing matters
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(700 + len(split), split, N, K)
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped %s" % split)
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_rows_outside_groups_untouched(preshuffled):
+    N, K = 128, 384
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(801, [40, 0, 77], N, K, totM=200)
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    bits = H.bits(D.view(torch.bfloat16))
+    assert np.all(bits[117:] == SENTINEL_BITS)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D[:117].view(torch.bfloat16)), ref[:117], "covered rows")
+
+
+def test_grouped_integer_valued_bit_exact():
+    """Codes in {-2..2}, power-of-two scales: every partial sum is an exact
+    FP32 integer, so group boundaries and scale addressing must be exact."""
+    rng = np.random.default_rng(5)
+    m_sizes = np.array([33, 0, 190, 7, 100], np.int64)
+    totM, N, K, G = int(m_sizes.sum()), 256, 1024, 5
+    vals = np.array([0xC0, 0xB8, 0x00, 0x38, 0x40], np.uint8)
+    XQ = vals[rng.integers(0, 5, (totM, K))]
+    WQ = vals[rng.integers(0, 5, (G, N, K))]
+    xs = (2.0 ** rng.integers(0, 3, totM * K // 128)).astype(np.float32)
+    ws = (2.0 ** rng.integers(0, 3, (G, N // 128, K // 128))).astype(np.float32)
+    for pre in (False, True):
+        D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, pre)
+        ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+        assert np.array_equal(H.bits(D.view(torch.bfloat16)), oracle.bf16_rne(ref))
+
+
+def test_grouped_scale_addressing_distinct_groups():
+    """Distinct per-group activation scales: a kernel that reads another
+    group's scales (the global-transpose mistake) fails this test."""
+    rng = np.random.default_rng(9)
+    m_sizes = np.array([20, 50, 0, 35], np.int64)
+    totM, N, K, G = int(m_sizes.sum()), 128, 512, 4
+    XQ = np.full((totM, K), 0x38, np.uint8)
+    WQ = np.full((G, N, K), 0x38, np.uint8)
+    xs = rng.integers(1, 9, totM * K // 128).astype(np.float32)
+    ws = np.ones((G, 1, K // 128), np.float32)
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, False)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    assert np.array_equal(H.bits(D.view(torch.bfloat16)), oracle.bf16_rne(ref))
+
+
+def test_grouped_precondition_violation_is_contained():
+    """sum(m_sizes) > totM: groups are clamped to [0, totM); nothing outside
+    D is touched and covered rows still match the clamped oracle."""
+    N, K = 128, 256
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(901, [30, 50], N, K)
+    bad = np.array([30, 500], np.int64)
+    guard = torch.full((totM + 64, N), 0, dtype=torch.int16, device=H.DEV)
+    guard.fill_(SENTINEL_BITS)
+    from block_scaled_precision_03_amd import mxgemm
+    mxgemm.grouped_run(2, H.dev(bad), H.dev(XQ), H.dev(xs), H.dev(WQ), H.dev(ws), guard[:totM],
+                       totM, N, K)
+    torch.cuda.synchronize()
+    bits = H.bits(guard.view(torch.bfloat16))
+    assert np.all(bits[totM:] == SENTINEL_BITS)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(guard[:30].view(torch.bfloat16)), ref[:30], "group 0")
