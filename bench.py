@@ -1,0 +1,269 @@
+"""Benchmark of the block-scaled GEMM library on one MI355X.
+
+A step = the six MXFP8 NT GEMMs of the LLM-shaped workload (M in {4096,
+16384} x (N, K) in {(4096, 4096), (14336, 4096), (4096, 14336)}; E4M3 codes
+with one E8M0 scale per 32 K values, FP32 accumulation, BF16 output), each
+one mxgemm_run call on weights preshuffled once before timing.  Inputs are
+seeded synthetic data resident in HBM before the timed region.
+
+Also measured (reported beside the headline, not part of `value`): the
+grouped groupwise FP8 GEMM (G=8) in microseconds per call, and the CPU
+oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-grouped]
+       [--no-cpu] [--only-step]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MXFP8_TFLOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 FLOP/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+C2_SHAPES = [(4096, 4096, 4096), (4096, 14336, 4096), (4096, 4096, 14336),
+             (16384, 4096, 4096), (16384, 14336, 4096), (16384, 4096, 14336)]
+C4_SHAPES = [(128, 2048, 7168), (1024, 2048, 7168), (16384, 2048, 7168),
+             (128, 7168, 2304), (1024, 7168, 2304), (16384, 7168, 2304)]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-grouped", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the MXFP8 step only (for profiler runs)")
+    ap.add_argument("--plain-b", action="store_true", help="time with plain (not preshuffled) B")
+    return ap.parse_args()
+
+
+def c2_inputs(torch, synth, mxgemm, dev, preshuffle):
+    """Quantized operands of the six GEMMs (X shared by the two M values)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    xs = {}
+    for ki, K in enumerate((4096, 14336)):
+        x = synth.normal(synth.seed_for(2, 1, ki), (16384, K))
+        q, s = synth.quant_mx(x, "e4m3")
+        xs[K] = (t(q), t(s))
+        del x
+    ws = {}
+    for wi, (N, K) in enumerate(((4096, 4096), (14336, 4096), (4096, 14336))):
+        w = synth.normal(synth.seed_for(2, 2, wi), (N, K), 0.02)
+        q, s = synth.quant_mx(w, "e4m3")
+        qd, sd = t(q), t(s)
+        if preshuffle:
+            qp = torch.empty(mxgemm.preshuffle_b_bytes(mxgemm.MXFP8_E4M3, N, K), dtype=torch.uint8, device=dev)
+            sp = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=dev)
+            mxgemm.preshuffle_b(mxgemm.MXFP8_E4M3, mxgemm.NT, qd, qp, N, K)
+            mxgemm.preshuffle_scales(sd, sp, N, K)
+            qd, sd = qp, sp
+        ws[(N, K)] = (qd, sd, q, s)
+        del w
+    torch.cuda.synchronize()
+    return xs, ws
+
+
+def time_step(torch, mxgemm, calls, steps, warmup):
+    """Run `calls` (list of closures) per step; per-launch HIP events on the
+    launch stream.  Returns (ms_per_step, per-call mean ms)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(steps):
+        for i, c in enumerate(calls):
+            ev[s][i][0].record(stream)
+            c()
+            ev[s][i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    per = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
+    return total_ms / steps, per.mean(axis=0), wall
+
+
+def grouped_bench(torch, synth, mxgemm, dev, reps=50):
+    """µs per call for the six grouped G=8 shapes (preshuffled weights):
+    warm (back-to-back calls) and cold (weights rotated through > 256 MB)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = []
+    G = 8
+    for si, (totM, N, K) in enumerate(C4_SHAPES):
+        m_sizes = synth.m_sizes_for(totM, G, synth.seed_for(4, 4, si))
+        x = synth.normal(synth.seed_for(4, 1, si), (totM, K))
+        xq, xsc = synth.quant_group_act(x, m_sizes)
+        w = synth.normal(synth.seed_for(4, 2, si), (G, N, K), 0.02)
+        wq, wsc = synth.quant_group_weight(w)
+        del x, w
+        dm, dx, dxs, dws = t(m_sizes), t(xq), t(xsc), t(wsc)
+        wplain = t(wq)
+        copies = max(1, int(np.ceil(300e6 / wq.nbytes)) + 1)
+        wps = []
+        for _ in range(copies):
+            wp = torch.empty_like(wplain)
+            mxgemm.grouped_preshuffle_b(G, wplain, wp, N, K)
+            wps.append(wp)
+        D = torch.empty((totM, N), dtype=torch.bfloat16, device=dev)
+        res = {"totM": totM, "N": N, "K": K, "m_sizes": [int(v) for v in m_sizes]}
+        for name, W, pre in (("plain", wplain, False), ("preshuffled", wps[0], True)):
+            call = lambda: mxgemm.grouped_run(G, dm, dx, dxs, W, dws, D, totM, N, K, b_preshuffled=pre)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            res[name + "_us"] = a.elapsed_time(b) * 1000.0 / reps
+        # cold: rotate through weight copies totalling > 256 MB
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        n = 0
+        for r in range(reps):
+            W = wps[r % copies]
+            mxgemm.grouped_run(G, dm, dx, dxs, W, dws, D, totM, N, K, b_preshuffled=True)
+            n += 1
+        b.record()
+        torch.cuda.synchronize()
+        res["preshuffled_cold_us"] = a.elapsed_time(b) * 1000.0 / n
+        flops = 2.0 * totM * N * K
+        nonempty = int(np.count_nonzero(m_sizes))
+        hbm = totM * K + nonempty * N * K + 4 * totM * K / 128 + 4 * G * (N / 128) * (K / 128) + 2 * totM * N + 8 * G
+        best = min(res["plain_us"], res["preshuffled_us"])
+        res["tflops_best_warm"] = flops / (best * 1e-6) / 1e12
+        res["algo_bytes"] = hbm
+        res["gbs_cold"] = hbm / (res["preshuffled_cold_us"] * 1e-6) / 1e9
+        out.append(res)
+        log("grouped %s: plain %.1f us, preshuffled %.1f us, cold %.1f us (%.0f GB/s)" % (
+            (totM, N, K), res["plain_us"], res["preshuffled_us"], res["preshuffled_cold_us"], res["gbs_cold"]))
+        del wps, wplain, dx, D
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(synth, target_s=12.0):
+    """The FP64 oracle, as it stands, on rows [0, R) of the M=16384,
+    N=4096, K=4096 MXFP8 GEMM (dequantize + plain FP64 dot products)."""
+    import oracle
+    N = K = 4096
+    x = synth.normal(synth.seed_for(2, 1, 0), (16384, K))
+    w = synth.normal(synth.seed_for(2, 2, 0), (N, K), 0.02)
+    qb, sb = synth.quant_mx(w, "e4m3")
+    opB = (oracle.E4M3, oracle.SCALE_MX, 0, qb, sb)
+    def run(rows):
+        qa, sa = synth.quant_mx(x[:rows], "e4m3")
+        t0 = time.perf_counter()
+        oracle.gemm((oracle.E4M3, oracle.SCALE_MX, 0, qa, sa), opB, rows, N, K)
+        return time.perf_counter() - t0
+    probe_rows = 16
+    tp = run(probe_rows)
+    rows = int(max(probe_rows, min(16384, probe_rows * target_s / max(tp, 1e-3))))
+    rows = max(16, rows // 16 * 16)
+    dt = run(rows)
+    flops = 2.0 * rows * N * K
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "rows 0..%d of the M=16384 N=4096 K=4096 MXFP8 NT GEMM (FP64 dequant + "
+                      "dot products), %.1f s" % (rows, dt),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_scaled_precision_03_amd import mxgemm, synth
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    mxgemm.init()
+    pre = not args.plain_b
+    log("generating MXFP8 inputs ...")
+    t0 = time.perf_counter()
+    xs, ws = c2_inputs(torch, synth, mxgemm, dev, pre)
+    log("inputs ready in %.1f s" % (time.perf_counter() - t0))
+    fmtB = mxgemm.MXFP8_E4M3 | (mxgemm.PRESHUFFLED if pre else 0)
+    outs = {}
+    calls = []
+    flops = []
+    for (M, N, K) in C2_SHAPES:
+        qa, sa = xs[K]
+        qa, sa = qa[:M], sa[:M]
+        qb, sb = ws[(N, K)][:2]
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        outs[(M, N, K)] = D
+        calls.append((lambda qa=qa, sa=sa, qb=qb, sb=sb, D=D, M=M, N=N, K=K:
+                      mxgemm.run(mxgemm.MXFP8_E4M3, fmtB, mxgemm.NT, qa, sa, qb, sb, D, M, N, K)))
+        flops.append(2.0 * M * N * K)
+    log("timing %d steps (+%d warmup) ..." % (args.steps, args.warmup))
+    ms, per_ms, wall = time_step(torch, mxgemm, calls, args.steps, args.warmup)
+    step_flops = sum(flops)
+    value = step_flops / (ms * 1e-3) / 1e12
+    kernel_ms = float(per_ms.sum())
+    achieved = step_flops / (kernel_ms * 1e-3) / 1e12
+    per_gemm = []
+    for (shape, f, pm) in zip(C2_SHAPES, flops, per_ms):
+        tf = f / (pm * 1e-3) / 1e12
+        per_gemm.append({"M": shape[0], "N": shape[1], "K": shape[2], "us": pm * 1000.0,
+                         "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP8_TFLOPS})
+        log("  %s: %.1f us, %.0f TFLOP/s (%.1f%% of peak)" % (shape, pm * 1000, tf, 100 * tf / PEAK_MXFP8_TFLOPS))
+    log("step: %.3f ms -> %.0f TFLOP/s" % (ms, value))
+    result = {
+        "metric": "MXFP8 NT GEMM TFLOP/s + % MFMA peak; grouped FP8 GEMM us/call (G=8)",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 x fp8_e4m3 (E8M0/32 scales), fp32 acc, bf16 out",
+        "data": "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights, quantized on the host)",
+        "config": {"workload": "MXFP8 NT GEMM, LLM shapes: M in {4096,16384} x (N,K) in "
+                               "{(4096,4096),(14336,4096),(4096,14336)}; one step = the 6 GEMMs",
+                   "b_preshuffled": pre, "layout": "NT"},
+        "pct_mfma_peak": 100.0 * value / PEAK_MXFP8_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MXFP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MXFP8_TFLOPS, "traffic": None,
+                     "kernel": "dense_kernel<E4M3,E4M3,MX,NT,preshuffled B>" if pre else
+                               "dense_kernel<E4M3,E4M3,MX,NT>",
+                     "kernel_ms_per_step": kernel_ms},
+        "per_gemm": per_gemm,
+    }
+    del outs, calls, xs, ws
+    torch.cuda.empty_cache()
+    if not args.only_step and not args.no_grouped:
+        log("grouped G=8 ...")
+        result["grouped"] = grouped_bench(torch, synth, mxgemm, dev)
+    if not args.only_step and not args.no_cpu:
+        log("CPU oracle sample ...")
+        result["cpu_baseline"] = cpu_baseline(synth)
+        log("cpu baseline: %.4g TFLOP/s on %d threads" % (result["cpu_baseline"]["value"],
+                                                          result["cpu_baseline"]["cores"]))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,7 +93,7 @@ extern "C" int mxgemm_validate(int fmtA, int fmtB, int layout, const void *A, co
   if (layout == MXG_TN && (M % 16 != 0 || M * 128 >= (1ll << 31))) return MXG_ERR_UNSUPPORTED;
   if ((layout == MXG_TN || layout == MXG_NN) && (N % 16 != 0 || N * 128 >= (1ll << 31)))
     return MXG_ERR_UNSUPPORTED;
-  if (fa.mx && (M * (K / 32) >= (1ll << 31) || cdiv(N, 16) * 16 * (K / 32) >= (1ll << 31)))
+  if (fa.mx && (M * (K / 32) >= (1ll << 31) || cdiv(N, 64) * 64 * (K / 32) >= (1ll << 31)))
     return MXG_ERR_UNSUPPORTED;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, fa.mx ? 16 : 4) || !aligned(sB, fb.mx ? 16 : 4))
     return MXG_ERR_MISALIGNED;
@@ -108,16 +108,14 @@ template <int FA, int FB>
 dense_fn pick_layout(bool mx, int layout, bool psb) {
   if (mx) {
     if (layout != MXG_NT) return nullptr;
-    return psb ? dense_kernel<FA, FB, SM_MX, false, false, true>
-               : dense_kernel<FA, FB, SM_MX, false, false, false>;
+    return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
   }
   if constexpr (FA == F_E2M1 || FB == F_E2M1) {
     return nullptr;
   } else {
     switch (layout) {
       case MXG_NT:
-        return psb ? dense_kernel<FA, FB, SM_TENSOR, false, false, true>
-                   : dense_kernel<FA, FB, SM_TENSOR, false, false, false>;
+        return psb ? dense_kernel<FA, FB, SM_TENSOR, false, false, true> : dense_kernel<FA, FB, SM_TENSOR, false, false, false>;
       case MXG_NN: return dense_kernel<FA, FB, SM_TENSOR, false, true, false>;
       case MXG_TN: return dense_kernel<FA, FB, SM_TENSOR, true, true, false>;
       default: return nullptr;
@@ -173,7 +171,7 @@ extern "C" int mxgemm_run(int fmtA, int fmtB, int layout, const void *A, const v
   a.tiles_n = (int)cdiv(N, DBN);
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(DNW8 * 64), 0, stream, a);
   return launch_status();
 }
 
@@ -250,8 +248,8 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
 extern "C" int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K) {
   const FmtInfo f = fmt_info(fmtB & ~MXG_PRESHUFFLED);
   if (!f.ok || N < 0 || K < 0 || K % 128 != 0) return -1;
-  const int64_t nt = cdiv(N, 16), nks = K / 128;
-  return nt * nks * (f.elem == F_E2M1 ? 1024 : 2048);
+  const int64_t ncg = cdiv(N, 64), nks = K / 128;
+  return ncg * nks * (f.elem == F_E2M1 ? 4096 : 8192);
 }
 
 extern "C" int mxgemm_preshuffle_b(int fmtB, int layout, const void *B, void *B_out, int64_t N, int64_t K,
@@ -282,7 +280,7 @@ extern "C" int mxgemm_preshuffle_b(int fmtB, int layout, const void *B, void *B_
 
 extern "C" int64_t mxgemm_preshuffle_scales_bytes(int64_t rows, int64_t K) {
   if (rows < 0 || K < 0 || K % 32 != 0) return -1;
-  return cdiv(rows, 16) * cdiv(K, 512) * 256;
+  return cdiv(rows, 64) * cdiv(K, 512) * 1024;
 }
 
 extern "C" int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K,

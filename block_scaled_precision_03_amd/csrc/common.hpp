@@ -4,6 +4,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace mxg {
 
@@ -15,6 +16,7 @@ typedef unsigned u4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 
 // Element-format codes understood by the scaled MFMA's cbsz/blgp fields.
 enum : int { F_E4M3 = 0, F_E5M2 = 1, F_E2M1 = 4 };
@@ -44,17 +46,62 @@ __device__ inline void dma4(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 4, (int)voff, 0, 0, 0);
 }
 
+// The same DMA issued as inline assembly, invisible to the compiler's
+// wait-count insertion: a kernel that uses it must itself wait (vmcnt) for
+// the DMA before any wave reads the destination, and must not overwrite a
+// destination that another wave may still read.  The resource is four SGPRs
+// (base, stride 0, num_records, dword 3 as in make_rsrc).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x4 rsrc4(const void *base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, nbytes, 0x00020000u};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// LDS byte address of a __shared__ object (32-bit LDS address space).
+__device__ inline uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// lds: LDS byte address of lane 0's destination, uniform; IMM is added to
+// it inside the instruction sequence so that call sites that differ only by
+// a constant share one base register.
+template <int BYTES, int IMM = 0>
+__device__ inline void dma_asm(uint32_t lds, const u32x4 &r, uint32_t voff, uint32_t soff) {
+  static_assert(BYTES == 4 || BYTES == 16, "DMA width");
+  if constexpr (BYTES == 16)
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff), "i"(IMM) : "memory", "m0", "scc");
+  else
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff), "i"(IMM) : "memory", "m0", "scc");
+}
+
+// Compile-time loop: f(std::integral_constant<int, J>) for J in [B, E).
+template <int B, int E, class F>
+__device__ inline void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+#pragma clang diagnostic pop
+
 __device__ inline uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
 }
 
+// LDS accesses cast the generic pointer straight to the LDS address space
+// (an address-space cast, not a round trip through an integer) so that
+// alias information of the pointer survives.
 __device__ inline v4i lds_read16(const void *p) {
-  return *(const lds_v4i *)(const __attribute__((address_space(3))) char *)(uintptr_t)(p);
+  return *(const lds_v4i *)p;
 }
 
 __device__ inline v2i lds_read_tr8(const void *p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (lds_v2i *)((__attribute__((address_space(3))) char *)(uintptr_t)(p)));
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)p);
 }
 
 // D += sum over a 16x16x128 block: first operand rows = output rows.
@@ -74,6 +121,9 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
+
+__device__ inline uint32_t lds_load_u32(const void *p) { return *(const lds_u32_t *)p; }
+__device__ inline void lds_store8(void *p, v2i v) { *(__attribute__((address_space(3))) v2i *)p = v; }
 
 // Wait for this wave's outstanding vector-memory loads (including LDS DMA).
 // s_waitcnt simm16 on gfx9: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8];

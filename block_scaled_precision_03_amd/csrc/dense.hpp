@@ -35,6 +35,7 @@ struct DenseArgs {
 };
 
 constexpr int DBM = 256, DBN = 256, DNW = 4;
+constexpr int DNW8 = 8;           // waves of the pipelined dense kernel
 constexpr int DSTAGE = (DBM + DBN) * 128;
 
 // ---------------------------------------------------------------------------
@@ -79,21 +80,23 @@ __device__ inline void load_t(const uint8_t *X, int64_t total, int64_t c0, int64
   }
 }
 
-// Preshuffled B: fragment (n-tile t, k-step ks) is contiguous (FP8: two 1 KiB
-// halves, FP4: one 1 KiB block) in lane order; copied linearly.
-template <bool FP4, int R = DBN, int NW = DNW>
-__device__ inline void load_ps(const uint8_t *X, int64_t total, int64_t nt0, int64_t nks,
+// Preshuffled B (layout documented in preshuffle.hpp): per stage, each of the
+// R/64 column groups contributes 8 KiB (FP8: k-step st; FP4: the two 4 KiB
+// chunks of k-steps 2st and 2st+1, adjacent in memory), copied linearly; in
+// LDS column group c sits at c*8192.
+template <int R, int NW, bool FP4 = false>
+__device__ inline void load_ps(const uint8_t *X, int64_t total, int64_t cg0, int64_t nks,
                                int st, uint8_t *lds, int w, int lane) {
-  constexpr int FRAG = FP4 ? 1024 : 2048;
+  constexpr int CGB = FP4 ? 4096 : 8192;
   const int64_t ks0 = FP4 ? 2 * (int64_t)st : (int64_t)st;
-  const int64_t base = (nt0 * nks + ks0) * FRAG;
+  const int64_t base = (cg0 * nks + ks0) * CGB;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, clamp_records(total - base));
-  constexpr int PER_W = (R / 16) * 2 / NW;
+  constexpr int PER_W = (R / 64) * 8 / NW;
 #pragma unroll
   for (int j = 0; j < PER_W; ++j) {
     const int idx = w * PER_W + j;
-    const int t = idx >> 1, sub = idx & 1;
-    const uint32_t voff = (uint32_t)(t * nks) * FRAG + sub * 1024 + lane * 16;
+    const int c = idx >> 3, sub = idx & 7;
+    const uint32_t voff = (uint32_t)(c * nks) * (uint32_t)CGB + sub * 1024 + lane * 16;
     dma16(rs, lds + idx * 1024, voff);
   }
 }
@@ -137,8 +140,9 @@ __device__ inline v8i frag_ps8(const uint8_t *region, int t, int lane) {
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// FP4: n-tile t of the block, k-step s of the stage.
 __device__ inline v4i frag_ps4(const uint8_t *region, int t, int s, int lane) {
-  return lds_read16(region + (t * 2 + s) * 1024 + lane * 16);
+  return lds_read16(region + (t >> 2) * 8192 + s * 4096 + (t & 3) * 1024 + lane * 16);
 }
 
 __device__ inline v8i widen(const v4i &v) {
@@ -152,7 +156,7 @@ __device__ inline v8i widen(const v4i &v) {
 // matrix-core result with the B tile as first operand).  In LDS, row m is
 // BN*2 bytes and its 8-byte chunk c sits at position c ^ (m % 16).  Rows at
 // or beyond row_lim and columns at or beyond N are not written.
-template <int BM, int BN, int FM, int FN>
+template <int BM, int BN, int FM, int FN, int NTHR = 256>
 __device__ inline void store_tile(const v4f (&acc)[FM][FN], float alpha, uint8_t *cs,
                                   uint16_t *D, int64_t m0, int64_t n0, int64_t row_lim,
                                   int64_t N, int wm, int wn) {
@@ -161,20 +165,19 @@ __device__ inline void store_tile(const v4f (&acc)[FM][FN], float alpha, uint8_t
   __syncthreads();
 #pragma unroll
   for (int a = 0; a < FM; ++a) {
-    const int m = wm * (BM / 2) + a * 16 + i16;
+    const int m = wm * (FM * 16) + a * 16 + i16;
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
-      const int c = (wn * (BN / 2) + b * 16 + 4 * q) >> 2;
+      const int c = (wn * (FN * 16) + b * 16 + 4 * q) >> 2;
       const v4f v = acc[a][b];
       const uint32_t lo = pack_bf16x2(v.x * alpha, v.y * alpha);
       const uint32_t hi = pack_bf16x2(v.z * alpha, v.w * alpha);
-      *(__attribute__((address_space(3))) v2i *)(__attribute__((address_space(3))) char *)(uintptr_t)(
-          cs + m * ROWB + ((c ^ (m & 15)) << 3)) = (v2i){(int)lo, (int)hi};
+      lds_store8(cs + m * ROWB + ((c ^ (m & 15)) << 3), (v2i){(int)lo, (int)hi});
     }
   }
   __syncthreads();
   constexpr int PAIRS = BN / 8;                 // 16-byte pairs per row
-  constexpr int RPP = 256 / PAIRS;              // rows per pass (256 threads)
+  constexpr int RPP = NTHR / PAIRS;             // rows per pass
   const bool vec_ok = (N & 7) == 0;
 #pragma unroll 4
   for (int it = 0; it < BM / RPP; ++it) {
@@ -216,114 +219,245 @@ __device__ inline void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &
   tn = in / rows;
 }
 
+// vmcnt(n) with expcnt/lgkmcnt left alone (n <= 63).
+template <int N>
+__device__ inline void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// The dense kernel: block tile 256 x 256, eight waves in a 2 x 4 grid (wave
+// tile 128 x 64, 8 x 4 matrix-core tiles, 128 accumulators), two waves per
+// SIMD so that one wave's LDS or barrier stall is covered by the other's
+// matrix work.  Two LDS stages of 128 bytes of K per row for A and B (plus
+// MX scales) are double buffered; every K step streams the next stage in by
+// DMA and touches the lines of the stage PF steps ahead so that they sit in
+// L2 by the time they are fetched.
+//
+// Every LDS access of the K loop goes through a restrict pointer per buffer
+// (two ring slots, their scale slots, the prefetch dump): the compiler can
+// then tell that the DMA filling one slot does not alias the reads of the
+// other, and does not stall those reads on it.
 template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
-__global__ __launch_bounds__(256, 1) void dense_kernel(DenseArgs p) {
-  constexpr bool FP4 = (FA == F_E2M1);
-  constexpr int KS = FP4 ? 2 : 1;          // 128-element K steps per stage
-  constexpr int FM = 8, FN = 8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * DSTAGE];
+struct DenseLoop {
+  static constexpr bool FP4 = (FA == F_E2M1);
+  static constexpr bool MX = (SMODE == SM_MX);
+  static constexpr int NW = DNW8;
+  static constexpr int KS = FP4 ? 2 : 1;        // 128-element K steps per stage
+  static constexpr int FM = 8, FN = 4;          // wave tile 128 x 64
+  static constexpr int PF = 3;                  // L2 prefetch distance (stages)
+  static constexpr int AB = DBM * 128;          // A bytes per stage
+  static constexpr int STAGE = (DBM + DBN) * 128;
+  static constexpr int SA_OFF = 0, SB_OFF = KS * 1024;
+  static constexpr int SSTAGE = MX ? KS * 1024 + (PSB ? 4096 : KS * 1024) : 0;
+  static constexpr int SLOT = STAGE + SSTAGE;   // [A tile][B tile][scales]
+  static constexpr int DUMP = 2 * SLOT;         // prefetch dump, 256 B per wave
+  static constexpr int LDS_BYTES = DUMP + NW * 256;
+  static constexpr int CGB = FP4 ? 4096 : 8192;
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int i16 = lane & 15, q = lane >> 4;
-  int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * DBM, n0 = (int64_t)tn * DBN;
-  const int64_t KB = FP4 ? p.K / 2 : p.K;   // bytes of K per row
-  const int nst = (int)(KB / 128);
-  const int64_t nks = p.K / 128;            // 128-element K steps
+  // Loop-invariant state.  Every global load of the loop is one buffer
+  // instruction: a resource fixed for the kernel, a per-lane offset fixed
+  // for the kernel (VGPR) and a uniform per-stage offset (SGPR).
+  struct Ctx {
+    const DenseArgs *p;
+    int lane, w, wm, wn, i16, q, nst;
+    int64_t m0, n0, KB, sk32, nks, ngrp;
+    u32x4 ra, rb, rs, rzero;                   // rs: this wave's scale source
+    u32x4 rp;                                  // this wave's prefetch source
+    uint32_t vo_a[2], vo_b[2];     // operand DMA offsets (by block parity)
+    uint32_t vo_p;                 // prefetch line offset
+    uint32_t vo_s;                 // scale DMA offset
+    uint32_t lds0;                 // LDS address of the kernel's LDS block (uniform)
+  };
 
-  v4f acc[FM][FN];
+  // Per-lane offsets of the 1 KiB wave DMAs of an operand tile.
+  //  K-contiguous rows (256 rows x 128 B): DMA block blk covers rows
+  //    8blk + lane/8; LDS position p of row r holds 16-byte piece
+  //    p ^ (r%8) ^ ((r/8)%2), so the lane reads piece (lane%8) ^ (lane/8) ^
+  //    (blk%2).  Uniform part of the offset: blk*8*KB + 128*st.
+  //  transposed (128 k-rows x 256 B): DMA block blk covers k-rows
+  //    4blk + lane/16; position c of k-row kk holds column chunk c ^ (kk%8),
+  //    so the lane reads chunk (lane%16) ^ ((4blk + lane/16) % 8).  Uniform
+  //    part: (4blk + 128 st) * Rtot.
+  __device__ static inline void dma_offsets(bool transposed, int lane, int64_t KB, int64_t Rtot,
+                                            uint32_t (&vo)[2]) {
 #pragma unroll
-  for (int a = 0; a < FM; ++a)
-#pragma unroll
-    for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  // Scale sources (MX only): plain [rows, K/32] bytes, or preshuffled B.
-  __amdgpu_buffer_rsrc_t rsa, rsb;
-  if constexpr (SMODE == SM_MX) {
-    rsa = make_rsrc(p.sA, clamp_records(p.sa_bytes));
-    rsb = make_rsrc(p.sB, clamp_records(p.sb_bytes));
+    for (int par = 0; par < 2; ++par) {
+      if (transposed) {
+        const int kk = par * 4 + (lane >> 4);
+        vo[par] = (uint32_t)((lane >> 4) * Rtot) + (uint32_t)(((lane & 15) ^ (kk & 7)) << 4);
+      } else {
+        const int r8 = lane >> 3;
+        vo[par] = (uint32_t)(r8 * KB) + (uint32_t)(((lane & 7) ^ r8 ^ par) << 4);
+      }
+    }
   }
-  const int64_t sk32 = p.K / 32;
-  const int64_t ngrp = (p.K + 511) / 512;
-  uint32_t sa_n[FM][KS], sb_n[FN][KS];
 
-  auto load_scales = [&](int st) {
-    if constexpr (SMODE == SM_MX) {
+  // Four 1 KiB DMAs of this wave into the tile at LDS address `tile`.
+  template <bool T>
+  __device__ static inline void load_tile(const Ctx &c, const u32x4 &r, const uint32_t (&vo)[2],
+                                          int64_t KB, int64_t Rtot, int st, uint32_t tile) {
+    const uint32_t base = tile + (uint32_t)c.w * 4096u;
+    static_for<0, 4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int blk = c.w * 4 + j;
+      const uint32_t soff = T ? (uint32_t)((4 * blk + 128 * (int64_t)st) * Rtot)
+                              : (uint32_t)(blk * 8 * KB + 128 * (int64_t)st);
+      dma_asm<16, j * 1024>(base, r, vo[j & 1], soff);
+    });
+  }
+
+  // DMA of stage st (operands and MX scales) into the ring slot at LDS
+  // address `slot`.  A stage past the last one issues the same instructions
+  // against an empty range.
+  __device__ static inline void issue(const Ctx &c, int st, uint32_t slot) {
+    const DenseArgs &p = *c.p;
+    const bool real = st < c.nst;
+    load_tile<TA>(c, real ? c.ra : c.rzero, c.vo_a, c.KB, p.M, st, slot);
+    if constexpr (PSB) {
+      // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
+      const uint32_t soff0 = (uint32_t)((c.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB) +
+                             (uint32_t)((c.w >> 1) * c.nks * CGB) + (uint32_t)(c.w & 1) * 4096u;
+      const uint32_t base = slot + AB + (uint32_t)c.w * 4096u;
+      const u32x4 rb = real ? c.rb : c.rzero;
+      static_for<0, 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        dma_asm<16, j * 1024>(base, rb, (uint32_t)(c.lane * 16), soff0 + j * 1024);
+      });
+    } else {
+      load_tile<TB>(c, real ? c.rb : c.rzero, c.vo_b, c.KB, p.N, st, slot + AB);
+    }
+    if constexpr (MX) {
+      // waves 0-3: A scales of rows 64w..; waves 4-7: B scales (plain: rows
+      // 64(w-4)..; preshuffled: column group w-4, four k steps per word).
+      const u32x4 r = real ? c.rs : c.rzero;
+      if (c.w < 4 || !PSB) {
+        const uint32_t dst = slot + STAGE + (c.w < 4 ? SA_OFF : SB_OFF) + (uint32_t)(c.w & 3) * 256u;
+        static_for<0, KS>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          dma_asm<4, s * 1024>(dst, r, c.vo_s, (uint32_t)(4 * ((int64_t)st * KS + s)));
+        });
+      } else {
+        const uint32_t soff = (uint32_t)((((int64_t)st * KS) / 4) * 1024);
+        dma_asm<16>(slot + STAGE + SB_OFF + (uint32_t)(c.w - 4) * 1024u, r, c.vo_s, soff);
+      }
+    }
+  }
+
+  // Touch every 128-byte line of stage st's A tile (waves 0-3) or B tile
+  // (waves 4-7): one 4-byte DMA per line into a dump area nobody reads, so
+  // that the real DMA PF stages later hits in L2.
+  __device__ static inline void prefetch(const Ctx &c, int st) {
+    const DenseArgs &p = *c.p;
+    const bool real = st < c.nst;
+    uint32_t soff;
+    if (c.w < 4) {
+      soff = TA ? (uint32_t)(128 * (int64_t)st * p.M) : (uint32_t)(128 * st);
+    } else {
+      if constexpr (PSB) soff = (uint32_t)((c.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB);
+      else if constexpr (TB) soff = (uint32_t)(128 * (int64_t)st * p.N);
+      else soff = (uint32_t)(128 * st);
+    }
+    dma_asm<4>(c.lds0 + DUMP + (uint32_t)c.w * 256u, real ? c.rp : c.rzero, c.vo_p, soff);
+  }
+
+  __device__ static inline uint32_t lds_u32(const uint8_t *p) { return lds_load_u32(p); }
+
+  // Per-lane LDS byte offsets of the fragment reads, fixed for the kernel.
+  // Each read is then base pointer + lane offset + a compile-time constant,
+  // which the compiler folds into the 16-bit offset field of the DS
+  // instruction (the lane offsets are masked to 16 bits so that it knows they
+  // are small), instead of keeping one address register per fragment.
+  struct Lanes {
+    uint32_t a[2], b[2];           // FP8 K-contiguous / preshuffled: the two 16-byte halves;
+                                   // FP4: the two k steps of the stage
+    uint32_t at[4][8], bt[4][4];   // transposed: per 8-byte piece t and tile
+    uint32_t sa, sb;               // scale words
+  };
+
+  __device__ static inline void lane_offsets(const Ctx &c, Lanes &L) {
+    const int i = c.i16, q = c.q;
+    const int f = (i & 7) ^ (i >> 3);
+    // K-contiguous tile rows: row r at r*128, piece p at (p ^ f)*16.
+    // FP8: halves h hold pieces q and q+4; FP4: k step h holds piece 4h+q.
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int64_t ks = (int64_t)st * KS + s;
+    for (int h = 0; h < 2; ++h) {
+      const int piece = FP4 ? 4 * h + q : q + 4 * h;
+      L.a[h] = ((uint32_t)((c.wm * 128 + i) * 128 + ((piece ^ f) << 4))) & 0xFFFFu;
+      if constexpr (PSB) L.b[h] = ((uint32_t)(c.wn * 8192 + (FP4 ? 0 : h * 1024) + c.lane * 16)) & 0xFFFFu;
+      else L.b[h] = ((uint32_t)((c.wn * 64 + i) * 128 + ((piece ^ f) << 4))) & 0xFFFFu;
+    }
+    // Transposed tiles (256 B per k-row): piece t of tile x.
 #pragma unroll
-        for (int a = 0; a < FM; ++a) {
-          const int64_t row = m0 + wm * 128 + a * 16 + i16;
-          sa_n[a][s] = buf_load_u32(rsa, (uint32_t)(row * sk32 + 4 * ks));
-        }
+    for (int t = 0; t < 4; ++t) {
+      const int kk = 16 * q + 8 * (t & 1) + 64 * (t >> 1) + (i >> 1);
 #pragma unroll
-        for (int b = 0; b < FN; ++b) {
-          if constexpr (PSB) {
-            const int64_t rt = (n0 + wn * 128) / 16 + b;
-            sb_n[b][s] = buf_load_u32(rsb, (uint32_t)(((rt * ngrp + ks / 4) * 64 + lane) * 4));
-          } else {
-            const int64_t row = n0 + wn * 128 + b * 16 + i16;
-            sb_n[b][s] = buf_load_u32(rsb, (uint32_t)(row * sk32 + 4 * ks));
-          }
+      for (int x = 0; x < 8; ++x) {
+        const int ca = c.wm * 8 + x;                 // 16-byte column chunk of A tile x
+        L.at[t][x] = ((uint32_t)(kk * 256 + ((ca ^ (kk & 7)) << 4) + ((i & 1) << 3))) & 0xFFFFu;
+        if (x < 4) {
+          const int cb = c.wn * 4 + x;
+          L.bt[t][x] = ((uint32_t)(kk * 256 + ((cb ^ (kk & 7)) << 4) + ((i & 1) << 3))) & 0xFFFFu;
         }
       }
     }
-  };
-
-  auto load_stage = [&](int st, uint8_t *buf) {
-    uint8_t *la = buf, *lb = buf + DBM * 128;
-    if constexpr (TA) load_t<DBM>(p.A, p.a_bytes, m0, p.M, st, la, w, lane);
-    else load_nt<DBM>(p.A, p.a_bytes, m0, KB, st, la, w, lane);
-    if constexpr (PSB) load_ps<FP4>(p.B, p.b_bytes, n0 / 16, nks, st, lb, w, lane);
-    else if constexpr (TB) load_t<DBN>(p.B, p.b_bytes, n0, p.N, st, lb, w, lane);
-    else load_nt<DBN>(p.B, p.b_bytes, n0, KB, st, lb, w, lane);
-  };
-
-  if (nst > 0) {
-    load_stage(0, smem);
-    load_scales(0);
+    L.sa = ((uint32_t)((c.wm * 128 + i) * 4)) & 0xFFFFu;
+    if constexpr (PSB) L.sb = ((uint32_t)(c.wn * 1024 + c.lane * 16)) & 0xFFFFu;
+    else L.sb = ((uint32_t)((c.wn * 64 + i) * 4)) & 0xFFFFu;
   }
-  wait_vmem();
-  __syncthreads();
 
-  for (int st = 0; st < nst; ++st) {
-    uint8_t *buf = smem + (st & 1) * DSTAGE;
-    const uint8_t *la = buf, *lb = buf + DBM * 128;
-    uint32_t sa_c[FM][KS], sb_c[FN][KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int a = 0; a < FM; ++a) sa_c[a][s] = sa_n[a][s];
-#pragma unroll
-      for (int b = 0; b < FN; ++b) sb_c[b][s] = sb_n[b][s];
-    }
-    // B fragments of this stage first; A fragments are read one 16-row tile
-    // ahead of the matrix-core instructions that consume them.
+  __device__ static inline v8i rd8(const uint8_t *base, uint32_t lo, uint32_t hi, int imm) {
+    const v4i x = lds_read16(base + lo + imm);
+    const v4i y = lds_read16(base + hi + imm);
+    return (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+  }
+
+  __device__ static inline v8i rdt(const uint8_t *base, const uint32_t (&off)[4]) {
+    v2i p0 = lds_read_tr8(base + off[0]);
+    v2i p1 = lds_read_tr8(base + off[1]);
+    v2i p2 = lds_read_tr8(base + off[2]);
+    v2i p3 = lds_read_tr8(base + off[3]);
+    return (v8i){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  }
+
+  __device__ static inline void compute(const Ctx &c, const Lanes &L, int st,
+                                        const uint8_t *slot, v4f (&acc)[FM][FN]) {
+    const uint8_t *la = slot, *lb = slot + AB, *ls = slot + STAGE;
     auto read_a = [&](int s, int a) -> v8i {
-      if constexpr (FP4) return widen(frag_nt4(la, wm * 128 + a * 16, s, lane));
-      else if constexpr (TA) return frag_t8<DBM>(la, wm * 128 + a * 16, lane);
-      else return frag_nt8(la, wm * 128 + a * 16, lane);
+      if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
+      else if constexpr (TA) {
+        const uint32_t o[4] = {L.at[0][a], L.at[1][a], L.at[2][a], L.at[3][a]};
+        return rdt(la, o);
+      } else return rd8(la, L.a[0], L.a[1], a * 2048);
     };
     auto read_b = [&](int s, int b) -> v8i {
       if constexpr (PSB) {
-        if constexpr (FP4) return widen(frag_ps4(lb, wn * 8 + b, s, lane));
-        else return frag_ps8(lb, wn * 8 + b, lane);
-      } else if constexpr (FP4) return widen(frag_nt4(lb, wn * 128 + b * 16, s, lane));
-      else if constexpr (TB) return frag_t8<DBN>(lb, wn * 128 + b * 16, lane);
-      else return frag_nt8(lb, wn * 128 + b * 16, lane);
+        if constexpr (FP4) return widen(lds_read16(lb + L.b[0] + s * 4096 + b * 1024));
+        else return rd8(lb, L.b[0], L.b[1], b * 2048);
+      } else if constexpr (FP4) {
+        return widen(lds_read16(lb + L.b[s] + b * 2048));
+      } else if constexpr (TB) {
+        const uint32_t o[4] = {L.bt[0][b], L.bt[1][b], L.bt[2][b], L.bt[3][b]};
+        return rdt(lb, o);
+      } else return rd8(lb, L.b[0], L.b[1], b * 2048);
     };
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       v8i bf[FN];
+      int sb[FN];
 #pragma unroll
-      for (int b = 0; b < FN; ++b) bf[b] = read_b(s, b);
-      if (s == 0 && st + 1 < nst) {
-        load_stage(st + 1, smem + ((st + 1) & 1) * DSTAGE);
-        load_scales(st + 1);
+      for (int b = 0; b < FN; ++b) {
+        bf[b] = read_b(s, b);
+        sb[b] = E8M0_ONE_X4;
+        if constexpr (MX) {
+          if constexpr (PSB) {
+            const uint32_t word = lds_u32(ls + SB_OFF + L.sb + b * 4);
+            sb[b] = (int)(word >> (8 * ((st * KS + s) & 3)));
+          } else {
+            const uint32_t word = lds_u32(ls + SB_OFF + s * 1024 + L.sb + b * 64);
+            sb[b] = (int)(word >> (8 * c.q));
+          }
+        }
       }
       v8i af = read_a(s, 0);
 #pragma unroll
@@ -331,29 +465,134 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(DenseArgs p) {
         v8i af_next;
         if (a + 1 < FM) af_next = read_a(s, a + 1);
         int sa = E8M0_ONE_X4;
-        if constexpr (SMODE == SM_MX) sa = (int)(sa_c[a][s] >> (8 * q));
-#pragma unroll
-        for (int b = 0; b < FN; ++b) {
-          int sb = E8M0_ONE_X4;
-          if constexpr (SMODE == SM_MX) {
-            if constexpr (PSB) sb = (int)(sb_c[b][s] >> (8 * ((st * KS + s) & 3)));
-            else sb = (int)(sb_c[b][s] >> (8 * q));
-          }
-          // First operand = B tile: the result lane holds 4 consecutive n.
-          acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb, sa);
+        if constexpr (MX) {
+          const uint32_t word = lds_u32(ls + SA_OFF + s * 1024 + L.sa + a * 64);
+          sa = (int)(word >> (8 * c.q));
         }
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+          // First operand = B tile: the result lane holds 4 consecutive n.
+          acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb[b], sa);
         if (a + 1 < FM) af = af_next;
+        // keep the A reads one tile ahead, not hoisted further (registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmem();
-    __syncthreads();
   }
 
-  // ---- epilogue
+  // One K step: consume stage st from slot c while stage st+1 streams into
+  // slot n and the lines of stage st+PF are pulled toward L2.  The DMAs are
+  // invisible to the compiler (dma_asm), so the waits below are the only
+  // ones: the DMA into slot n is issued after the barrier that retired every
+  // wave's reads of it, and slot n is read only after the wait + barrier.
+  __device__ static inline void step(const Ctx &c, const Lanes &L, int st, const uint8_t *sc,
+                                     uint32_t sn, v4f (&acc)[FM][FN]) {
+    issue(c, st + 1, sn);
+    prefetch(c, st + PF);
+    compute(c, L, st, sc, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage st+1 (this wave's part) has landed once only the prefetch touch
+    // issued after it is outstanding; the barrier publishes every wave's DMA.
+    wait_vmem_le<1>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ static inline void run(const Ctx &c, v4f (&acc)[FM][FN], uint8_t *smem) {
+    Lanes L;
+    lane_offsets(c, L);
+    const uint8_t *s0 = smem, *s1 = smem + SLOT;
+    const uint32_t a0 = c.lds0, a1 = a0 + SLOT;
+    issue(c, 0, a0);
+#pragma unroll
+    for (int j = 1; j < PF; ++j) prefetch(c, j);
+    wait_vmem_le<PF - 1>();
+    __syncthreads();
+    int st = 0;
+    for (; st + 2 <= c.nst; st += 2) {
+      step(c, L, st, s0, a1, acc);
+      step(c, L, st + 1, s1, a0, acc);
+    }
+    if (st < c.nst) step(c, L, st, s0, a1, acc);
+    // Drain the last DMAs (they write LDS) before the epilogue reuses it.
+    wait_vmem_le<0>();
+  }
+};
+
+template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
+__global__ __launch_bounds__(DNW8 * 64, 1) void dense_kernel(DenseArgs p) {
+  typedef DenseLoop<FA, FB, SMODE, TA, TB, PSB> L;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS_BYTES];
+
+  typename L::Ctx c;
+  c.p = &p;
+  c.lane = threadIdx.x & 63;
+  c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
+  c.wm = c.w >> 2;
+  c.wn = c.w & 3;
+  c.i16 = c.lane & 15;
+  c.q = c.lane >> 4;
+  int tm, tn;
+  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  c.m0 = (int64_t)tm * DBM;
+  c.n0 = (int64_t)tn * DBN;
+  c.KB = L::FP4 ? p.K / 2 : p.K;
+  c.nst = (int)(c.KB / 128);
+  c.sk32 = p.K / 32;
+  c.nks = p.K / 128;
+  c.ngrp = (p.K + 511) / 512;
+  c.rzero = rsrc4(p.B, 0);
+  {
+    // A: rows m0.. (K-contiguous) or columns m0.. of [K, M]; B likewise.
+    const int64_t abase = TA ? c.m0 : c.m0 * c.KB;
+    c.ra = rsrc4(p.A + abase, clamp_records(p.a_bytes - abase));
+    int64_t bbase;
+    if constexpr (PSB) bbase = 0;
+    else bbase = TB ? c.n0 : c.n0 * c.KB;
+    c.rb = rsrc4(p.B + bbase, clamp_records(p.b_bytes - bbase));
+    L::dma_offsets(TA, c.lane, c.KB, p.M, c.vo_a);
+    L::dma_offsets(TB, c.lane, c.KB, p.N, c.vo_b);
+    // prefetch: waves 0-3 touch the 256 lines of the A tile, 4-7 those of B
+    const int idx = 64 * (c.w & 3) + c.lane;
+    if (c.w < 4) {
+      c.rp = c.ra;
+      c.vo_p = TA ? (uint32_t)((idx >> 1) * p.M + (idx & 1) * 128) : (uint32_t)(idx * c.KB);
+    } else {
+      c.rp = c.rb;
+      if constexpr (PSB) c.vo_p = (uint32_t)((idx >> 6) * c.nks * L::CGB + (idx & 63) * 128);
+      else c.vo_p = TB ? (uint32_t)((idx >> 1) * p.N + (idx & 1) * 128) : (uint32_t)(idx * c.KB);
+    }
+  }
+  c.rs = c.rzero;
+  c.vo_s = 0;
+  if constexpr (L::MX) {
+    if (c.w < 4) {
+      const int64_t b = (c.m0 + 64 * c.w) * c.sk32;
+      c.rs = rsrc4((const uint8_t *)p.sA + b, clamp_records(p.sa_bytes - b));
+      c.vo_s = (uint32_t)(c.lane * c.sk32);
+    } else if constexpr (PSB) {
+      const int64_t b = (c.n0 / 64 + (c.w - 4)) * c.ngrp * 1024;
+      c.rs = rsrc4((const uint8_t *)p.sB + b, clamp_records(p.sb_bytes - b));
+      c.vo_s = (uint32_t)(c.lane * 16);
+    } else {
+      const int64_t b = (c.n0 + 64 * (c.w - 4)) * c.sk32;
+      c.rs = rsrc4((const uint8_t *)p.sB + b, clamp_records(p.sb_bytes - b));
+      c.vo_s = (uint32_t)(c.lane * c.sk32);
+    }
+  }
+
+  v4f acc[L::FM][L::FN];
+#pragma unroll
+  for (int a = 0; a < L::FM; ++a)
+#pragma unroll
+    for (int b = 0; b < L::FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  c.lds0 = lds_addr(smem);
+  L::run(c, acc, smem);
+
   float alpha = 1.0f;
   if constexpr (SMODE == SM_TENSOR) alpha = *(const float *)p.sA * *(const float *)p.sB;
-  store_tile<DBM, DBN, FM, FN>(acc, alpha, smem, p.D, m0, n0, p.M, p.N, wm, wn);
+  store_tile<DBM, DBN, L::FM, L::FN, L::NW * 64>(acc, alpha, smem, p.D, c.m0, c.n0, p.M, p.N, c.wm, c.wn);
 }
 
 }  // namespace mxg

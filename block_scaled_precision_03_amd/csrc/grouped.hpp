@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256, 1) void grouped_kernel(GroupedArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
   const int wm = w >> 1, wn = w & 1;
   const int i16 = lane & 15;
   const int tm_flat = blockIdx.x / p.tiles_n;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, 1) void grouped_kernel(GroupedArgs p) {
   };
   auto load_stage = [&](int st, uint8_t *buf) {
     load_nt<BM, 4>(p.XQ, p.totM * K, row0, K, st, buf, w, lane);
-    if constexpr (PSB) load_ps<false, BN, 4>(Wg, wbytes, n0 / 16, kb_n, st, buf + BM * 128, w, lane);
+    if constexpr (PSB) load_ps<BN, 4>(Wg, wbytes, n0 / 64, kb_n, st, buf + BM * 128, w, lane);
     else load_nt<BN, 4>(Wg, wbytes, n0, K, st, buf + BM * 128, w, lane);
   };
 

@@ -91,9 +91,9 @@ def test_preshuffle_sizes():
     m = _mx()
     assert m.preshuffle_b_bytes(0, 4096, 4096) == 4096 * 4096
     assert m.preshuffle_b_bytes(4, 8192, 8192) == 8192 * 8192 // 2
-    assert m.preshuffle_b_bytes(0, 100, 256) == 112 * 256
+    assert m.preshuffle_b_bytes(0, 100, 256) == 128 * 256          # rows padded to 64
     assert m.preshuffle_scales_bytes(4096, 4096) == 4096 * 4096 // 32
-    assert m.preshuffle_scales_bytes(11008, 11008) == 688 * 22 * 256
+    assert m.preshuffle_scales_bytes(11008, 11008) == 172 * 22 * 1024
 
 
 def test_ops_reject_bad_args_before_device_use():
