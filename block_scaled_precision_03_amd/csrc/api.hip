@@ -45,6 +45,21 @@ int launch_status() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of the current device: the grid size of the persistent dense
+// kernel (one workgroup per compute unit).  Queried once per device.
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 }  // namespace
 
 extern "C" const char *mxgemm_status_string(int s) {
@@ -65,6 +80,7 @@ extern "C" int mxgemm_init(void) {
   hipFuncAttributes attr;
   if (hipFuncGetAttributes(&attr, (const void *)dense_kernel<F_E4M3, F_E4M3, SM_MX, false, false, false>) != hipSuccess)
     return MXG_ERR_HIP;
+  (void)cu_count();
   return MXG_OK;
 }
 
@@ -169,8 +185,10 @@ extern "C" int mxgemm_run(int fmtA, int fmtB, int layout, const void *A, const v
   a.sb_bytes = fb.mx ? (psb ? mxgemm_preshuffle_scales_bytes(N, K) : N * (K / 32)) : 4;
   a.tiles_m = (int)cdiv(M, DBM);
   a.tiles_n = (int)cdiv(N, DBN);
-  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-  if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  // Persistent grid: one workgroup per compute unit, each walking its tiles.
+  const int64_t blocks = tiles < cu_count() ? tiles : cu_count();
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(DNW8 * 64), 0, stream, a);
   return launch_status();
 }

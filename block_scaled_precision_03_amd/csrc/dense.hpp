@@ -201,24 +201,6 @@ __device__ inline void store_tile(const v4f (&acc)[FM][FN], float alpha, uint8_t
   }
 }
 
-// ---------------------------------------------------------------------------
-// Block -> output tile.  Consecutive workgroups land on different XCDs
-// (round-robin over 8); remap so that each XCD works on a compact band of
-// tiles, then walk tiles in groups of 8 tile-rows for L2 reuse.
-__device__ inline void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int nb = tiles_m * tiles_n;
-  int b = bid;
-  if ((nb & 7) == 0) b = (bid & 7) * (nb >> 3) + (bid >> 3);
-  constexpr int GM = 8;
-  const int per_group = GM * tiles_n;
-  const int g = b / per_group;
-  const int first = g * GM;
-  const int rows = min(GM, tiles_m - first);
-  const int in = b - g * per_group;
-  tm = first + in % rows;
-  tn = in / rows;
-}
-
 // vmcnt(n) with expcnt/lgkmcnt left alone (n <= 63).
 template <int N>
 __device__ inline void wait_vmem_le() {
@@ -231,13 +213,15 @@ __device__ inline void wait_vmem_le() {
 // SIMD so that one wave's LDS or barrier stall is covered by the other's
 // matrix work.  Two LDS stages of 128 bytes of K per row for A and B (plus
 // MX scales) are double buffered; every K step streams the next stage in by
-// DMA and touches the lines of the stage PF steps ahead so that they sit in
-// L2 by the time they are fetched.
+// DMA while the current one feeds the matrix cores.
 //
-// Every LDS access of the K loop goes through a restrict pointer per buffer
-// (two ring slots, their scale slots, the prefetch dump): the compiler can
-// then tell that the DMA filling one slot does not alias the reads of the
-// other, and does not stall those reads on it.
+// The kernel is persistent: one workgroup per compute unit walks a list of
+// output tiles, and the K steps of consecutive tiles form one unbroken
+// pipeline.  The stage after a tile's last K step is the first stage of the
+// next tile, and the finished tile's accumulators go out as BF16 straight
+// from registers while that stage streams in, so no compute unit idles on an
+// epilogue, a workgroup launch or a cold first stage between tiles.
+//
 template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
 struct DenseLoop {
   static constexpr bool FP4 = (FA == F_E2M1);
@@ -245,30 +229,60 @@ struct DenseLoop {
   static constexpr int NW = DNW8;
   static constexpr int KS = FP4 ? 2 : 1;        // 128-element K steps per stage
   static constexpr int FM = 8, FN = 4;          // wave tile 128 x 64
-  static constexpr int PF = 3;                  // L2 prefetch distance (stages)
   static constexpr int AB = DBM * 128;          // A bytes per stage
   static constexpr int STAGE = (DBM + DBN) * 128;
   static constexpr int SA_OFF = 0, SB_OFF = KS * 1024;
   static constexpr int SSTAGE = MX ? KS * 1024 + (PSB ? 4096 : KS * 1024) : 0;
-  static constexpr int SLOT = STAGE + SSTAGE;   // [A tile][B tile][scales]
-  static constexpr int DUMP = 2 * SLOT;         // prefetch dump, 256 B per wave
-  static constexpr int LDS_BYTES = DUMP + NW * 256;
+  // LDS: [A slot 0][A slot 1][B slot 0][B slot 1][scales slot 0][slot 1].
+  // A read offset within either slot then fits the 16-bit offset field of a
+  // DS instruction on top of one per-lane base register per operand.
+  static constexpr int B_REG = 2 * AB, S_REG = 4 * AB;
+  static constexpr int LDS_BYTES = S_REG + 2 * SSTAGE;
   static constexpr int CGB = FP4 ? 4096 : 8192;
 
   // Loop-invariant state.  Every global load of the loop is one buffer
-  // instruction: a resource fixed for the kernel, a per-lane offset fixed
-  // for the kernel (VGPR) and a uniform per-stage offset (SGPR).
+  // instruction: a resource fixed for the tile, a per-lane offset fixed for
+  // the kernel (VGPR) and a uniform per-stage offset (SGPR).
   struct Ctx {
     const DenseArgs *p;
     int lane, w, wm, wn, i16, q, nst;
-    int64_t m0, n0, KB, sk32, nks, ngrp;
-    u32x4 ra, rb, rs, rzero;                   // rs: this wave's scale source
-    u32x4 rp;                                  // this wave's prefetch source
+    int64_t KB, sk32, nks, ngrp;
     uint32_t vo_a[2], vo_b[2];     // operand DMA offsets (by block parity)
-    uint32_t vo_p;                 // prefetch line offset
     uint32_t vo_s;                 // scale DMA offset
     uint32_t lds0;                 // LDS address of the kernel's LDS block (uniform)
   };
+
+  // The DMA sources of one output tile (uniform).
+  struct Tile {
+    int64_t m0, n0;
+    u32x4 ra, rb, rs;              // rs: this wave's scale source
+  };
+
+  __device__ static inline void set_tile(const Ctx &c, int64_t m0, int64_t n0, Tile &t) {
+    const DenseArgs &p = *c.p;
+    t.m0 = m0;
+    t.n0 = n0;
+    // A: rows m0.. (K-contiguous) or columns m0.. of [K, M]; B likewise.
+    const int64_t abase = TA ? m0 : m0 * c.KB;
+    t.ra = rsrc4(p.A + abase, clamp_records(p.a_bytes - abase));
+    int64_t bbase;
+    if constexpr (PSB) bbase = 0;
+    else bbase = TB ? n0 : n0 * c.KB;
+    t.rb = rsrc4(p.B + bbase, clamp_records(p.b_bytes - bbase));
+    t.rs = (u32x4){0u, 0u, 0u, 0u};
+    if constexpr (MX) {
+      if (c.w < 4) {
+        const int64_t b = (m0 + 64 * c.w) * c.sk32;
+        t.rs = rsrc4((const uint8_t *)p.sA + b, clamp_records(p.sa_bytes - b));
+      } else if constexpr (PSB) {
+        const int64_t b = (n0 / 64 + (c.w - 4)) * c.ngrp * 1024;
+        t.rs = rsrc4((const uint8_t *)p.sB + b, clamp_records(p.sb_bytes - b));
+      } else {
+        const int64_t b = (n0 + 64 * (c.w - 4)) * c.sk32;
+        t.rs = rsrc4((const uint8_t *)p.sB + b, clamp_records(p.sb_bytes - b));
+      }
+    }
+  }
 
   // Per-lane offsets of the 1 KiB wave DMAs of an operand tile.
   //  K-contiguous rows (256 rows x 128 B): DMA block blk covers rows
@@ -307,71 +321,55 @@ struct DenseLoop {
     });
   }
 
-  // DMA of stage st (operands and MX scales) into the ring slot at LDS
-  // address `slot`.  A stage past the last one issues the same instructions
-  // against an empty range.
-  __device__ static inline void issue(const Ctx &c, int st, uint32_t slot) {
+  // DMA of stage st of tile t (operands and MX scales) into ring slot si.
+  __device__ static inline void issue(const Ctx &c, const Tile &t, int st, int si) {
     const DenseArgs &p = *c.p;
-    const bool real = st < c.nst;
-    load_tile<TA>(c, real ? c.ra : c.rzero, c.vo_a, c.KB, p.M, st, slot);
+    const uint32_t slot = c.lds0 + (uint32_t)si * AB;
+    const uint32_t sslot = c.lds0 + S_REG + (uint32_t)si * SSTAGE;
+    load_tile<TA>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
     if constexpr (PSB) {
       // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
-      const uint32_t soff0 = (uint32_t)((c.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB) +
+      const uint32_t soff0 = (uint32_t)((t.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB) +
                              (uint32_t)((c.w >> 1) * c.nks * CGB) + (uint32_t)(c.w & 1) * 4096u;
-      const uint32_t base = slot + AB + (uint32_t)c.w * 4096u;
-      const u32x4 rb = real ? c.rb : c.rzero;
+      const uint32_t base = slot + B_REG + (uint32_t)c.w * 4096u;
+      const u32x4 rb = t.rb;
       static_for<0, 4>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         dma_asm<16, j * 1024>(base, rb, (uint32_t)(c.lane * 16), soff0 + j * 1024);
       });
     } else {
-      load_tile<TB>(c, real ? c.rb : c.rzero, c.vo_b, c.KB, p.N, st, slot + AB);
+      load_tile<TB>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
     }
     if constexpr (MX) {
       // waves 0-3: A scales of rows 64w..; waves 4-7: B scales (plain: rows
       // 64(w-4)..; preshuffled: column group w-4, four k steps per word).
-      const u32x4 r = real ? c.rs : c.rzero;
+      const u32x4 r = t.rs;
       if (c.w < 4 || !PSB) {
-        const uint32_t dst = slot + STAGE + (c.w < 4 ? SA_OFF : SB_OFF) + (uint32_t)(c.w & 3) * 256u;
+        const uint32_t dst = sslot + (c.w < 4 ? SA_OFF : SB_OFF) + (uint32_t)(c.w & 3) * 256u;
         static_for<0, KS>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
           dma_asm<4, s * 1024>(dst, r, c.vo_s, (uint32_t)(4 * ((int64_t)st * KS + s)));
         });
       } else {
         const uint32_t soff = (uint32_t)((((int64_t)st * KS) / 4) * 1024);
-        dma_asm<16>(slot + STAGE + SB_OFF + (uint32_t)(c.w - 4) * 1024u, r, c.vo_s, soff);
+        dma_asm<16>(sslot + SB_OFF + (uint32_t)(c.w - 4) * 1024u, r, c.vo_s, soff);
       }
     }
-  }
-
-  // Touch every 128-byte line of stage st's A tile (waves 0-3) or B tile
-  // (waves 4-7): one 4-byte DMA per line into a dump area nobody reads, so
-  // that the real DMA PF stages later hits in L2.
-  __device__ static inline void prefetch(const Ctx &c, int st) {
-    const DenseArgs &p = *c.p;
-    const bool real = st < c.nst;
-    uint32_t soff;
-    if (c.w < 4) {
-      soff = TA ? (uint32_t)(128 * (int64_t)st * p.M) : (uint32_t)(128 * st);
-    } else {
-      if constexpr (PSB) soff = (uint32_t)((c.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB);
-      else if constexpr (TB) soff = (uint32_t)(128 * (int64_t)st * p.N);
-      else soff = (uint32_t)(128 * st);
-    }
-    dma_asm<4>(c.lds0 + DUMP + (uint32_t)c.w * 256u, real ? c.rp : c.rzero, c.vo_p, soff);
   }
 
   __device__ static inline uint32_t lds_u32(const uint8_t *p) { return lds_load_u32(p); }
 
   // Per-lane LDS byte offsets of the fragment reads, fixed for the kernel.
-  // Each read is then base pointer + lane offset + a compile-time constant,
-  // which the compiler folds into the 16-bit offset field of the DS
-  // instruction (the lane offsets are masked to 16 bits so that it knows they
-  // are small), instead of keeping one address register per fragment.
+  // Each read is then lane offset + a compile-time constant (slot, tile,
+  // half), which the compiler folds into the 16-bit offset field of the DS
+  // instruction (the lane offsets are masked so that it knows they are
+  // small and non-negative), instead of keeping one address register per
+  // fragment and slot.
+  static constexpr uint32_t LMASK = 0x3FFFFu;
   struct Lanes {
     uint32_t a[2], b[2];           // FP8 K-contiguous / preshuffled: the two 16-byte halves;
                                    // FP4: the two k steps of the stage
-    uint32_t at[4][8], bt[4][4];   // transposed: per 8-byte piece t and tile
+    uint32_t at[4], bt[4];         // transposed: per 8-byte piece t, tile 0
     uint32_t sa, sb;               // scale words
   };
 
@@ -383,27 +381,23 @@ struct DenseLoop {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int piece = FP4 ? 4 * h + q : q + 4 * h;
-      L.a[h] = ((uint32_t)((c.wm * 128 + i) * 128 + ((piece ^ f) << 4))) & 0xFFFFu;
-      if constexpr (PSB) L.b[h] = ((uint32_t)(c.wn * 8192 + (FP4 ? 0 : h * 1024) + c.lane * 16)) & 0xFFFFu;
-      else L.b[h] = ((uint32_t)((c.wn * 64 + i) * 128 + ((piece ^ f) << 4))) & 0xFFFFu;
+      L.a[h] = ((uint32_t)((c.wm * 128 + i) * 128 + ((piece ^ f) << 4))) & LMASK;
+      if constexpr (PSB) L.b[h] = ((uint32_t)(B_REG + c.wn * 8192 + (FP4 ? 0 : h * 1024) + c.lane * 16)) & LMASK;
+      else L.b[h] = ((uint32_t)(B_REG + (c.wn * 64 + i) * 128 + ((piece ^ f) << 4))) & LMASK;
     }
-    // Transposed tiles (256 B per k-row): piece t of tile x.
+    // Transposed tiles (256 B per k-row): piece t of tile 0.  Tile x sits x
+    // 16-byte chunks further, and since the chunk index is XOR-swizzled by
+    // kk%8 in its low three bits, its offset is the tile-0 offset ^ (x << 4).
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kk = 16 * q + 8 * (t & 1) + 64 * (t >> 1) + (i >> 1);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int ca = c.wm * 8 + x;                 // 16-byte column chunk of A tile x
-        L.at[t][x] = ((uint32_t)(kk * 256 + ((ca ^ (kk & 7)) << 4) + ((i & 1) << 3))) & 0xFFFFu;
-        if (x < 4) {
-          const int cb = c.wn * 4 + x;
-          L.bt[t][x] = ((uint32_t)(kk * 256 + ((cb ^ (kk & 7)) << 4) + ((i & 1) << 3))) & 0xFFFFu;
-        }
-      }
+      const int ca = c.wm * 8, cb = c.wn * 4;
+      L.at[t] = ((uint32_t)(kk * 256 + ((ca ^ (kk & 7)) << 4) + ((i & 1) << 3))) & LMASK;
+      L.bt[t] = ((uint32_t)(B_REG + kk * 256 + ((cb ^ (kk & 7)) << 4) + ((i & 1) << 3))) & LMASK;
     }
-    L.sa = ((uint32_t)((c.wm * 128 + i) * 4)) & 0xFFFFu;
-    if constexpr (PSB) L.sb = ((uint32_t)(c.wn * 1024 + c.lane * 16)) & 0xFFFFu;
-    else L.sb = ((uint32_t)((c.wn * 64 + i) * 4)) & 0xFFFFu;
+    L.sa = ((uint32_t)(S_REG + (c.wm * 128 + i) * 4)) & LMASK;
+    if constexpr (PSB) L.sb = ((uint32_t)(S_REG + c.wn * 1024 + c.lane * 16)) & LMASK;
+    else L.sb = ((uint32_t)(S_REG + (c.wn * 64 + i) * 4)) & LMASK;
   }
 
   __device__ static inline v8i rd8(const uint8_t *base, uint32_t lo, uint32_t hi, int imm) {
@@ -421,12 +415,14 @@ struct DenseLoop {
   }
 
   __device__ static inline void compute(const Ctx &c, const Lanes &L, int st,
-                                        const uint8_t *slot, v4f (&acc)[FM][FN]) {
-    const uint8_t *la = slot, *lb = slot + AB, *ls = slot + STAGE;
+                                        const uint8_t *smem, int si, v4f (&acc)[FM][FN]) {
+    // The B and scale lane offsets include their regions' bases.
+    const uint8_t *la = smem + si * AB, *lb = smem + si * AB, *ls = smem + si * SSTAGE;
     auto read_a = [&](int s, int a) -> v8i {
       if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
       else if constexpr (TA) {
-        const uint32_t o[4] = {L.at[0][a], L.at[1][a], L.at[2][a], L.at[3][a]};
+        const uint32_t x = (uint32_t)a << 4;
+        const uint32_t o[4] = {L.at[0] ^ x, L.at[1] ^ x, L.at[2] ^ x, L.at[3] ^ x};
         return rdt(la, o);
       } else return rd8(la, L.a[0], L.a[1], a * 2048);
     };
@@ -437,7 +433,8 @@ struct DenseLoop {
       } else if constexpr (FP4) {
         return widen(lds_read16(lb + L.b[s] + b * 2048));
       } else if constexpr (TB) {
-        const uint32_t o[4] = {L.bt[0][b], L.bt[1][b], L.bt[2][b], L.bt[3][b]};
+        const uint32_t x = (uint32_t)b << 4;
+        const uint32_t o[4] = {L.bt[0] ^ x, L.bt[1] ^ x, L.bt[2] ^ x, L.bt[3] ^ x};
         return rdt(lb, o);
       } else return rd8(lb, L.b[0], L.b[1], b * 2048);
     };
@@ -480,49 +477,148 @@ struct DenseLoop {
     }
   }
 
-  // One K step: consume stage st from slot c while stage st+1 streams into
-  // slot n and the lines of stage st+PF are pulled toward L2.  The DMAs are
-  // invisible to the compiler (dma_asm), so the waits below are the only
-  // ones: the DMA into slot n is issued after the barrier that retired every
-  // wave's reads of it, and slot n is read only after the wait + barrier.
-  __device__ static inline void step(const Ctx &c, const Lanes &L, int st, const uint8_t *sc,
-                                     uint32_t sn, v4f (&acc)[FM][FN]) {
-    issue(c, st + 1, sn);
-    prefetch(c, st + PF);
-    compute(c, L, st, sc, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    // Stage st+1 (this wave's part) has landed once only the prefetch touch
-    // issued after it is outstanding; the barrier publishes every wave's DMA.
-    wait_vmem_le<1>();
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+  // The finished tile's accumulators (times alpha) as BF16, stored straight
+  // from registers: lane (i, q) of matrix-core tile (a, b) holds row
+  // wm*128 + 16a + i, columns wn*64 + 16b + 4q .. +3, i.e. one 8-byte store.
+  // Edge tiles mask rows >= M and columns >= N element by element.
+  __device__ static inline void epilogue(const Ctx &c, int64_t m0, int64_t n0, float alpha,
+                                         const v4f (&acc)[FM][FN]) {
+    const DenseArgs &p = *c.p;
+    const int64_t N = p.N;
+    const int64_t row0 = m0 + c.wm * (FM * 16) + c.i16;
+    const int64_t col0 = n0 + c.wn * (FN * 16) + 4 * c.q;
+    const bool full = m0 + DBM <= p.M && n0 + DBN <= N && (N & 3) == 0;
+    uint16_t *base = p.D + row0 * N + col0;
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+#pragma unroll
+      for (int b = 0; b < FN; ++b) {
+        const v4f v = acc[a][b];
+        const uint32_t lo = pack_bf16x2(v.x * alpha, v.y * alpha);
+        const uint32_t hi = pack_bf16x2(v.z * alpha, v.w * alpha);
+        uint16_t *dst = base + (int64_t)(a * 16) * N + b * 16;
+        if (full) {
+          *(v2i *)dst = (v2i){(int)lo, (int)hi};
+        } else if (row0 + a * 16 < p.M) {
+          const int64_t col = col0 + b * 16;
+          if ((N & 3) == 0 && col + 4 <= N) {
+            *(v2i *)dst = (v2i){(int)lo, (int)hi};
+          } else {
+            const uint32_t u[2] = {lo, hi};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < N) dst[e] = (uint16_t)(u[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
   }
 
-  __device__ static inline void run(const Ctx &c, v4f (&acc)[FM][FN], uint8_t *smem) {
+  // The K loop over every tile of this workgroup.  Global step g (K step k
+  // of tile t, g = t*nst + k) consumes its stage from slot g%2 while the
+  // next stage (K step k+1 of tile t, or the first K step of tile t+1)
+  // streams into the other slot.  The DMAs are invisible to the compiler
+  // (dma_asm), so the waits below are the only ones: the DMA into a slot is
+  // issued after the barrier that retired every wave's reads of it, and the
+  // slot is read only after the wait + barrier.  A tile's epilogue runs once
+  // its last step is done, with the next tile's first stage already in LDS;
+  // its stores drain during that tile's first step.
+  template <class TileAt>
+  __device__ static inline void run(const Ctx &c, int ntiles, TileAt tile_at, float alpha,
+                                    uint8_t *smem) {
     Lanes L;
     lane_offsets(c, L);
-    const uint8_t *s0 = smem, *s1 = smem + SLOT;
-    const uint32_t a0 = c.lds0, a1 = a0 + SLOT;
-    issue(c, 0, a0);
+
+    v4f acc[FM][FN];
 #pragma unroll
-    for (int j = 1; j < PF; ++j) prefetch(c, j);
-    wait_vmem_le<PF - 1>();
-    __syncthreads();
-    int st = 0;
-    for (; st + 2 <= c.nst; st += 2) {
-      step(c, L, st, s0, a1, acc);
-      step(c, L, st + 1, s1, a0, acc);
-    }
-    if (st < c.nst) step(c, L, st, s0, a1, acc);
-    // Drain the last DMAs (they write LDS) before the epilogue reuses it.
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    int tm, tn;
+    tile_at(0, tm, tn);
+    Tile cur;
+    set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, cur);
+    issue(c, cur, 0, 0);
     wait_vmem_le<0>();
+    __syncthreads();
+
+    const int nst = c.nst;
+    for (int t = 0; t < ntiles; ++t) {
+      const bool more = t + 1 < ntiles;
+      if (more) tile_at(t + 1, tm, tn);
+      auto step = [&](int k, int sc, int sn) {
+        if (k + 1 < nst) {
+          issue(c, cur, k + 1, sn);
+        } else if (more) {
+          // first stage of the next tile (its sources are built here, not
+          // kept live through the K loop)
+          Tile nxt;
+          set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, nxt);
+          issue(c, nxt, 0, sn);
+        }
+        compute(c, L, k, smem, sc, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        // The next stage (this wave's part) and the previous epilogue's
+        // stores have landed; the barrier publishes every wave's DMA.
+        wait_vmem_le<0>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      int k = 0;
+      if (((int64_t)t * nst) & 1) {      // odd start: first step from slot 1
+        step(0, 1, 0);
+        k = 1;
+      }
+      for (; k + 2 <= nst; k += 2) {
+        step(k, 0, 1);
+        step(k + 1, 1, 0);
+      }
+      if (k < nst) step(k, 0, 1);
+      epilogue(c, cur.m0, cur.n0, alpha, acc);
+      if (more) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+        set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, cur);
+      }
+    }
   }
 };
+
+// The k-th tile of workgroup bid in a persistent grid of P workgroups: it
+// takes virtual tiles bid, bid + P, bid + 2P, ...  Workgroups are dealt to
+// the eight XCDs round-robin, so within each round of P virtual tiles (the
+// ones that run at the same time) those of one XCD (bid % 8 equal) are
+// remapped to a compact band of the tile order.  The tile order walks groups
+// of 8 tile-rows, column by column, so that the 32 tiles an XCD runs at once
+// share 8 A panels and 4 B panels in its L2.
+__device__ inline void persistent_tile(int bid, int k, int P, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int nb = tiles_m * tiles_n;
+  const int base = k * P;
+  const int size = min(P, nb - base);
+  const int b = base + (((size & 7) == 0) ? (bid & 7) * (size >> 3) + (bid >> 3) : bid);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int g = b / per_group;
+  const int first = g * GM;
+  const int rows = min(GM, tiles_m - first);
+  const int in = b - g * per_group;
+  tm = first + in % rows;
+  tn = in / rows;
+}
 
 template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
 __global__ __launch_bounds__(DNW8 * 64, 1) void dense_kernel(DenseArgs p) {
   typedef DenseLoop<FA, FB, SMODE, TA, TB, PSB> L;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS_BYTES];
+
+  const int nb = p.tiles_m * p.tiles_n;
+  const int P = (int)gridDim.x;
+  const int bid = (int)blockIdx.x;
+  if (bid >= nb) return;
+  const int ntiles = (nb - bid + P - 1) / P;
 
   typename L::Ctx c;
   c.p = &p;
@@ -532,67 +628,31 @@ __global__ __launch_bounds__(DNW8 * 64, 1) void dense_kernel(DenseArgs p) {
   c.wn = c.w & 3;
   c.i16 = c.lane & 15;
   c.q = c.lane >> 4;
-  int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  c.m0 = (int64_t)tm * DBM;
-  c.n0 = (int64_t)tn * DBN;
   c.KB = L::FP4 ? p.K / 2 : p.K;
   c.nst = (int)(c.KB / 128);
   c.sk32 = p.K / 32;
   c.nks = p.K / 128;
   c.ngrp = (p.K + 511) / 512;
-  c.rzero = rsrc4(p.B, 0);
-  {
-    // A: rows m0.. (K-contiguous) or columns m0.. of [K, M]; B likewise.
-    const int64_t abase = TA ? c.m0 : c.m0 * c.KB;
-    c.ra = rsrc4(p.A + abase, clamp_records(p.a_bytes - abase));
-    int64_t bbase;
-    if constexpr (PSB) bbase = 0;
-    else bbase = TB ? c.n0 : c.n0 * c.KB;
-    c.rb = rsrc4(p.B + bbase, clamp_records(p.b_bytes - bbase));
-    L::dma_offsets(TA, c.lane, c.KB, p.M, c.vo_a);
-    L::dma_offsets(TB, c.lane, c.KB, p.N, c.vo_b);
-    // prefetch: waves 0-3 touch the 256 lines of the A tile, 4-7 those of B
-    const int idx = 64 * (c.w & 3) + c.lane;
-    if (c.w < 4) {
-      c.rp = c.ra;
-      c.vo_p = TA ? (uint32_t)((idx >> 1) * p.M + (idx & 1) * 128) : (uint32_t)(idx * c.KB);
-    } else {
-      c.rp = c.rb;
-      if constexpr (PSB) c.vo_p = (uint32_t)((idx >> 6) * c.nks * L::CGB + (idx & 63) * 128);
-      else c.vo_p = TB ? (uint32_t)((idx >> 1) * p.N + (idx & 1) * 128) : (uint32_t)(idx * c.KB);
-    }
-  }
-  c.rs = c.rzero;
+  L::dma_offsets(TA, c.lane, c.KB, p.M, c.vo_a);
+  L::dma_offsets(TB, c.lane, c.KB, p.N, c.vo_b);
   c.vo_s = 0;
   if constexpr (L::MX) {
-    if (c.w < 4) {
-      const int64_t b = (c.m0 + 64 * c.w) * c.sk32;
-      c.rs = rsrc4((const uint8_t *)p.sA + b, clamp_records(p.sa_bytes - b));
-      c.vo_s = (uint32_t)(c.lane * c.sk32);
-    } else if constexpr (PSB) {
-      const int64_t b = (c.n0 / 64 + (c.w - 4)) * c.ngrp * 1024;
-      c.rs = rsrc4((const uint8_t *)p.sB + b, clamp_records(p.sb_bytes - b));
-      c.vo_s = (uint32_t)(c.lane * 16);
-    } else {
-      const int64_t b = (c.n0 + 64 * (c.w - 4)) * c.sk32;
-      c.rs = rsrc4((const uint8_t *)p.sB + b, clamp_records(p.sb_bytes - b));
-      c.vo_s = (uint32_t)(c.lane * c.sk32);
-    }
+    if (c.w < 4 || !PSB) c.vo_s = (uint32_t)(c.lane * c.sk32);
+    else c.vo_s = (uint32_t)(c.lane * 16);
   }
-
-  v4f acc[L::FM][L::FN];
-#pragma unroll
-  for (int a = 0; a < L::FM; ++a)
-#pragma unroll
-    for (int b = 0; b < L::FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
-
   c.lds0 = lds_addr(smem);
-  L::run(c, acc, smem);
 
   float alpha = 1.0f;
   if constexpr (SMODE == SM_TENSOR) alpha = *(const float *)p.sA * *(const float *)p.sB;
-  store_tile<DBM, DBN, L::FM, L::FN, L::NW * 64>(acc, alpha, smem, p.D, c.m0, c.n0, p.M, p.N, c.wm, c.wn);
+
+  auto tile_at = [&](int k, int &tm, int &tn) {
+    // Opaque copies: keeps the division set-up of the tile order from being
+    // hoisted out of the tile loop into registers the K loop needs.
+    int P_ = P, tm_ = p.tiles_m, tn_ = p.tiles_n;
+    asm volatile("" : "+s"(P_), "+s"(tm_), "+s"(tn_));
+    persistent_tile(bid, k, P_, tm_, tn_, tm, tn);
+  };
+  L::run(c, ntiles, tile_at, alpha, smem);
 }
 
 }  // namespace mxg

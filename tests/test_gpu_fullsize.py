@@ -1,0 +1,81 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the
+benchmark times (MXFP8 and MXFP4 with preshuffled B; tensor-wise FP8 in the
+three layouts of a linear layer's forward, data-gradient and
+weight-gradient GEMMs).  The oracle computes sampled output entries one by
+one: random entries, the four corners, the last row and column, and one
+entry per tile row and tile column."""
+import numpy as np
+import pytest
+
+import oracle
+from block_scaled_precision_03_amd import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+E4, E5, F4 = 0, 1, 4
+T4, T5 = 16, 17
+NT, NN, TN = 0, 1, 2
+
+
+def _check_sampled(D, opA, opB, M, N, K, what, count=4000):
+    d = H.bf16_to_f64(D)
+    rng = np.random.default_rng(M + 3 * N + 5 * K)
+    im, inn = H.sample_indices(rng, M, N, count)
+    im = np.concatenate([im, np.arange(0, M, 256), rng.integers(0, M, (N + 255) // 256)])
+    inn = np.concatenate([inn, rng.integers(0, N, (M + 255) // 256), np.arange(0, N, 256)])
+    ref = oracle.gemm_entries(opA.orc(), opB.orc(), M, N, K, im, inn)
+    H.assert_close(d[im, inn], ref, what)
+
+
+# MXFP8 NT, LLM shapes: activations N(0,1), weights 0.02 N(0,1).
+C2 = [(4096, 4096, 4096), (4096, 14336, 4096), (4096, 4096, 14336),
+      (16384, 4096, 4096), (16384, 14336, 4096), (16384, 4096, 14336)]
+
+
+@pytest.mark.parametrize("M,N,K", C2)
+def test_mxfp8_llm_shapes(M, N, K):
+    ki = 0 if K == 4096 else 1
+    wi = {(4096, 4096): 0, (14336, 4096): 1, (4096, 14336): 2}[(N, K)]
+    x = synth.normal(synth.seed_for(2, 1, ki), (M, K))
+    w = synth.normal(synth.seed_for(2, 2, wi), (N, K), 0.02)
+    opA = H.make_operand(E4, x, False)
+    opB = H.make_operand(E4, w, False)
+    del x, w
+    D = H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=True)
+    _check_sampled(D, opA, opB, M, N, K, "mxfp8 %dx%dx%d" % (M, N, K))
+
+
+# Tensor-wise FP8 (E4M3 A x E5M2 B) for a 4096 -> 11008 linear at 8192
+# tokens: forward Y = X W^T (NT), data gradient dX = dY W (NN), weight
+# gradient dW = dY^T X (TN).
+C3 = [
+    ("fwd", NT, 8192, 11008, 4096),
+    ("dgrad", NN, 8192, 4096, 11008),
+    ("wgrad", TN, 11008, 4096, 8192),
+]
+
+
+@pytest.mark.parametrize("name,layout,M,N,K", C3)
+def test_tensorwise_linear_layer(name, layout, M, N, K):
+    idx = [c[0] for c in C3].index(name)
+    ta = layout == TN
+    tb = layout in (NN, TN)
+    a = synth.normal(synth.seed_for(3, 1, idx), (M, K))
+    b = synth.normal(synth.seed_for(3, 2, idx), (N, K), 0.02)
+    opA = H.make_operand(T4, a, ta)
+    opB = H.make_operand(T5, b, tb)
+    del a, b
+    D = H.run_dense(layout, opA, opB, M, N, K)
+    _check_sampled(D, opA, opB, M, N, K, "tensor-wise %s" % name)
+
+
+def test_mxfp4_8192_cube():
+    M = N = K = 8192
+    x = synth.normal(synth.seed_for(5, 1), (M, K))
+    w = synth.normal(synth.seed_for(5, 2), (N, K))
+    opA = H.make_operand(F4, x, False)
+    opB = H.make_operand(F4, w, False)
+    del x, w
+    D = H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=True)
+    _check_sampled(D, opA, opB, M, N, K, "mxfp4 8192^3")
