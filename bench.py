@@ -7,12 +7,21 @@ one mxgemm_run call on weights preshuffled once before timing.  Inputs are
 seeded synthetic data resident in HBM before the timed region.
 
 Also measured (reported beside the headline, not part of `value`): the
-grouped groupwise FP8 GEMM (G=8) in microseconds per call, and the CPU
-oracle on a bounded sample of the same workload.
+grouped groupwise FP8 GEMM (G=8) in microseconds per call, tensor-wise FP8
+GEMMs of a 4096 -> 11008 linear layer at 8192 tokens (forward NT, data
+gradient NN, weight gradient TN), the MXFP4 8192^3 GEMM, and the CPU oracle
+on a bounded sample of the MXFP8 workload.
+
+`roofline` describes the dominant kernel (the MXFP8 NT kernel with
+preshuffled B): algorithmic FLOPs per launch (2MNK) over its mean launch
+duration from HIP events on the launch stream.  Its `traffic` (HBM bytes per
+launch) is read from the committed rocprofv3 counter summary when that
+summary was taken from the current kernel sources, else null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-grouped]
-       [--no-cpu] [--only-step]
+       [--no-cpu] [--no-extra] [--only-step] [--copy-probe]
 """
+import hashlib
 import argparse
 import json
 import os
@@ -25,7 +34,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MXFP8_TFLOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 FLOP/clk/CU (dense)
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_MXFP4_TFLOPS = 10066.3
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_mxfp8_nt_psb_llm_shapes_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_03_amd", "csrc", f)
+                  for f in ("common.hpp", "dense.hpp", "api.hip")]
+C3_CASES = [("fwd", 0, 8192, 11008, 4096), ("dgrad", 1, 8192, 4096, 11008),
+            ("wgrad", 2, 11008, 4096, 8192)]
 C2_SHAPES = [(4096, 4096, 4096), (4096, 14336, 4096), (4096, 4096, 14336),
              (16384, 4096, 4096), (16384, 14336, 4096), (16384, 4096, 14336)]
 C4_SHAPES = [(128, 2048, 7168), (1024, 2048, 7168), (16384, 2048, 7168),
@@ -46,7 +62,50 @@ def parse():
     ap.add_argument("--only-step", action="store_true",
                     help="time the MXFP8 step only (for profiler runs)")
     ap.add_argument("--plain-b", action="store_true", help="time with plain (not preshuffled) B")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the tensor-wise FP8 and MXFP4 measurements")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB read + 256 MiB write elementwise kernel "
+                         "(the calibration of the HBM byte counters)")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per launch of the MXFP8 kernel from the committed counter
+    summary, if it was taken from the current kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(torch):
+    """A plain elementwise kernel of known traffic: y = -x over 256 MiB of
+    FP32 reads 256 MiB and writes 256 MiB per launch."""
+    n = 64 << 20
+    x = torch.randn(n, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": True, "read_bytes": 4 * n, "write_bytes": 4 * n,
+                      "launches": 5}), flush=True)
 
 
 def c2_inputs(torch, synth, mxgemm, dev, preshuffle):
@@ -164,6 +223,73 @@ def grouped_bench(torch, synth, mxgemm, dev, reps=50):
     return out
 
 
+def time_calls(torch, call, reps=20, warmup=3):
+    """Mean µs per launch of `call` over `reps` launches (HIP events on the
+    launch stream)."""
+    for _ in range(warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1000.0 / reps
+
+
+def tensorwise_bench(torch, synth, mxgemm, dev):
+    """Tensor-wise FP8 (E4M3 A x E5M2 B, FP32 per-tensor scales) GEMMs of a
+    4096 -> 11008 linear layer at 8192 tokens in its three layouts."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = []
+    for idx, (name, layout, M, N, K) in enumerate(C3_CASES):
+        a = synth.normal(synth.seed_for(3, 1, idx), (M, K))
+        b = synth.normal(synth.seed_for(3, 2, idx), (N, K), 0.02)
+        qa, sa = synth.quant_tensor(a, "e4m3")
+        qb, sb = synth.quant_tensor(b, "e5m2")
+        del a, b
+        if layout == mxgemm.TN:
+            qa = qa.T
+        if layout in (mxgemm.NN, mxgemm.TN):
+            qb = qb.T
+        A, B = t(qa), t(qb)
+        SA, SB = t(np.array([sa], np.float32)), t(np.array([sb], np.float32))
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = time_calls(torch, lambda: mxgemm.run(mxgemm.FP8_E4M3_TENSOR, mxgemm.FP8_E5M2_TENSOR,
+                                                  layout, A, SA, B, SB, D, M, N, K))
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "M": M, "N": N, "K": K,
+                    "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_FP8_TFLOPS})
+        log("tensor-wise %s %s (%d,%d,%d): %.1f us, %.0f TFLOP/s (%.1f%% of FP8 peak)" % (
+            name, out[-1]["layout"], M, N, K, us, tf, 100.0 * tf / PEAK_FP8_TFLOPS))
+        del A, B, D
+    torch.cuda.empty_cache()
+    return out
+
+
+def mxfp4_bench(torch, synth, mxgemm, dev):
+    """MXFP4 NT GEMM, M = N = K = 8192, preshuffled B."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    M = N = K = 8192
+    qa, sa = synth.quant_mx(synth.normal(synth.seed_for(5, 1), (M, K)), "e2m1")
+    qb, sb = synth.quant_mx(synth.normal(synth.seed_for(5, 2), (N, K)), "e2m1")
+    A, SA, Bp, SBp = t(qa), t(sa), t(qb), t(sb)
+    B = torch.empty(mxgemm.preshuffle_b_bytes(mxgemm.MXFP4_E2M1, N, K), dtype=torch.uint8, device=dev)
+    SB = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=dev)
+    mxgemm.preshuffle_b(mxgemm.MXFP4_E2M1, mxgemm.NT, Bp, B, N, K)
+    mxgemm.preshuffle_scales(SBp, SB, N, K)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = time_calls(torch, lambda: mxgemm.run(mxgemm.MXFP4_E2M1, mxgemm.MXFP4_E2M1 | mxgemm.PRESHUFFLED,
+                                              mxgemm.NT, A, SA, B, SB, D, M, N, K))
+    tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    log("mxfp4 8192^3: %.1f us, %.0f TFLOP/s (%.1f%% of FP4 peak)" % (us, tf, 100.0 * tf / PEAK_MXFP4_TFLOPS))
+    del A, B, D
+    torch.cuda.empty_cache()
+    return {"M": M, "N": N, "K": K, "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP4_TFLOPS}
+
+
 def cpu_baseline(synth, target_s=12.0):
     """The FP64 oracle, as it stands, on rows [0, R) of the M=16384,
     N=4096, K=4096 MXFP8 GEMM (dequantize + plain FP64 dot products)."""
@@ -198,6 +324,9 @@ def main():
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     from block_scaled_precision_03_amd import mxgemm, synth
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -244,9 +373,13 @@ def main():
                    "b_preshuffled": pre, "layout": "NT"},
         "pct_mfma_peak": 100.0 * value / PEAK_MXFP8_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MXFP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_MXFP8_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MXFP8_TFLOPS,
+                     "traffic": committed_traffic() if pre else None,
                      "kernel": "dense_kernel<E4M3,E4M3,MX,NT,preshuffled B>" if pre else
                                "dense_kernel<E4M3,E4M3,MX,NT>",
+                     "launches_per_step": len(C2_SHAPES),
+                     "mean_launch_us": kernel_ms * 1000.0 / len(C2_SHAPES),
+                     "flops_per_launch": step_flops / len(C2_SHAPES),
                      "kernel_ms_per_step": kernel_ms},
         "per_gemm": per_gemm,
     }
@@ -255,6 +388,11 @@ def main():
     if not args.only_step and not args.no_grouped:
         log("grouped G=8 ...")
         result["grouped"] = grouped_bench(torch, synth, mxgemm, dev)
+    if not args.only_step and not args.no_extra:
+        log("tensor-wise FP8 ...")
+        result["tensorwise_fp8"] = tensorwise_bench(torch, synth, mxgemm, dev)
+        log("MXFP4 ...")
+        result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
     if not args.only_step and not args.no_cpu:
         log("CPU oracle sample ...")
         result["cpu_baseline"] = cpu_baseline(synth)

@@ -231,13 +231,16 @@ struct DenseLoop {
   static constexpr int FM = 8, FN = 4;          // wave tile 128 x 64
   static constexpr int AB = DBM * 128;          // A bytes per stage
   static constexpr int STAGE = (DBM + DBN) * 128;
-  static constexpr int SA_OFF = 0, SB_OFF = KS * 1024;
-  static constexpr int SSTAGE = MX ? KS * 1024 + (PSB ? 4096 : KS * 1024) : 0;
+  // MX scales arrive in groups of four K steps (16 bytes per row): A rows
+  // at SA_OFF + 16 row, B rows (or, preshuffled, B column groups of 1 KiB)
+  // at SB_OFF.  Two group slots.
+  static constexpr int SA_OFF = 0, SB_OFF = 4096;
+  static constexpr int SGROUP = MX ? 8192 : 0;
   // LDS: [A slot 0][A slot 1][B slot 0][B slot 1][scales slot 0][slot 1].
   // A read offset within either slot then fits the 16-bit offset field of a
   // DS instruction on top of one per-lane base register per operand.
   static constexpr int B_REG = 2 * AB, S_REG = 4 * AB;
-  static constexpr int LDS_BYTES = S_REG + 2 * SSTAGE;
+  static constexpr int LDS_BYTES = S_REG + 2 * SGROUP;
   static constexpr int CGB = FP4 ? 4096 : 8192;
 
   // Loop-invariant state.  Every global load of the loop is one buffer
@@ -321,11 +324,11 @@ struct DenseLoop {
     });
   }
 
-  // DMA of stage st of tile t (operands and MX scales) into ring slot si.
-  __device__ static inline void issue(const Ctx &c, const Tile &t, int st, int si) {
+  // DMA of stage st of tile t (operands and MX scales) into ring slot si
+  // (operands) and scale slot gs.
+  __device__ static inline void issue(const Ctx &c, const Tile &t, int st, int si, int gs) {
     const DenseArgs &p = *c.p;
     const uint32_t slot = c.lds0 + (uint32_t)si * AB;
-    const uint32_t sslot = c.lds0 + S_REG + (uint32_t)si * SSTAGE;
     load_tile<TA>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
     if constexpr (PSB) {
       // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
@@ -341,18 +344,16 @@ struct DenseLoop {
       load_tile<TB>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
     }
     if constexpr (MX) {
-      // waves 0-3: A scales of rows 64w..; waves 4-7: B scales (plain: rows
-      // 64(w-4)..; preshuffled: column group w-4, four k steps per word).
-      const u32x4 r = t.rs;
-      if (c.w < 4 || !PSB) {
-        const uint32_t dst = sslot + (c.w < 4 ? SA_OFF : SB_OFF) + (uint32_t)(c.w & 3) * 256u;
-        static_for<0, KS>([&](auto sc) {
-          constexpr int s = decltype(sc)::value;
-          dma_asm<4, s * 1024>(dst, r, c.vo_s, (uint32_t)(4 * ((int64_t)st * KS + s)));
-        });
-      } else {
-        const uint32_t soff = (uint32_t)((((int64_t)st * KS) / 4) * 1024);
-        dma_asm<16>(sslot + SB_OFF + (uint32_t)(c.w - 4) * 1024u, r, c.vo_s, soff);
+      // With the first stage of each group of four K steps, scale slot gs
+      // receives the group's scales: waves 0-3 the A rows 64w.. (16 bytes
+      // each), waves 4-7 the B rows 64(w-4).. or, preshuffled, column group
+      // w-4 (1 KiB: four 16-row subtiles x 64 lanes x one word).
+      if (((st * KS) & 3) == 0) {
+        const uint32_t grp = (uint32_t)(st * KS / 4);
+        const uint32_t dst = c.lds0 + S_REG + (uint32_t)gs * SGROUP + (c.w < 4 ? SA_OFF : SB_OFF) +
+                             (uint32_t)(c.w & 3) * 1024u;
+        const uint32_t soff = (PSB && c.w >= 4) ? grp * 1024u : grp * 16u;
+        dma_asm<16>(dst, t.rs, c.vo_s, soff);
       }
     }
   }
@@ -395,9 +396,9 @@ struct DenseLoop {
       L.at[t] = ((uint32_t)(kk * 256 + ((ca ^ (kk & 7)) << 4) + ((i & 1) << 3))) & LMASK;
       L.bt[t] = ((uint32_t)(B_REG + kk * 256 + ((cb ^ (kk & 7)) << 4) + ((i & 1) << 3))) & LMASK;
     }
-    L.sa = ((uint32_t)(S_REG + (c.wm * 128 + i) * 4)) & LMASK;
-    if constexpr (PSB) L.sb = ((uint32_t)(S_REG + c.wn * 1024 + c.lane * 16)) & LMASK;
-    else L.sb = ((uint32_t)(S_REG + (c.wn * 64 + i) * 4)) & LMASK;
+    L.sa = ((uint32_t)(S_REG + SA_OFF + (c.wm * 128 + i) * 16)) & LMASK;
+    if constexpr (PSB) L.sb = ((uint32_t)(S_REG + SB_OFF + c.wn * 1024 + c.lane * 4)) & LMASK;
+    else L.sb = ((uint32_t)(S_REG + SB_OFF + (c.wn * 64 + i) * 16)) & LMASK;
   }
 
   __device__ static inline v8i rd8(const uint8_t *base, uint32_t lo, uint32_t hi, int imm) {
@@ -415,9 +416,9 @@ struct DenseLoop {
   }
 
   __device__ static inline void compute(const Ctx &c, const Lanes &L, int st,
-                                        const uint8_t *smem, int si, v4f (&acc)[FM][FN]) {
+                                        const uint8_t *smem, int si, int gs, v4f (&acc)[FM][FN]) {
     // The B and scale lane offsets include their regions' bases.
-    const uint8_t *la = smem + si * AB, *lb = smem + si * AB, *ls = smem + si * SSTAGE;
+    const uint8_t *la = smem + si * AB, *lb = smem + si * AB, *ls = smem + gs * SGROUP;
     auto read_a = [&](int s, int a) -> v8i {
       if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
       else if constexpr (TA) {
@@ -447,11 +448,12 @@ struct DenseLoop {
         bf[b] = read_b(s, b);
         sb[b] = E8M0_ONE_X4;
         if constexpr (MX) {
+          const int j = (st * KS + s) & 3;      // K step within the scale group
           if constexpr (PSB) {
-            const uint32_t word = lds_u32(ls + SB_OFF + L.sb + b * 4);
-            sb[b] = (int)(word >> (8 * ((st * KS + s) & 3)));
+            const uint32_t word = lds_u32(ls + L.sb + b * 256);
+            sb[b] = (int)(word >> (8 * j));
           } else {
-            const uint32_t word = lds_u32(ls + SB_OFF + s * 1024 + L.sb + b * 64);
+            const uint32_t word = lds_u32(ls + L.sb + b * 256 + j * 4);
             sb[b] = (int)(word >> (8 * c.q));
           }
         }
@@ -463,7 +465,8 @@ struct DenseLoop {
         if (a + 1 < FM) af_next = read_a(s, a + 1);
         int sa = E8M0_ONE_X4;
         if constexpr (MX) {
-          const uint32_t word = lds_u32(ls + SA_OFF + s * 1024 + L.sa + a * 64);
+          const int j = (st * KS + s) & 3;
+          const uint32_t word = lds_u32(ls + L.sa + a * 256 + j * 4);
           sa = (int)(word >> (8 * c.q));
         }
 #pragma unroll
@@ -539,25 +542,28 @@ struct DenseLoop {
     tile_at(0, tm, tn);
     Tile cur;
     set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, cur);
-    issue(c, cur, 0, 0);
+    issue(c, cur, 0, 0, 0);
     wait_vmem_le<0>();
     __syncthreads();
 
     const int nst = c.nst;
+    const int ngrp = (int)c.ngrp;              // scale groups per tile
     for (int t = 0; t < ntiles; ++t) {
       const bool more = t + 1 < ntiles;
+      // scale slot of group g of this tile: (t*ngrp + g) % 2
+      const int g0 = t * ngrp;
       if (more) tile_at(t + 1, tm, tn);
       auto step = [&](int k, int sc, int sn) {
         if (k + 1 < nst) {
-          issue(c, cur, k + 1, sn);
+          issue(c, cur, k + 1, sn, (g0 + (k + 1) * KS / 4) & 1);
         } else if (more) {
           // first stage of the next tile (its sources are built here, not
           // kept live through the K loop)
           Tile nxt;
           set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, nxt);
-          issue(c, nxt, 0, sn);
+          issue(c, nxt, 0, sn, (g0 + ngrp) & 1);
         }
-        compute(c, L, k, smem, sc, acc);
+        compute(c, L, k, smem, sc, (g0 + k * KS / 4) & 1, acc);
         __builtin_amdgcn_sched_barrier(0);
         // The next stage (this wave's part) and the previous epilogue's
         // stores have landed; the barrier publishes every wave's DMA.

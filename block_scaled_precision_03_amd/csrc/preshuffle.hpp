@@ -12,9 +12,11 @@
 // FP4 B: chunk (cg, ks) of 4 KiB at (cg*nks + ks)*4096; lane l of n-tile t
 //   at +1024t + 16l holds packed bytes 64ks + 16(l/16) + j of row
 //   64cg + 16t + l%16 (K values 128ks + 32(l/16) + [0, 32)).
-// E8M0 scales: 32-bit word ((cg*ngrp + g)*64 + l)*4 + t (ngrp = ceil(K/512)),
+// E8M0 scales: 32-bit word ((cg*ngrp + g)*4 + t)*64 + l (ngrp = ceil(K/512)),
 //   byte j = scale of row 64cg + 16t + l%16, 32-K block 16g + 4j + l/16;
-//   padding reads as 127 (2^0).
+//   padding reads as 127 (2^0).  A column group's words for one group of
+//   four K steps are 1 KiB in (subtile, lane) order, so a wave reads the
+//   words of one subtile as 64 consecutive words.
 #pragma once
 #include "common.hpp"
 
@@ -64,8 +66,8 @@ __global__ __launch_bounds__(256) void preshuffle_scales_kernel(const uint8_t *_
   const int64_t wi = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (wi >= nwords) return;
   const int64_t sk = K / 32, ngrp = (K + 511) / 512;
-  const int t = (int)(wi & 3);
-  const int lane = (int)((wi >> 2) & 63);
+  const int lane = (int)(wi & 63);
+  const int t = (int)((wi >> 6) & 3);
   const int64_t cgg = wi >> 8;
   const int64_t cg = cgg / ngrp, g = cgg % ngrp;
   const int64_t row = 64 * cg + 16 * t + (lane & 15);
