@@ -310,12 +310,13 @@ struct DenseLoop {
     }
   }
 
-  // Four 1 KiB DMAs of this wave into the tile at LDS address `tile`.
-  template <bool T>
+  // 1 KiB DMAs J0 .. J1-1 (of four) of this wave into the tile at LDS
+  // address `tile`.
+  template <bool T, int J0, int J1>
   __device__ static inline void load_tile(const Ctx &c, const u32x4 &r, const uint32_t (&vo)[2],
                                           int64_t KB, int64_t Rtot, int st, uint32_t tile) {
     const uint32_t base = tile + (uint32_t)c.w * 4096u;
-    static_for<0, 4>([&](auto jc) {
+    static_for<J0, J1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int blk = c.w * 4 + j;
       const uint32_t soff = T ? (uint32_t)((4 * blk + 128 * (int64_t)st) * Rtot)
@@ -325,25 +326,34 @@ struct DenseLoop {
   }
 
   // DMA of stage st of tile t (operands and MX scales) into ring slot si
-  // (operands) and scale slot gs.
+  // (operands) and scale slot gs.  PART selects a quarter of it (0, 1: the A
+  // tile's first and second halves; 2: B's first half; 3: B's second half
+  // and the scales) so that the issue can be spread over the K step; -1
+  // issues everything.
+  template <int PART = -1>
   __device__ static inline void issue(const Ctx &c, const Tile &t, int st, int si, int gs) {
     const DenseArgs &p = *c.p;
     const uint32_t slot = c.lds0 + (uint32_t)si * AB;
-    load_tile<TA>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
-    if constexpr (PSB) {
-      // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
-      const uint32_t soff0 = (uint32_t)((t.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB) +
-                             (uint32_t)((c.w >> 1) * c.nks * CGB) + (uint32_t)(c.w & 1) * 4096u;
-      const uint32_t base = slot + B_REG + (uint32_t)c.w * 4096u;
-      const u32x4 rb = t.rb;
-      static_for<0, 4>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        dma_asm<16, j * 1024>(base, rb, (uint32_t)(c.lane * 16), soff0 + j * 1024);
-      });
-    } else {
-      load_tile<TB>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
+    constexpr bool ALL = PART < 0;
+    if constexpr (ALL || PART == 0) load_tile<TA, 0, 2>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
+    if constexpr (ALL || PART == 1) load_tile<TA, 2, 4>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
+    if constexpr (ALL || PART >= 2) {
+      constexpr int J0 = (PART == 3) ? 2 : 0, J1 = (PART == 2) ? 2 : 4;
+      if constexpr (PSB) {
+        // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
+        const uint32_t soff0 = (uint32_t)((t.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB) +
+                               (uint32_t)((c.w >> 1) * c.nks * CGB) + (uint32_t)(c.w & 1) * 4096u;
+        const uint32_t base = slot + B_REG + (uint32_t)c.w * 4096u;
+        const u32x4 rb = t.rb;
+        static_for<J0, J1>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          dma_asm<16, j * 1024>(base, rb, (uint32_t)(c.lane * 16), soff0 + j * 1024);
+        });
+      } else {
+        load_tile<TB, J0, J1>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
+      }
     }
-    if constexpr (MX) {
+    if constexpr (MX && (ALL || PART == 3)) {
       // With the first stage of each group of four K steps, scale slot gs
       // receives the group's scales: waves 0-3 the A rows 64w.. (16 bytes
       // each), waves 4-7 the B rows 64(w-4).. or, preshuffled, column group
@@ -415,8 +425,89 @@ struct DenseLoop {
     return (v8i){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   }
 
+  // Epilogue of one finished tile: its accumulators (times alpha) as BF16.
+  // Lane (i, q) of matrix-core tile (a, b) holds row wm*128 + 16a + i,
+  // columns wn*64 + 16b + 4q .. +3.  For full tiles two neighbouring tiles
+  // (b = 2p, 2p+1) are recombined across lanes l and l^16 (ds_bpermute) so
+  // that every lane holds 8 consecutive columns: lanes with q even get
+  // columns 8(q/2) .. +7 of tile 2p, lanes with q odd those of tile 2p+1.  One
+  // 16-byte store per lane then covers 64 contiguous bytes of 16 rows.  Edge
+  // tiles (and N not a multiple of 8) store element by element with masks.
+  struct Epi {
+    __amdgpu_buffer_rsrc_t rd;   // full tiles: D from the tile's origin
+    uint32_t voff;               // full tiles: this lane's byte offset in the tile
+    uint32_t rowstride;          // bytes of 16 rows of D
+    int m0, n0;                  // tile origin (edge tiles)
+    float alpha;
+    bool full, on;
+  };
+  static constexpr int EPI_STORES = FM * FN / 2;   // store instructions per full tile
+
+  __device__ static inline void make_epi(const Ctx &c, int64_t m0, int64_t n0, float alpha, bool on,
+                                         Epi &e) {
+    const DenseArgs &p = *c.p;
+    e.m0 = (int)m0;
+    e.n0 = (int)n0;
+    e.alpha = alpha;
+    e.on = on;
+    e.full = m0 + DBM <= p.M && n0 + DBN <= p.N && (p.N & 7) == 0 && p.N < (1 << 23);
+    const int64_t org = m0 * p.N + n0;
+    e.rd = make_rsrc(p.D + org, clamp_records(2 * (p.M * p.N - org)));
+    e.rowstride = (uint32_t)(32 * p.N);
+    const int lane = (int)__lane_id(), i = lane & 15, q = lane >> 4;
+    e.voff = (uint32_t)(2 * ((c.wm * (FM * 16) + i) * p.N + c.wn * (FN * 16) + 16 * (q & 1) + 8 * (q >> 1)));
+  }
+
+  __device__ static inline void store_rows(const Ctx &c, const Epi &e, int a, const v4f (&row)[FN]) {
+    const float al = e.alpha;
+    if (e.full) {
+      // computed here, not hoisted into a register per row tile
+      uint32_t rs = e.rowstride;
+      asm volatile("" : "+s"(rs));
+      const int lane = (int)__lane_id();
+      const bool odd = ((lane >> 4) & 1) != 0;
+      const int partner = (lane ^ 16) << 2;
+#pragma unroll
+      for (int pr = 0; pr < FN / 2; ++pr) {
+        const v4f x = row[2 * pr], y = row[2 * pr + 1];
+        const uint32_t xlo = pack_bf16x2(x.x * al, x.y * al), xhi = pack_bf16x2(x.z * al, x.w * al);
+        const uint32_t ylo = pack_bf16x2(y.x * al, y.y * al), yhi = pack_bf16x2(y.z * al, y.w * al);
+        // q even keeps its tile-2p chunk and takes the partner's; q odd the
+        // same with tile 2p+1
+        const uint32_t rlo = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)(odd ? xlo : ylo));
+        const uint32_t rhi = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)(odd ? xhi : yhi));
+        const v4i v = odd ? (v4i){(int)rlo, (int)rhi, (int)ylo, (int)yhi}
+                          : (v4i){(int)xlo, (int)xhi, (int)rlo, (int)rhi};
+        __builtin_amdgcn_raw_buffer_store_b128(v, e.rd, (int)e.voff, (int)((uint32_t)a * rs + 64u * pr), 0);
+      }
+    } else {
+      // edge tiles: lane position recomputed here rather than kept live
+      const DenseArgs &p = *c.p;
+      const int lane = (int)__lane_id(), i = lane & 15, q = lane >> 4;
+      const int64_t r = (int64_t)e.m0 + c.wm * (FM * 16) + a * 16 + i;
+      if (r < p.M) {
+        uint16_t *dst = p.D + r * p.N;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          const v4f v = row[b];
+          const uint32_t u[2] = {pack_bf16x2(v.x * al, v.y * al), pack_bf16x2(v.z * al, v.w * al)};
+          const int64_t col = (int64_t)e.n0 + c.wn * (FN * 16) + b * 16 + 4 * q;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (col + k < p.N) dst[col + k] = (uint16_t)(u[k >> 1] >> (16 * (k & 1)));
+        }
+      }
+    }
+  }
+
+  // One K step from ring slot si (scale slot gs).  With EPI the step is the
+  // first of a tile: each accumulator row a-tile is first handed to the
+  // epilogue `e` (the previous tile's result, stored while the matrix cores
+  // run) and then restarted from zero.
+  template <bool EPI>
   __device__ static inline void compute(const Ctx &c, const Lanes &L, int st,
-                                        const uint8_t *smem, int si, int gs, v4f (&acc)[FM][FN]) {
+                                        const uint8_t *smem, int si, int gs, v4f (&acc)[FM][FN],
+                                        const struct Epi &e) {
     // The B and scale lane offsets include their regions' bases.
     const uint8_t *la = smem + si * AB, *lb = smem + si * AB, *ls = smem + gs * SGROUP;
     auto read_a = [&](int s, int a) -> v8i {
@@ -469,10 +560,17 @@ struct DenseLoop {
           const uint32_t word = lds_u32(ls + L.sa + a * 256 + j * 4);
           sa = (int)(word >> (8 * c.q));
         }
+        if (EPI && s == 0) {
+          if (e.on) store_rows(c, e, a, acc[a]);
 #pragma unroll
-        for (int b = 0; b < FN; ++b)
-          // First operand = B tile: the result lane holds 4 consecutive n.
-          acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb[b], sa);
+          for (int b = 0; b < FN; ++b)
+            acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f}, sb[b], sa);
+        } else {
+#pragma unroll
+          for (int b = 0; b < FN; ++b)
+            // First operand = B tile: the result lane holds 4 consecutive n.
+            acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb[b], sa);
+        }
         if (a + 1 < FM) af = af_next;
         // keep the A reads one tile ahead, not hoisted further (registers)
         __builtin_amdgcn_sched_barrier(0);
@@ -480,52 +578,18 @@ struct DenseLoop {
     }
   }
 
-  // The finished tile's accumulators (times alpha) as BF16, stored straight
-  // from registers: lane (i, q) of matrix-core tile (a, b) holds row
-  // wm*128 + 16a + i, columns wn*64 + 16b + 4q .. +3, i.e. one 8-byte store.
-  // Edge tiles mask rows >= M and columns >= N element by element.
-  __device__ static inline void epilogue(const Ctx &c, int64_t m0, int64_t n0, float alpha,
-                                         const v4f (&acc)[FM][FN]) {
-    const DenseArgs &p = *c.p;
-    const int64_t N = p.N;
-    const int64_t row0 = m0 + c.wm * (FM * 16) + c.i16;
-    const int64_t col0 = n0 + c.wn * (FN * 16) + 4 * c.q;
-    const bool full = m0 + DBM <= p.M && n0 + DBN <= N && (N & 3) == 0;
-    uint16_t *base = p.D + row0 * N + col0;
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-#pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        const v4f v = acc[a][b];
-        const uint32_t lo = pack_bf16x2(v.x * alpha, v.y * alpha);
-        const uint32_t hi = pack_bf16x2(v.z * alpha, v.w * alpha);
-        uint16_t *dst = base + (int64_t)(a * 16) * N + b * 16;
-        if (full) {
-          *(v2i *)dst = (v2i){(int)lo, (int)hi};
-        } else if (row0 + a * 16 < p.M) {
-          const int64_t col = col0 + b * 16;
-          if ((N & 3) == 0 && col + 4 <= N) {
-            *(v2i *)dst = (v2i){(int)lo, (int)hi};
-          } else {
-            const uint32_t u[2] = {lo, hi};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (col + e < N) dst[e] = (uint16_t)(u[e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-    }
-  }
-
-  // The K loop over every tile of this workgroup.  Global step g (K step k
-  // of tile t, g = t*nst + k) consumes its stage from slot g%2 while the
-  // next stage (K step k+1 of tile t, or the first K step of tile t+1)
-  // streams into the other slot.  The DMAs are invisible to the compiler
-  // (dma_asm), so the waits below are the only ones: the DMA into a slot is
-  // issued after the barrier that retired every wave's reads of it, and the
-  // slot is read only after the wait + barrier.  A tile's epilogue runs once
-  // its last step is done, with the next tile's first stage already in LDS;
-  // its stores drain during that tile's first step.
+  // The K loop over every tile of this workgroup.  K step k of a tile reads
+  // ring slot k % 2 while the next stage (K step k+1, or the first K step of
+  // the next tile) streams into the other slot.  The DMAs are invisible to
+  // the compiler (dma_asm), so the waits below are the only ones: the DMA
+  // into a slot is issued after the barrier that retired every wave's reads
+  // of it, and the slot is read only after the wait + barrier.
+  //
+  // A tile's first K step stores the previous tile's result (store_rows) as
+  // its accumulators restart.  Vector-memory operations of a wave are counted
+  // in issue order, so at the end of that step waiting until at most
+  // EPI_STORES operations are outstanding means the stage DMA issued before
+  // the stores has landed, and the stores drain during the next K step.
   template <class TileAt>
   __device__ static inline void run(const Ctx &c, int ntiles, TileAt tile_at, float alpha,
                                     uint8_t *smem) {
@@ -547,49 +611,57 @@ struct DenseLoop {
     __syncthreads();
 
     const int nst = c.nst;
+    const bool odd = (nst & 1) != 0;
     const int ngrp = (int)c.ngrp;              // scale groups per tile
+    Epi e;
+    make_epi(c, 0, 0, alpha, false, e);
     for (int t = 0; t < ntiles; ++t) {
       const bool more = t + 1 < ntiles;
-      // scale slot of group g of this tile: (t*ngrp + g) % 2
-      const int g0 = t * ngrp;
+      const int g0 = t * ngrp;                 // scale slot of group g: (g0 + g) % 2
       if (more) tile_at(t + 1, tm, tn);
-      auto step = [&](int k, int sc, int sn) {
+      auto step = [&](auto epi, auto slot, int k) {
+        constexpr bool EPI = decltype(epi)::value;
+        constexpr int SC = decltype(slot)::value, SN = 1 - SC;
         if (k + 1 < nst) {
-          issue(c, cur, k + 1, sn, (g0 + (k + 1) * KS / 4) & 1);
-        } else if (more) {
-          // first stage of the next tile (its sources are built here, not
-          // kept live through the K loop)
+          issue(c, cur, k + 1, SN, (g0 + (k + 1) * KS / 4) & 1);
+        } else if (more && !odd) {
+          // first stage of the next tile into slot 0 (this step reads slot 1);
+          // its sources are built here, not kept live through the K loop
           Tile nxt;
           set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, nxt);
-          issue(c, nxt, 0, sn, (g0 + ngrp) & 1);
+          issue(c, nxt, 0, SN, (g0 + ngrp) & 1);
         }
-        compute(c, L, k, smem, sc, (g0 + k * KS / 4) & 1, acc);
+        compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
         __builtin_amdgcn_sched_barrier(0);
-        // The next stage (this wave's part) and the previous epilogue's
-        // stores have landed; the barrier publishes every wave's DMA.
-        wait_vmem_le<0>();
+        // This wave's part of the next stage has landed (and, with no
+        // epilogue in flight, everything else); the barrier publishes every
+        // wave's DMA.
+        if (EPI && e.on && e.full) wait_vmem_le<EPI_STORES>();
+        else wait_vmem_le<0>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       };
-      int k = 0;
-      if (((int64_t)t * nst) & 1) {      // odd start: first step from slot 1
-        step(0, 1, 0);
-        k = 1;
-      }
+      step(std::true_type{}, std::integral_constant<int, 0>{}, 0);
+      int k = 1;
       for (; k + 2 <= nst; k += 2) {
-        step(k, 0, 1);
-        step(k + 1, 1, 0);
+        step(std::false_type{}, std::integral_constant<int, 1>{}, k);
+        step(std::false_type{}, std::integral_constant<int, 0>{}, k + 1);
       }
-      if (k < nst) step(k, 0, 1);
-      epilogue(c, cur.m0, cur.n0, alpha, acc);
+      if (k < nst) step(std::false_type{}, std::integral_constant<int, 1>{}, k);
+      // this tile's result goes out during the next tile's first step
+      make_epi(c, cur.m0, cur.n0, alpha, true, e);
       if (more) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-          for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
         set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, cur);
+        if (odd) {
+          // the last step read slot 0: the next tile's first stage follows it
+          issue(c, cur, 0, 0, (g0 + ngrp) & 1);
+          wait_vmem_le<0>();
+          __syncthreads();
+        }
       }
     }
+#pragma unroll
+    for (int a = 0; a < FM; ++a) store_rows(c, e, a, acc[a]);
   }
 };
 

@@ -81,3 +81,28 @@ def test_tensorwise_multitile(layout, ta, tb, K):
     opA = H.make_operand(T4, x, ta)
     opB = H.make_operand(T5, w, tb)
     _sampled(layout, opA, opB, M, N, K, "tensor layout %d K=%d" % (layout, K))
+
+
+@pytest.mark.parametrize("fa,fb,M,N,K", [
+    (E4, E4, 300, 520, 384), (E5, E5, 300, 520, 384), (E4, E5, 512, 768, 256),
+    (E5, E4, 4352, 4096, 256), (F4, F4, 512, 512, 512),
+])
+def test_every_output_written_repeatedly(fa, fb, M, N, K):
+    """Each call must write every element of D: a NaN sentinel fill may not
+    survive, and five calls in a row give the same bits (guards against an
+    epilogue whose cross-lane exchange or store ordering is unreliable)."""
+    x = synth.normal(7041 + M + fa, (M, K))
+    w = synth.normal(7042 + N + fb, (N, K))
+    opA = H.make_operand(fa, x, False)
+    opB = H.make_operand(fb, w, False)
+    ref = oracle.gemm(opA.orc(), opB.orc(), M, N, K)
+    first = None
+    for rep in range(5):
+        D = H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=(rep % 2 == 1), d_fill=float("nan"))
+        d = H.bf16_to_f64(D)
+        assert not np.isnan(d).any(), "unwritten outputs on call %d" % rep
+        H.assert_close(d, ref, "call %d" % rep)
+        b = H.bits(D)
+        if first is None:
+            first = b
+        assert np.array_equal(first, b), "call %d differs from call 0" % rep
