@@ -549,17 +549,21 @@ struct DenseLoop {
           }
         }
       }
+      // All A scale words of the step up front: read beside the matrix-core
+      // tile that needs them, each would stall its tile on an LDS round trip.
+      uint32_t saw[FM];
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        saw[a] = 0;
+        if constexpr (MX) saw[a] = lds_u32(ls + L.sa + a * 256 + ((st * KS + s) & 3) * 4);
+      }
       v8i af = read_a(s, 0);
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         v8i af_next;
         if (a + 1 < FM) af_next = read_a(s, a + 1);
         int sa = E8M0_ONE_X4;
-        if constexpr (MX) {
-          const int j = (st * KS + s) & 3;
-          const uint32_t word = lds_u32(ls + L.sa + a * 256 + j * 4);
-          sa = (int)(word >> (8 * c.q));
-        }
+        if constexpr (MX) sa = (int)(saw[a] >> (8 * c.q));
         if (EPI && s == 0) {
           if (e.on) store_rows(c, e, a, acc[a]);
 #pragma unroll
@@ -576,6 +580,16 @@ struct DenseLoop {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+
+  // Keeps a step's matrix-core instructions ahead of the wait that ends the
+  // step.  They only touch registers, so without this the compiler is free to
+  // sink them past the wait and barrier into the next step, which leaves the
+  // wait for the next stage's DMA with nothing to overlap.
+  __device__ static inline void pin(v4f (&acc)[FM][FN]) {
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+      asm volatile("" : "+v"(acc[a][0]), "+v"(acc[a][1]), "+v"(acc[a][2]), "+v"(acc[a][3]));
   }
 
   // The K loop over every tile of this workgroup.  K step k of a tile reads
@@ -632,6 +646,10 @@ struct DenseLoop {
           issue(c, nxt, 0, SN, (g0 + ngrp) & 1);
         }
         compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
+        // (not for a transposed A: with that variant's register pressure,
+        // pinning gave rare non-finite outputs at full size, which the
+        // full-size determinism tests now guard against)
+        if constexpr (!TA) pin(acc);
         __builtin_amdgcn_sched_barrier(0);
         // This wave's part of the next stage has landed (and, with no
         // epilogue in flight, everything else); the barrier publishes every

@@ -79,3 +79,56 @@ def test_mxfp4_8192_cube():
     del x, w
     D = H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=True)
     _check_sampled(D, opA, opB, M, N, K, "mxfp4 8192^3")
+
+
+def _bits_of(run):
+    D = run()
+    return H.bits(D)
+
+
+@pytest.mark.parametrize("M,N,K", [(16384, 14336, 4096), (4096, 4096, 14336)])
+def test_mxfp8_full_size_deterministic_and_layout_independent(M, N, K):
+    """Every element at full size, not a sample: repeated calls give the same
+    bits, and the preshuffled-B and plain-B kernels agree bit for bit (their
+    per-element arithmetic is identical).  A race on a staging buffer or an
+    epilogue that drops or mixes data would break one of the two."""
+    x = synth.normal(synth.seed_for(2, 1, 7), (M, K))
+    w = synth.normal(synth.seed_for(2, 2, 7), (N, K), 0.02)
+    opA = H.make_operand(E4, x, False)
+    opB = H.make_operand(E5, w, False)
+    del x, w
+    b0 = _bits_of(lambda: H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=True, d_fill=float("nan")))
+    b1 = _bits_of(lambda: H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=True, d_fill=float("nan")))
+    b2 = _bits_of(lambda: H.run_dense(NT, opA, opB, M, N, K, d_fill=float("nan")))
+    assert np.array_equal(b0, b1), "preshuffled-B kernel not deterministic"
+    assert np.array_equal(b0, b2), "preshuffled-B and plain-B kernels differ"
+    assert not np.isnan(oracle.bf16_bits_to_f64(b0)).any()
+
+
+@pytest.mark.parametrize("name,layout,M,N,K", C3)
+def test_tensorwise_full_size_deterministic(name, layout, M, N, K):
+    """Three calls at full size give identical, finite bits (E4M3 and E5M2
+    operands: bytes of one read as the other would show up as Inf/NaN)."""
+    idx = [c[0] for c in C3].index(name)
+    a = synth.normal(synth.seed_for(3, 1, idx), (M, K))
+    b = synth.normal(synth.seed_for(3, 2, idx), (N, K), 0.02)
+    opA = H.make_operand(T4, a, layout == TN)
+    opB = H.make_operand(T5, b, layout in (NN, TN))
+    del a, b
+    outs = [_bits_of(lambda: H.run_dense(layout, opA, opB, M, N, K, d_fill=float("nan"))) for _ in range(3)]
+    for o in outs:
+        assert np.isfinite(oracle.bf16_bits_to_f64(o)).all(), "non-finite output in %s" % name
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_mxfp4_full_size_deterministic_and_layout_independent():
+    M = N = K = 8192
+    x = synth.normal(synth.seed_for(5, 1, 7), (M, K))
+    w = synth.normal(synth.seed_for(5, 2, 7), (N, K))
+    opA = H.make_operand(F4, x, False)
+    opB = H.make_operand(F4, w, False)
+    del x, w
+    b0 = _bits_of(lambda: H.run_dense(NT, opA, opB, M, N, K, preshuffle_b=True, d_fill=float("nan")))
+    b1 = _bits_of(lambda: H.run_dense(NT, opA, opB, M, N, K, d_fill=float("nan")))
+    assert np.array_equal(b0, b1)
+    assert not np.isnan(oracle.bf16_bits_to_f64(b0)).any()
