@@ -242,6 +242,7 @@ struct DenseLoop {
   static constexpr int B_REG = 2 * AB, S_REG = 4 * AB;
   static constexpr int LDS_BYTES = S_REG + 2 * SGROUP;
   static constexpr int CGB = FP4 ? 4096 : 8192;
+  static constexpr bool PIN = !TA && !TB && (PSB || !MX || FP4);
 
   // Loop-invariant state.  Every global load of the loop is one buffer
   // instruction: a resource fixed for the tile, a per-lane offset fixed for
@@ -646,10 +647,11 @@ struct DenseLoop {
           issue(c, nxt, 0, SN, (g0 + ngrp) & 1);
         }
         compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
-        // (not for a transposed A: with that variant's register pressure,
-        // pinning gave rare non-finite outputs at full size, which the
-        // full-size determinism tests now guard against)
-        if constexpr (!TA) pin(acc);
+        // Only where registers allow: for the transposed variants and MX FP8
+        // with plain B it costs spills in the K loop (and with a transposed A
+        // it gave rare non-finite outputs at full size, which the full-size
+        // determinism tests now guard against).
+        if constexpr (PIN) pin(acc);
         __builtin_amdgcn_sched_barrier(0);
         // This wave's part of the next stage has landed (and, with no
         // epilogue in flight, everything else); the barrier publishes every
