@@ -4,6 +4,8 @@
 // stream or returns an error before enqueueing anything.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <algorithm>
+#include <cmath>
 #include <stdio.h>
 
 #include "../../include/mxgemm.h"
@@ -37,6 +39,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // Largest operand extents the 32-bit in-kernel offsets support.
 constexpr int64_t MAX_ROW_BYTES = 1ll << 22;   // bytes of K per row (256 rows < 2^30)
 constexpr int64_t MAX_DIM = 1ll << 31;
+constexpr int64_t MAX_T_BYTES = 0x7FFFFFF0ll;   // a transposed operand, whole
 
 int launch_status() {
   const hipError_t e = hipGetLastError();
@@ -44,6 +47,12 @@ int launch_status() {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The persistent grouped kernel: GS_KS K steps per ring stage, GS_NS ring
+// slots (74 KiB of LDS with the group table), GS_OCC workgroups per compute
+// unit, so that one workgroup's wait-barrier-compute chain overlaps the
+// other's.
+constexpr int GS_KS = 2, GS_NS = 2, GS_OCC = 2;
 
 // Compute units of the current device: the grid size of the persistent dense
 // kernel (one workgroup per compute unit).  Queried once per device.
@@ -106,8 +115,10 @@ extern "C" int mxgemm_validate(int fmtA, int fmtB, int layout, const void *A, co
   if (K % (fp4 ? 256 : 128) != 0) return MXG_ERR_UNSUPPORTED;
   const int64_t kb = fp4 ? K / 2 : K;
   if (kb > MAX_ROW_BYTES) return MXG_ERR_UNSUPPORTED;
-  if (layout == MXG_TN && (M % 16 != 0 || M * 128 >= (1ll << 31))) return MXG_ERR_UNSUPPORTED;
-  if ((layout == MXG_TN || layout == MXG_NN) && (N % 16 != 0 || N * 128 >= (1ll << 31)))
+  // A transposed operand is addressed from a tile's first column through
+  // all K rows with one 32-bit range-checked offset.
+  if (layout == MXG_TN && (M % 16 != 0 || M * K >= MAX_T_BYTES)) return MXG_ERR_UNSUPPORTED;
+  if ((layout == MXG_TN || layout == MXG_NN) && (N % 16 != 0 || N * K >= MAX_T_BYTES))
     return MXG_ERR_UNSUPPORTED;
   if (fa.mx && (M * (K / 32) >= (1ll << 31) || cdiv(N, 64) * 64 * (K / 32) >= (1ll << 31)))
     return MXG_ERR_UNSUPPORTED;
@@ -240,7 +251,6 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
                        stream, m_sizes, G, (uint16_t *)D, totM, N);
     return launch_status();
   }
-  constexpr int BM = 128, BN = 128;
   GroupedArgs a;
   a.m_sizes = m_sizes;
   a.XQ = (const uint8_t *)XQ;
@@ -252,21 +262,53 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   a.N = N;
   a.K = K;
   a.G = G;
-  a.tiles_n = (int)(N / BN);
-  const int64_t tiles_m = cdiv(totM, BM) + G - 1;
-  const int64_t blocks = tiles_m * a.tiles_n;
+  const bool stream_kernel = grouped_fp8_gemm_variant(G, totM, N, K) == MXG_GROUPED_STREAM;
+  const int B = stream_kernel ? GroupedStream::BM : 128;   // square tiles
+  a.tiles_n = (int)(N / B);
+  const int64_t blocks = (cdiv(totM, B) + G - 1) * a.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
-  if (b_preshuffled)
-    hipLaunchKernelGGL((grouped_kernel<BM, BN, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((grouped_kernel<BM, BN, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (stream_kernel) {
+    // persistent: GS_OCC workgroups per compute unit (fewer if fewer tiles)
+    const unsigned P = (unsigned)std::min<int64_t>(blocks, (int64_t)GS_OCC * cu_count());
+    if (b_preshuffled)
+      hipLaunchKernelGGL((grouped_stream_kernel<true, GS_KS, GS_NS>), dim3(P), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((grouped_stream_kernel<false, GS_KS, GS_NS>), dim3(P), dim3(256), 0, stream, a);
+  } else if (b_preshuffled) {
+    hipLaunchKernelGGL((grouped_kernel<128, 128, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((grouped_kernel<128, 128, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
   return launch_status();
+}
+
+// Kernel choice from the static shapes (the host never reads m_sizes): the
+// estimated time of each, from the tile counts' upper bounds.
+//  - persistent 64 x 64 (weight streaming): ~0.6 us per 128-K tile step per
+//    workgroup, GS_OCC workgroups per compute unit, walking all tile steps
+//    evenly; at least the weights' bytes at ~5 TB/s.
+//  - 128 x 128 (two workgroups per compute unit, one tile each): ~1.25 us
+//    per K step per round of resident workgroups; at least the weights'
+//    bytes at ~4 TB/s.
+// The constants are fitted to measured times of both kernels on MI355X over
+// totM 128 .. 8192, (N, K) = (2048, 7168) and (7168, 2304), G = 8.
+extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K) {
+  if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM;
+  const double slots = 2.0 * cu_count(), nst = (double)(K / 128);
+  const double wbytes = (double)G * (double)N * (double)K;
+  const double steps_s = (double)(cdiv(totM, 64) + G - 1) * (double)(N / 64) * nst;
+  const double t_s = std::max(0.6 * steps_s / ((double)GS_OCC * cu_count()), wbytes / 5.0e6);
+  const double blocks_o = (double)(cdiv(totM, 128) + G - 1) * (double)(N / 128);
+  const double t_o = std::max(1.25 * std::ceil(blocks_o / slots) * nst, wbytes / 4.0e6);
+  return t_s <= t_o ? MXG_GROUPED_STREAM : MXG_GROUPED_TILED;
 }
 
 extern "C" int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K) {
   const FmtInfo f = fmt_info(fmtB & ~MXG_PRESHUFFLED);
   if (!f.ok || N < 0 || K < 0 || K % 128 != 0) return -1;
-  const int64_t ncg = cdiv(N, 64), nks = K / 128;
+  // Whole 256-row tiles (four column groups each), so that a dense tile on
+  // the last columns finds all its column groups inside the buffer.
+  const int64_t ncg = cdiv(N, 256) * 4, nks = K / 128;
   return ncg * nks * (f.elem == F_E2M1 ? 4096 : 8192);
 }
 

@@ -65,18 +65,55 @@ __device__ inline uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// A wave-uniform value or resource forced into scalar registers (free when
+// the compiler already keeps it there), as the "s" operands below require.
+__device__ inline uint32_t sreg(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline u32x4 sreg(const u32x4 &r) {
+  return (u32x4){sreg(r.x), sreg(r.y), sreg(r.z), sreg(r.w)};
+}
+
 // lds: LDS byte address of lane 0's destination, uniform; IMM is added to
 // it inside the instruction sequence so that call sites that differ only by
-// a constant share one base register.
+// a constant share one base register.  The buffer range check covers the
+// vector offset only, never the scalar offset soff: soff may only carry a
+// part of the offset that keeps every lane inside the resource.
 template <int BYTES, int IMM = 0>
 __device__ inline void dma_asm(uint32_t lds, const u32x4 &r, uint32_t voff, uint32_t soff) {
   static_assert(BYTES == 4 || BYTES == 16, "DMA width");
   if constexpr (BYTES == 16)
     asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff), "i"(IMM) : "memory", "m0", "scc");
+                 ::"s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(soff)), "i"(IMM) : "memory", "m0", "scc");
   else
     asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff), "i"(IMM) : "memory", "m0", "scc");
+                 ::"s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(soff)), "i"(IMM) : "memory", "m0", "scc");
+}
+
+// The same DMA with the whole source offset, voff + add (add uniform), in
+// the vector offset, so that the range check sees all of it: lanes whose
+// bytes lie past the resource's end read zeros and touch no memory.  The sum
+// is formed inside the block (a temporary VGPR) so that the compiler does not
+// precompute and keep every DMA's offset live.
+template <int BYTES, int IMM = 0>
+__device__ inline void dma_asm_v(uint32_t lds, const u32x4 &r, uint32_t voff, uint32_t add) {
+  static_assert(BYTES == 4 || BYTES == 16, "DMA width");
+  uint32_t t;
+  if constexpr (BYTES == 16)
+    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %4, %2\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
+                 : "=&v"(t) : "s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(add)), "i"(IMM) : "memory", "m0", "scc");
+  else
+    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %4, %2\n\tbuffer_load_dword %0, %3, 0 offen lds"
+                 : "=&v"(t) : "s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(add)), "i"(IMM) : "memory", "m0", "scc");
+}
+
+// A 16-byte buffer store (D[voff + soff] = v) and three wait states in one
+// assembly block.  The store reads its data VGPRs after it issues; a VALU
+// write of those VGPRs in the next two cycles corrupts what is stored.  The
+// compiler's hazard checks assume no such hazard when soffset is an SGPR,
+// which does not hold on gfx950 (seen as a wrong last dword in lanes 12-15
+// of each row of 16 lanes), so the wait is part of the store itself.
+__device__ inline void store16_asm(const v4i &v, const u32x4 &r, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 2"
+               ::"v"(v), "v"(voff), "s"(sreg(r)), "s"(sreg(soff)) : "memory");
 }
 
 // Compile-time loop: f(std::integral_constant<int, J>) for J in [B, E).

@@ -269,6 +269,8 @@ struct DenseLoop {
     // A: rows m0.. (K-contiguous) or columns m0.. of [K, M]; B likewise.
     const int64_t abase = TA ? m0 : m0 * c.KB;
     t.ra = rsrc4(p.A + abase, clamp_records(p.a_bytes - abase));
+    // Preshuffled B: the whole buffer (it holds every column group of every
+    // 256-column tile, padding included); the offsets below stay inside it.
     int64_t bbase;
     if constexpr (PSB) bbase = 0;
     else bbase = TB ? n0 : n0 * c.KB;
@@ -312,17 +314,20 @@ struct DenseLoop {
   }
 
   // 1 KiB DMAs J0 .. J1-1 (of four) of this wave into the tile at LDS
-  // address `tile`.
+  // address `tile`.  The whole offset goes through the range check (the
+  // resource ends where the operand ends), so rows past M (N), and columns
+  // past the end of a transposed operand's last k-row, read zeros.
   template <bool T, int J0, int J1>
   __device__ static inline void load_tile(const Ctx &c, const u32x4 &r, const uint32_t (&vo)[2],
                                           int64_t KB, int64_t Rtot, int st, uint32_t tile) {
     const uint32_t base = tile + (uint32_t)c.w * 4096u;
+    auto add = [&](int blk) {
+      return T ? (uint32_t)((4 * blk + 128 * (int64_t)st) * Rtot)
+               : (uint32_t)(blk * 8 * KB + 128 * (int64_t)st);
+    };
     static_for<J0, J1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      const int blk = c.w * 4 + j;
-      const uint32_t soff = T ? (uint32_t)((4 * blk + 128 * (int64_t)st) * Rtot)
-                              : (uint32_t)(blk * 8 * KB + 128 * (int64_t)st);
-      dma_asm<16, j * 1024>(base, r, vo[j & 1], soff);
+      dma_asm_v<16, j * 1024>(base, r, vo[j & 1], add(c.w * 4 + j));
     });
   }
 
@@ -435,7 +440,7 @@ struct DenseLoop {
   // 16-byte store per lane then covers 64 contiguous bytes of 16 rows.  Edge
   // tiles (and N not a multiple of 8) store element by element with masks.
   struct Epi {
-    __amdgpu_buffer_rsrc_t rd;   // full tiles: D from the tile's origin
+    u32x4 rd;                    // full tiles: D from the tile's origin
     uint32_t voff;               // full tiles: this lane's byte offset in the tile
     uint32_t rowstride;          // bytes of 16 rows of D
     int m0, n0;                  // tile origin (edge tiles)
@@ -453,7 +458,7 @@ struct DenseLoop {
     e.on = on;
     e.full = m0 + DBM <= p.M && n0 + DBN <= p.N && (p.N & 7) == 0 && p.N < (1 << 23);
     const int64_t org = m0 * p.N + n0;
-    e.rd = make_rsrc(p.D + org, clamp_records(2 * (p.M * p.N - org)));
+    e.rd = rsrc4(p.D + org, clamp_records(2 * (p.M * p.N - org)));
     e.rowstride = (uint32_t)(32 * p.N);
     const int lane = (int)__lane_id(), i = lane & 15, q = lane >> 4;
     e.voff = (uint32_t)(2 * ((c.wm * (FM * 16) + i) * p.N + c.wn * (FN * 16) + 16 * (q & 1) + 8 * (q >> 1)));
@@ -479,7 +484,7 @@ struct DenseLoop {
         const uint32_t rhi = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)(odd ? xhi : yhi));
         const v4i v = odd ? (v4i){(int)rlo, (int)rhi, (int)ylo, (int)yhi}
                           : (v4i){(int)xlo, (int)xhi, (int)rlo, (int)rhi};
-        __builtin_amdgcn_raw_buffer_store_b128(v, e.rd, (int)e.voff, (int)((uint32_t)a * rs + 64u * pr), 0);
+        store16_asm(v, e.rd, e.voff, (uint32_t)a * rs + 64u * pr);
       }
     } else {
       // edge tiles: lane position recomputed here rather than kept live

@@ -18,6 +18,7 @@
 // * B is either plain [G, N, K] (staged through XOR-swizzled LDS like A) or
 //   preshuffled per group (copied linearly into LDS).
 #pragma once
+#include "../../include/mxgemm.h"
 #include "dense.hpp"
 
 namespace mxg {
@@ -140,6 +141,311 @@ __global__ __launch_bounds__(256, 1) void grouped_kernel(GroupedArgs p) {
   }
 
   store_tile<BM, BN, FM, FN>(acc, 1.0f, smem, p.D, row0, n0, row_lim, N, wm, wn);
+}
+
+}  // namespace mxg
+
+namespace mxg {
+
+// Grouped kernel for few rows per group (the weight-streaming regime: the
+// weights dominate the bytes and HBM, not the matrix cores, sets the time).
+//
+// * 64 x 64 output tiles.  The real tiles (groups with rows only, none
+//   spanning two groups) are numbered group by group, N-tile major and M-tile
+//   minor, so that consecutive tiles share one weight tile.
+// * Persistent grid of P workgroups, one per compute unit: workgroup j walks
+//   tiles j, j + P, j + 2P, ...; workgroups are renumbered so that
+//   consecutive j run on one XCD (one L2), and tiles that read the same
+//   weights at the same time share it.
+// * An eight-slot ring of 128-K stages (A rows, weight rows, the tile's
+//   activation scales and weight block scale: 16.5 KiB) is filled by
+//   buffer-load-to-LDS DMA issued from inline assembly with explicit waits.
+//   The ring runs across tile boundaries: seven stages stay in flight from
+//   the first K step of a workgroup's first tile to the last of its last,
+//   so each compute unit keeps about 56 KiB of weights outstanding.
+// * Per stage, four waves (2 x 2, 32 x 32 each) run the scaled matrix-core
+//   instruction with the neutral E8M0 scale into a zeroed accumulator and
+//   add the partial times xs(row, kb) * ws(g, n/128, kb) in FP32.  A tile's
+//   result is stored as BF16 straight from the accumulators.
+// * 8-row blocks of A past the tile's group read nothing (empty range).
+struct GroupedStream {
+  static constexpr int BM = 64, BN = 64;
+  static constexpr int FM = 2, FN = 2;
+  static constexpr int AB = BM * 128, BB = BN * 128;
+  static constexpr int SC = 512;                    // xs (64 floats) + ws (64 copies)
+  static constexpr int STEP = AB + BB + SC;         // one 128-K step
+};
+
+// Group table of a workgroup, in LDS: rows[g] = first row of group g (groups
+// clamped to [0, totM) in order, so rows[g] = min(sum of the earlier
+// max(m_sizes, 0), totM)), mtile[g] = number of 64-row tiles of the groups
+// before g; entry G closes both.  Built by wave 0 with a 64-lane prefix sum
+// per chunk of 64 groups.
+struct GroupTable {
+  int32_t rows[MXG_GROUPED_MAX_G + 1];
+  int32_t mtile[MXG_GROUPED_MAX_G + 1];
+};
+
+__device__ inline int64_t wave_incl_sum(int64_t x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ inline void build_group_table(const GroupedArgs &p, GroupTable &gt, int lane) {
+  constexpr int BM = GroupedStream::BM;
+  int64_t rows = 0, tiles = 0;
+  for (int c = 0; c < p.G; c += 64) {
+    const int g = c + lane;
+    int64_t s = g < p.G ? p.m_sizes[g] : 0;
+    s = s < 0 ? 0 : (s > p.totM ? p.totM : s);
+    const int64_t incl = wave_incl_sum(s, lane);
+    const int64_t r0 = min(rows + incl - s, p.totM), r1 = min(rows + incl, p.totM);
+    const int64_t mt = (r1 - r0 + BM - 1) / BM;
+    const int64_t tincl = wave_incl_sum(mt, lane);
+    if (g < p.G) {
+      gt.rows[g] = (int32_t)r0;
+      gt.mtile[g] = (int32_t)(tiles + tincl - mt);
+    }
+    rows = min(rows + __shfl(incl, 63, 64), p.totM);
+    tiles += __shfl(tincl, 63, 64);
+  }
+  if (lane == 0) {
+    gt.rows[p.G] = (int32_t)rows;
+    gt.mtile[p.G] = (int32_t)tiles;
+  }
+}
+
+// A value every lane holds alike, moved to scalar registers.
+__device__ inline int32_t uni32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Real tile t (t < mtile[G] * tiles_n): tiles are numbered group by group,
+// N-tile major, M-tile minor within a group.
+struct StreamTile {
+  int64_t start, mg, row0, n0;
+  int g;
+};
+
+__device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable &gt, int64_t t) {
+  const int32_t u = (int32_t)(t / p.tiles_n);        // 64-row tile index over all groups
+  // the last group g with mtile[g] <= u (a non-empty one: an empty group
+  // shares its mtile with the group after it)
+  int lo = 0, hi = p.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uni32(gt.mtile[mid]) <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  const int g = lo;
+  const int32_t mt0 = uni32(gt.mtile[g]), r0 = uni32(gt.rows[g]);
+  const int64_t mt = uni32(gt.mtile[g + 1]) - mt0;
+  const int64_t local = t - (int64_t)mt0 * p.tiles_n;
+  const int64_t tn = local / mt, tm = local - tn * mt;
+  StreamTile r;
+  r.g = g;
+  r.start = r0;
+  r.mg = uni32(gt.rows[g + 1]) - r0;
+  r.row0 = r.start + tm * GroupedStream::BM;
+  r.n0 = tn * GroupedStream::BN;
+  return r;
+}
+
+// KS 128-K steps per ring stage, NS ring slots.
+template <bool PSB, int KS, int NS>
+__global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
+  typedef GroupedStream S;
+  constexpr int BM = S::BM, FM = S::FM, FN = S::FN;
+  constexpr int STAGE = KS * S::STEP;
+  // DMAs per stage and wave: A and B two each per K step, plus one per K
+  // step for the activation scales (wave 0) or the weight block scale
+  // (wave 1).
+  constexpr int OPS_LO = 4 * KS, OPS_HI = 5 * KS;
+  static_assert(OPS_HI * (NS - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  __shared__ GroupTable gt;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int i16 = lane & 15, q = lane >> 4;
+
+  if (w == 0) build_group_table(p, gt, lane);
+  __syncthreads();
+  const int P = (int)gridDim.x;
+  int j = (int)blockIdx.x;
+  if ((P & 7) == 0) j = (j & 7) * (P >> 3) + (j >> 3);
+  const int64_t T = (int64_t)uni32(gt.mtile[p.G]) * p.tiles_n;   // real tiles
+  if (j >= T) return;
+  const int64_t ntile = (T - 1 - j) / P + 1;       // tiles of this workgroup
+  const int64_t K = p.K, N = p.N;
+  const int nst = (int)(K / 128);                  // K steps per tile
+  const int nsg = (nst + KS - 1) / KS;             // stages per tile
+  const int64_t kb_n = K / 128;
+  const int64_t V = ntile * nsg;                   // stages of this workgroup
+
+  const u32x4 rx = rsrc4(p.xs, clamp_records(p.totM * kb_n * 4));
+  const u32x4 rw = rsrc4(p.ws, clamp_records((int64_t)p.G * (N / 128) * kb_n * 4));
+  const u32x4 rzero = rsrc4(p.xs, 0);
+  // lane offsets of the row-tile DMAs (8 rows x 128 B per DMA; row r keeps
+  // 16-byte piece c at position c ^ (r%8) ^ ((r/8)%2))
+  uint32_t vo[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int r8 = lane >> 3;
+    vo[par] = (uint32_t)(r8 * K) + (uint32_t)(((lane & 7) ^ r8 ^ par) << 4);
+  }
+  const uint32_t lds0 = lds_addr(smem);
+
+  // Issue side: the tile whose stages are being issued.
+  struct Src {
+    u32x4 ra, rb;
+    uint32_t xs0, ws0, mg4;
+    int vrows;
+  };
+  auto make_src = [&](int64_t i) {
+    const StreamTile t = stream_tile(p, gt, j + i * P);
+    Src s;
+    const int64_t abase = t.row0 * K;
+    s.ra = rsrc4(p.XQ + abase, clamp_records(p.totM * K - abase));
+    const int64_t bbase = (int64_t)t.g * N * K + t.n0 * K;
+    s.rb = rsrc4(p.WQ + bbase, clamp_records(N * K - t.n0 * K));
+    s.xs0 = (uint32_t)((t.start * kb_n + (t.row0 - t.start)) * 4);
+    s.ws0 = (uint32_t)((((int64_t)t.g * (N / 128) + t.n0 / 128) * kb_n) * 4);
+    s.mg4 = (uint32_t)(t.mg * 4);
+    const int64_t left = t.start + t.mg - t.row0;
+    s.vrows = (int)(left < BM ? left : BM);
+    return s;
+  };
+  Src src = make_src(0);
+  int64_t iss_i = 0;
+  int iss_sg = 0;
+
+  // Stage (iss_i, iss_sg) into slot sl, then advance; K steps past the
+  // tile's last one and stages past the workgroup's last read an empty
+  // range (zeros: their partials add exactly 0, and the wait counts stay
+  // uniform).
+  auto issue = [&](int sl) {
+    const bool real = iss_i < ntile;
+    const uint32_t slot = lds0 + (uint32_t)sl * STAGE;
+    static_for<0, KS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int st = iss_sg * KS + s;
+      const bool live = real && st < nst;
+      const uint32_t ka = slot + (uint32_t)s * S::AB;
+      const uint32_t kb = slot + (uint32_t)(KS * S::AB + s * S::BB);
+      const uint32_t ksc = slot + (uint32_t)(KS * (S::AB + S::BB) + s * S::SC);
+      static_for<0, 2>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        const int blk = 2 * w + jj;
+        const u32x4 r = (live && blk * 8 < src.vrows) ? src.ra : rzero;
+        dma_asm_v<16>(ka + (uint32_t)blk * 1024u, r, vo[jj], (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
+      });
+      const u32x4 rb = live ? src.rb : rzero;
+      static_for<0, 2>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        const int blk = 2 * w + jj;
+        if constexpr (PSB)
+          dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, (uint32_t)lane * 16u,
+                      (uint32_t)(st * 8192 + blk * 1024));
+        else
+          dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, vo[jj],
+                      (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
+      });
+      if (w == 0) dma_asm_v<4>(ksc, live ? rx : rzero, (uint32_t)lane * 4u, src.xs0 + (uint32_t)st * src.mg4);
+      if (w == 1) dma_asm<4>(ksc + 256u, live ? rw : rzero, 0u, src.ws0 + (uint32_t)st * 4u);
+    });
+    if (++iss_sg == nsg) {
+      iss_sg = 0;
+      ++iss_i;
+      if (iss_i < ntile) src = make_src(iss_i);
+    }
+  };
+  // Stage v has landed once only this wave's DMAs of the NS - 2 stages
+  // issued after it (and any result stores, issued later still) are
+  // outstanding.
+  auto wait_stage = [&]() {
+    if (w < 2) wait_vmem_le<OPS_HI * (NS - 2)>();
+    else wait_vmem_le<OPS_LO * (NS - 2)>();
+  };
+
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // fragment lane offsets
+  const int f = (i16 & 7) ^ (i16 >> 3);
+  const uint32_t oa0 = (uint32_t)((wm * 32 + i16) * 128 + ((q ^ f) << 4));
+  const uint32_t oa1 = (uint32_t)((wm * 32 + i16) * 128 + (((q + 4) ^ f) << 4));
+  const uint32_t ob0 = PSB ? (uint32_t)(wn * 2 * 2048 + lane * 16)
+                           : (uint32_t)((wn * 32 + i16) * 128 + ((q ^ f) << 4));
+  const uint32_t ob1 = PSB ? ob0 + 1024u : (uint32_t)((wn * 32 + i16) * 128 + (((q + 4) ^ f) << 4));
+  const uint32_t oxs = (uint32_t)((wm * 32 + i16) * 4);
+
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  wait_stage();
+  __syncthreads();
+
+  int64_t ci = 0;      // tile being computed
+  int csg = 0;         // its stage
+  for (int64_t v = 0; v < V; ++v) {
+    const int sl = (int)(v % NS);
+    issue((int)((v + NS - 1) % NS));
+    const uint8_t *stg = smem + sl * STAGE;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint8_t *la = stg + s * S::AB, *lb = stg + KS * S::AB + s * S::BB;
+      const uint8_t *lsc = stg + KS * (S::AB + S::BB) + s * S::SC;
+      v8i bf[FN];
+#pragma unroll
+      for (int b = 0; b < FN; ++b) {
+        const v4i x = lds_read16(lb + ob0 + b * 2048), y = lds_read16(lb + ob1 + b * 2048);
+        bf[b] = (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+      }
+      const float wsc = __uint_as_float(lds_load_u32(lsc + 256));
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        const v4i x = lds_read16(la + oa0 + a * 2048), y = lds_read16(la + oa1 + a * 2048);
+        const v8i af = (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        const float sc = __uint_as_float(lds_load_u32(lsc + oxs + a * 64)) * wsc;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          const v4f part = mfma_scaled<F_E4M3, F_E4M3>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f},
+                                                        E8M0_ONE_X4, E8M0_ONE_X4);
+          acc[a][b] += part * sc;
+        }
+      }
+    }
+    if (++csg == nsg) {
+      // Last K step of tile ci: lane (i16, q) holds rows 16a + i16 and
+      // columns 16b + 4q .. +3 of the wave's 32 x 32 block.
+      const StreamTile t = stream_tile(p, gt, j + ci * P);
+      const int64_t row_lim = t.start + t.mg;
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        const int64_t row = t.row0 + wm * 32 + a * 16 + i16;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          const v4f r = acc[a][b];
+          const uint32_t lo = pack_bf16x2(r.x, r.y), hi = pack_bf16x2(r.z, r.w);
+          if (row < row_lim)
+            *(v2i *)(p.D + row * N + t.n0 + wn * 32 + b * 16 + 4 * q) = (v2i){(int)lo, (int)hi};
+          acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      csg = 0;
+      ++ci;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_stage();   // stage v + 1
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmem_le<0>();
 }
 
 }  // namespace mxg

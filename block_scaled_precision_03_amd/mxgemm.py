@@ -18,10 +18,11 @@ FP8_E4M3_TENSOR, FP8_E5M2_TENSOR = 16, 17
 PRESHUFFLED = 0x100
 NT, NN, TN = 0, 1, 2
 GROUPED_MAX_G = 1024
+GROUPED_STREAM, GROUPED_TILED = 0, 1
 
 EXPORTS = (
     "mxgemm_init", "mxgemm_status_string", "mxgemm_run", "mxgemm_validate",
-    "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate",
+    "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate", "grouped_fp8_gemm_variant",
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b",
@@ -45,6 +46,8 @@ _lib.grouped_fp8_gemm_run.restype = _i
 _lib.grouped_fp8_gemm_run.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p]
 _lib.grouped_fp8_gemm_validate.restype = _i
 _lib.grouped_fp8_gemm_validate.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i]
+_lib.grouped_fp8_gemm_variant.restype = _i
+_lib.grouped_fp8_gemm_variant.argtypes = [_i, _i64, _i64, _i64]
 _lib.mxgemm_preshuffle_b_bytes.restype = _i64
 _lib.mxgemm_preshuffle_b_bytes.argtypes = [_i, _i64, _i64]
 _lib.mxgemm_preshuffle_b.restype = _i
@@ -117,6 +120,12 @@ def grouped_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_pres
     return _lib.grouped_fp8_gemm_validate(G, _ptr(m_sizes), _ptr(XQ), _ptr(x_scale), _ptr(WQ),
                                           _ptr(w_scale), _ptr(D), totM, N, K,
                                           int(bool(b_preshuffled)))
+
+
+def grouped_variant(G, totM, N, K):
+    """GROUPED_STREAM or GROUPED_TILED: the kernel grouped_run launches for
+    these shapes on the current device."""
+    return _lib.grouped_fp8_gemm_variant(G, totM, N, K)
 
 
 def preshuffle_b_bytes(fmtB, N, K):

@@ -104,7 +104,8 @@ const char *mxgemm_status_string(int status);
  * D           BF16 [M,N] row-major, written in full.
  * Divisibility: MX needs K % 128 == 0 (E2M1: K % 256 == 0); NN/TN need the
  *             contiguous dimension of each transposed operand (M for A 'T',
- *             N for B 'N') to be a multiple of 16.  Otherwise
+ *             N for B 'N') to be a multiple of 16, and each transposed
+ *             operand to hold fewer than 2^31 - 16 bytes.  Otherwise
  *             MXG_ERR_UNSUPPORTED.  A, B, sA, sB and D must be 16-byte
  *             aligned (MXG_ERR_MISALIGNED).
  * Edge rows/columns (M, N not multiples of the tile) are masked.
@@ -154,6 +155,18 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
                               int b_preshuffled);
 
 /*
+ * grouped_fp8_gemm_variant: which kernel grouped_fp8_gemm_run launches for
+ * these static shapes on the current device (the choice never depends on
+ * m_sizes' contents): MXG_GROUPED_STREAM, the persistent 64 x 64 kernel for
+ * the weight-streaming regime (few rows per group), or MXG_GROUPED_TILED,
+ * 128 x 128 tiles for the matrix-core regime.  Both compute the same
+ * function; the results of the two may differ in the last bit of a BF16
+ * output only where their FP32 sums do.  Never fails.
+ */
+enum { MXG_GROUPED_STREAM = 0, MXG_GROUPED_TILED = 1 };
+int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K);
+
+/*
  * Preshuffle: one-time re-layout of a B operand (weights) into the order in
  * which the matrix-core K-loop consumes it ("Add FlyDSL grouped groupwise FP8
  * GEMM for ROCm", PR body: callers shuffle once at load time).
@@ -161,8 +174,8 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
  * mxgemm_preshuffle_b: B codes of format fmtB (E4M3/E5M2/E2M1, MX or tensor)
  * stored per `layout`'s B ('T' = [N,K], 'N' = [K,N]; E2M1 only [N,K]) ->
  * B_out of mxgemm_preshuffle_b_bytes(fmtB, N, K) bytes, consumable by
- * mxgemm_run with fmtB | MXG_PRESHUFFLED and layout MXG_NT.  Padding beyond N
- * is zero-filled.  K must satisfy mxgemm_run's divisibility rule.
+ * mxgemm_run with fmtB | MXG_PRESHUFFLED and layout MXG_NT.  N is padded to
+ * a multiple of 256 and the padding is zero-filled.  K must satisfy mxgemm_run's divisibility rule.
  */
 int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K);
 int mxgemm_preshuffle_b(int fmtB, int layout, const void *B, void *B_out,

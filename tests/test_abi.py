@@ -91,7 +91,8 @@ def test_preshuffle_sizes():
     m = _mx()
     assert m.preshuffle_b_bytes(0, 4096, 4096) == 4096 * 4096
     assert m.preshuffle_b_bytes(4, 8192, 8192) == 8192 * 8192 // 2
-    assert m.preshuffle_b_bytes(0, 100, 256) == 128 * 256          # rows padded to 64
+    assert m.preshuffle_b_bytes(0, 100, 256) == 256 * 256          # rows padded to 256
+    assert m.preshuffle_b_bytes(4, 300, 512) == 512 * 512 // 2
     assert m.preshuffle_scales_bytes(4096, 4096) == 4096 * 4096 // 32
     assert m.preshuffle_scales_bytes(11008, 11008) == 172 * 22 * 1024
 

@@ -124,3 +124,49 @@ def test_grouped_precondition_violation_is_contained():
     assert np.all(bits[totM:] == SENTINEL_BITS)
     ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
     H.assert_close(H.bf16_to_f64(guard[:30].view(torch.bfloat16)), ref[:30], "group 0")
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_long_k(preshuffled):
+    """K = 2304 (18 steps of 128): the skinny kernel's eight-slot DMA ring
+    wraps twice, and its stages past the last K step read nothing."""
+    N, K = 384, 2304
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(911, [90, 7, 0, 160, 33], N, K)
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped long K")
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_tiled_kernel(preshuffled):
+    """Shapes for which the 128 x 128 kernel runs (the matrix-core regime),
+    uneven groups, one empty, none tile aligned."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 2048, 256
+    split = [1500, 0, 1077, 2100, 1, 700, 2500, 314]
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(921, split, N, K)
+    assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_TILED
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped tiled kernel")
+
+
+def test_grouped_small_shapes_take_the_streaming_kernel():
+    """The parity cases above with few rows run the persistent kernel."""
+    from block_scaled_precision_03_amd import mxgemm
+    for split in SPLITS:
+        assert mxgemm.grouped_variant(len(split), int(sum(split)), 256, 640) == mxgemm.GROUPED_STREAM
+    assert mxgemm.grouped_variant(8, 128, 2048, 7168) == mxgemm.GROUPED_STREAM
+
+
+def test_grouped_many_groups():
+    """G = 150 (more than one 64-group chunk of the persistent kernel's group
+    table), most groups empty or short."""
+    rng = np.random.default_rng(31)
+    split = rng.integers(0, 40, 150)
+    split[rng.random(150) < 0.5] = 0
+    N, K = 128, 256
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(931, split, N, K)
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, True)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped G=150")
