@@ -9,15 +9,19 @@
 // backend for TE PyTorch", Supported Data Types: tensor-wise and mixed
 // E4M3/E5M2 FP8).
 //
-// Block tile 256x256, four waves in a 2x2 grid (128x128 per wave, 8x8
-// matrix-core tiles of 16x16).  Each stage holds 128 bytes of K per row of A
-// and B (one 128-element K step for FP8, two for FP4) in LDS, double
-// buffered (2 x 64 KiB of the 160 KiB).  Operands travel global -> LDS by
-// buffer-load-to-LDS DMA, 16 bytes per lane, into XOR-swizzled rows so that
-// the fragment reads are free of bank conflicts.  Transposed operands (the
-// 'T' side of NN/TN) are kept in LDS k-major and read with the transposing
-// ds_read_b64_tr_b8.  The epilogue stages the BF16 tile through the same LDS
-// and writes 16-byte coalesced rows.
+// Block tile 256x256, eight waves (two per SIMD) in a 2x4 grid (128x64 per
+// wave, 8x4 matrix-core tiles of 16x16).  Each stage holds 128 bytes of K per
+// row of A and B (one 128-element K step for FP8, two for FP4) in LDS, double
+// buffered, plus the MX scales of a group of four K steps.  Operands travel
+// global -> LDS by buffer-load-to-LDS DMA, 16 bytes per lane, issued from
+// inline assembly with explicit waits, into XOR-swizzled rows so that the
+// fragment reads are free of bank conflicts.  Transposed operands (the 'T'
+// side of NN/TN) are kept in LDS k-major and read with the transposing
+// ds_read_b64_tr_b8.  The grid is persistent (one workgroup per compute
+// unit): the tiles of a workgroup share one K pipeline, the next tile's first
+// stage streams in during the current tile's last K step, and a finished
+// tile is stored from registers (BF16, 16-byte rows after a cross-lane
+// exchange) during the next tile's first K step.
 #pragma once
 #include "common.hpp"
 
