@@ -22,6 +22,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-grouped]
        [--no-cpu] [--no-extra] [--only-step] [--copy-probe]
 """
 import hashlib
+import re
 import argparse
 import json
 import os
@@ -71,10 +72,17 @@ def parse():
 
 
 def kernel_source_hash():
+    """SHA-256 of the kernel sources' code: comments and blank lines are
+    dropped, so that editing a comment does not void a measurement but any
+    change to the code does."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 
