@@ -48,11 +48,11 @@ int launch_status() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The persistent grouped kernel: GS_KS K steps per ring stage, GS_NS ring
-// slots (74 KiB of LDS with the group table), GS_OCC workgroups per compute
-// unit, so that one workgroup's wait-barrier-compute chain overlaps the
-// other's.
-constexpr int GS_KS = 2, GS_NS = 2, GS_OCC = 2;
+// The persistent grouped kernels run GS_OCC workgroups per compute unit (74
+// and 59 KiB of LDS with the group table: 64-row tiles with two 128-K steps
+// per ring stage, 128-row tiles with one; two ring slots), so that one
+// workgroup's wait-barrier-compute chain overlaps the other's.
+constexpr int GS_OCC = 2;
 
 // Compute units of the current device: the grid size of the persistent dense
 // kernel (one workgroup per compute unit).  Queried once per device.
@@ -262,19 +262,22 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   a.N = N;
   a.K = K;
   a.G = G;
-  const bool stream_kernel = grouped_fp8_gemm_variant(G, totM, N, K) == MXG_GROUPED_STREAM;
-  const int B = stream_kernel ? GroupedStream::BM : 128;   // square tiles
-  a.tiles_n = (int)(N / B);
-  const int64_t blocks = (cdiv(totM, B) + G - 1) * a.tiles_n;
+  const int variant = grouped_fp8_gemm_variant(G, totM, N, K);
+  const int BM = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
+  const int BN = variant == MXG_GROUPED_TILED ? 128 : 64;
+  a.tiles_n = (int)(N / BN);
+  const int64_t blocks = (cdiv(totM, BM) + G - 1) * a.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
-  if (stream_kernel) {
-    // persistent: GS_OCC workgroups per compute unit (fewer if fewer tiles)
-    const unsigned P = (unsigned)std::min<int64_t>(blocks, (int64_t)GS_OCC * cu_count());
-    if (b_preshuffled)
-      hipLaunchKernelGGL((grouped_stream_kernel<true, GS_KS, GS_NS>), dim3(P), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((grouped_stream_kernel<false, GS_KS, GS_NS>), dim3(P), dim3(256), 0, stream, a);
-  } else if (b_preshuffled) {
+  // persistent kernels: GS_OCC workgroups per compute unit (fewer if fewer tiles)
+  const unsigned P = (unsigned)std::min<int64_t>(blocks, (int64_t)GS_OCC * cu_count());
+  const bool pre = b_preshuffled != 0;
+  if (variant == MXG_GROUPED_STREAM64) {
+    if (pre) hipLaunchKernelGGL((grouped_stream_kernel<true, 64, 2, 2>), dim3(P), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((grouped_stream_kernel<false, 64, 2, 2>), dim3(P), dim3(256), 0, stream, a);
+  } else if (variant == MXG_GROUPED_STREAM128) {
+    if (pre) hipLaunchKernelGGL((grouped_stream_kernel<true, 128, 1, 2>), dim3(P), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((grouped_stream_kernel<false, 128, 1, 2>), dim3(P), dim3(256), 0, stream, a);
+  } else if (pre) {
     hipLaunchKernelGGL((grouped_kernel<128, 128, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((grouped_kernel<128, 128, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
@@ -283,24 +286,30 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
 }
 
 // Kernel choice from the static shapes (the host never reads m_sizes): the
-// estimated time of each, from the tile counts' upper bounds.
-//  - persistent 64 x 64 (weight streaming): ~0.6 us per 128-K tile step per
-//    workgroup, GS_OCC workgroups per compute unit, walking all tile steps
-//    evenly; at least the weights' bytes at ~5 TB/s.
+// estimated time of each, from upper bounds of the tile counts.
+//  - persistent, 64 x 64 or 128 x 64 tiles (weight streaming): ~0.6 or
+//    ~0.87 us per 128-K tile step per workgroup, GS_OCC workgroups per
+//    compute unit walking all tile steps evenly; at least the weights' bytes
+//    at ~5 TB/s.
 //  - 128 x 128 (two workgroups per compute unit, one tile each): ~1.25 us
 //    per K step per round of resident workgroups; at least the weights'
 //    bytes at ~4 TB/s.
-// The constants are fitted to measured times of both kernels on MI355X over
-// totM 128 .. 8192, (N, K) = (2048, 7168) and (7168, 2304), G = 8.
+// The constants are fitted to measured times of the three kernels on MI355X
+// over totM 128 .. 8192, (N, K) = (2048, 7168) and (7168, 2304), G = 8.
 extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K) {
-  if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM;
-  const double slots = 2.0 * cu_count(), nst = (double)(K / 128);
+  if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM64;
+  const double cus = cu_count(), nst = (double)(K / 128);
   const double wbytes = (double)G * (double)N * (double)K;
-  const double steps_s = (double)(cdiv(totM, 64) + G - 1) * (double)(N / 64) * nst;
-  const double t_s = std::max(0.6 * steps_s / ((double)GS_OCC * cu_count()), wbytes / 5.0e6);
+  const double tiles_n = (double)(N / 64);
+  const double slots = (double)GS_OCC * cus;
+  const double t64 = std::max(0.6 * (double)(cdiv(totM, 64) + G - 1) * tiles_n * nst / slots,
+                              wbytes / 5.0e6);
+  const double t128 = std::max(0.87 * (double)(cdiv(totM, 128) + G - 1) * tiles_n * nst / slots,
+                               wbytes / 5.0e6);
   const double blocks_o = (double)(cdiv(totM, 128) + G - 1) * (double)(N / 128);
-  const double t_o = std::max(1.25 * std::ceil(blocks_o / slots) * nst, wbytes / 4.0e6);
-  return t_s <= t_o ? MXG_GROUPED_STREAM : MXG_GROUPED_TILED;
+  const double t_o = std::max(1.25 * std::ceil(blocks_o / (2.0 * cus)) * nst, wbytes / 4.0e6);
+  if (t64 <= t128 && t64 <= t_o) return MXG_GROUPED_STREAM64;
+  return t128 <= t_o ? MXG_GROUPED_STREAM128 : MXG_GROUPED_TILED;
 }
 
 extern "C" int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K) {

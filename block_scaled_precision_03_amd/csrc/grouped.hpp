@@ -168,17 +168,21 @@ namespace mxg {
 //   add the partial times xs(row, kb) * ws(g, n/128, kb) in FP32.  A tile's
 //   result is stored as BF16 straight from the accumulators.
 // * 8-row blocks of A past the tile's group read nothing (empty range).
+// Tile BM x 64 (BM = 64 or 128), four waves in a 2 x 2 grid of
+// (BM/2) x 32 each.
+template <int BM_>
 struct GroupedStream {
-  static constexpr int BM = 64, BN = 64;
-  static constexpr int FM = 2, FN = 2;
+  static constexpr int BM = BM_, BN = 64;
+  static constexpr int FM = BM / 32, FN = 2;
   static constexpr int AB = BM * 128, BB = BN * 128;
-  static constexpr int SC = 512;                    // xs (64 floats) + ws (64 copies)
+  static constexpr int SC = BM * 4 + 256;           // xs (BM floats) + ws (64 copies)
   static constexpr int STEP = AB + BB + SC;         // one 128-K step
+  static constexpr int ABLK = BM / 32;              // A DMAs per wave and K step
 };
 
 // Group table of a workgroup, in LDS: rows[g] = first row of group g (groups
 // clamped to [0, totM) in order, so rows[g] = min(sum of the earlier
-// max(m_sizes, 0), totM)), mtile[g] = number of 64-row tiles of the groups
+// max(m_sizes, 0), totM)), mtile[g] = number of BM-row tiles of the groups
 // before g; entry G closes both.  Built by wave 0 with a 64-lane prefix sum
 // per chunk of 64 groups.
 struct GroupTable {
@@ -195,8 +199,8 @@ __device__ inline int64_t wave_incl_sum(int64_t x, int lane) {
   return x;
 }
 
+template <int BM>
 __device__ inline void build_group_table(const GroupedArgs &p, GroupTable &gt, int lane) {
-  constexpr int BM = GroupedStream::BM;
   int64_t rows = 0, tiles = 0;
   for (int c = 0; c < p.G; c += 64) {
     const int g = c + lane;
@@ -229,8 +233,9 @@ struct StreamTile {
   int g;
 };
 
+template <int BM>
 __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable &gt, int64_t t) {
-  const int32_t u = (int32_t)(t / p.tiles_n);        // 64-row tile index over all groups
+  const int32_t u = (int32_t)(t / p.tiles_n);        // BM-row tile index over all groups
   // the last group g with mtile[g] <= u (a non-empty one: an empty group
   // shares its mtile with the group after it)
   int lo = 0, hi = p.G - 1;
@@ -248,21 +253,21 @@ __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable 
   r.g = g;
   r.start = r0;
   r.mg = uni32(gt.rows[g + 1]) - r0;
-  r.row0 = r.start + tm * GroupedStream::BM;
-  r.n0 = tn * GroupedStream::BN;
+  r.row0 = r.start + tm * BM;
+  r.n0 = tn * 64;
   return r;
 }
 
-// KS 128-K steps per ring stage, NS ring slots.
-template <bool PSB, int KS, int NS>
+// BM-row tiles, KS 128-K steps per ring stage, NS ring slots.
+template <bool PSB, int BM, int KS, int NS>
 __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
-  typedef GroupedStream S;
-  constexpr int BM = S::BM, FM = S::FM, FN = S::FN;
+  typedef GroupedStream<BM> S;
+  constexpr int FM = S::FM, FN = S::FN, ABLK = S::ABLK;
   constexpr int STAGE = KS * S::STEP;
-  // DMAs per stage and wave: A and B two each per K step, plus one per K
-  // step for the activation scales (wave 0) or the weight block scale
-  // (wave 1).
-  constexpr int OPS_LO = 4 * KS, OPS_HI = 5 * KS;
+  // DMAs per stage and wave: ABLK for A and two for B per K step, plus one
+  // per K step for the activation scales (waves 0 and, with 128 rows, 2) or
+  // the weight block scale (wave 1).
+  constexpr int OPS_LO = (ABLK + 2) * KS, OPS_HI = (ABLK + 3) * KS;
   static_assert(OPS_HI * (NS - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   __shared__ GroupTable gt;
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   const int wm = w >> 1, wn = w & 1;
   const int i16 = lane & 15, q = lane >> 4;
 
-  if (w == 0) build_group_table(p, gt, lane);
+  if (w == 0) build_group_table<BM>(p, gt, lane);
   __syncthreads();
   const int P = (int)gridDim.x;
   int j = (int)blockIdx.x;
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     int vrows;
   };
   auto make_src = [&](int64_t i) {
-    const StreamTile t = stream_tile(p, gt, j + i * P);
+    const StreamTile t = stream_tile<BM>(p, gt, j + i * P);
     Src s;
     const int64_t abase = t.row0 * K;
     s.ra = rsrc4(p.XQ + abase, clamp_records(p.totM * K - abase));
@@ -337,11 +342,11 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
       const uint32_t ka = slot + (uint32_t)s * S::AB;
       const uint32_t kb = slot + (uint32_t)(KS * S::AB + s * S::BB);
       const uint32_t ksc = slot + (uint32_t)(KS * (S::AB + S::BB) + s * S::SC);
-      static_for<0, 2>([&](auto jc) {
+      static_for<0, ABLK>([&](auto jc) {
         constexpr int jj = decltype(jc)::value;
-        const int blk = 2 * w + jj;
+        const int blk = ABLK * w + jj;
         const u32x4 r = (live && blk * 8 < src.vrows) ? src.ra : rzero;
-        dma_asm_v<16>(ka + (uint32_t)blk * 1024u, r, vo[jj], (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
+        dma_asm_v<16>(ka + (uint32_t)blk * 1024u, r, vo[jj & 1], (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
       });
       const u32x4 rb = live ? src.rb : rzero;
       static_for<0, 2>([&](auto jc) {
@@ -354,8 +359,11 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
           dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, vo[jj],
                       (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
       });
-      if (w == 0) dma_asm_v<4>(ksc, live ? rx : rzero, (uint32_t)lane * 4u, src.xs0 + (uint32_t)st * src.mg4);
-      if (w == 1) dma_asm<4>(ksc + 256u, live ? rw : rzero, 0u, src.ws0 + (uint32_t)st * 4u);
+      // activation scales of rows 64h .. 64h + 63 by wave 2h
+      if ((w & 1) == 0 && 32 * w < BM)
+        dma_asm_v<4>(ksc + (uint32_t)(128 * w), live ? rx : rzero, (uint32_t)lane * 4u,
+                     src.xs0 + (uint32_t)(128 * w) + (uint32_t)st * src.mg4);
+      if (w == 1) dma_asm<4>(ksc + (uint32_t)(BM * 4), live ? rw : rzero, 0u, src.ws0 + (uint32_t)st * 4u);
     });
     if (++iss_sg == nsg) {
       iss_sg = 0;
@@ -366,8 +374,9 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   // Stage v has landed once only this wave's DMAs of the NS - 2 stages
   // issued after it (and any result stores, issued later still) are
   // outstanding.
+  const bool hi_ops = w < 2 || (BM == 128 && w == 2);
   auto wait_stage = [&]() {
-    if (w < 2) wait_vmem_le<OPS_HI * (NS - 2)>();
+    if (hi_ops) wait_vmem_le<OPS_HI * (NS - 2)>();
     else wait_vmem_le<OPS_LO * (NS - 2)>();
   };
 
@@ -379,12 +388,12 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
 
   // fragment lane offsets
   const int f = (i16 & 7) ^ (i16 >> 3);
-  const uint32_t oa0 = (uint32_t)((wm * 32 + i16) * 128 + ((q ^ f) << 4));
-  const uint32_t oa1 = (uint32_t)((wm * 32 + i16) * 128 + (((q + 4) ^ f) << 4));
+  const uint32_t oa0 = (uint32_t)((wm * (BM / 2) + i16) * 128 + ((q ^ f) << 4));
+  const uint32_t oa1 = (uint32_t)((wm * (BM / 2) + i16) * 128 + (((q + 4) ^ f) << 4));
   const uint32_t ob0 = PSB ? (uint32_t)(wn * 2 * 2048 + lane * 16)
                            : (uint32_t)((wn * 32 + i16) * 128 + ((q ^ f) << 4));
   const uint32_t ob1 = PSB ? ob0 + 1024u : (uint32_t)((wn * 32 + i16) * 128 + (((q + 4) ^ f) << 4));
-  const uint32_t oxs = (uint32_t)((wm * 32 + i16) * 4);
+  const uint32_t oxs = (uint32_t)((wm * (BM / 2) + i16) * 4);
 
   for (int s = 0; s < NS - 1; ++s) issue(s);
   wait_stage();
@@ -406,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
         const v4i x = lds_read16(lb + ob0 + b * 2048), y = lds_read16(lb + ob1 + b * 2048);
         bf[b] = (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
       }
-      const float wsc = __uint_as_float(lds_load_u32(lsc + 256));
+      const float wsc = __uint_as_float(lds_load_u32(lsc + BM * 4));
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         const v4i x = lds_read16(la + oa0 + a * 2048), y = lds_read16(la + oa1 + a * 2048);
@@ -423,11 +432,11 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     if (++csg == nsg) {
       // Last K step of tile ci: lane (i16, q) holds rows 16a + i16 and
       // columns 16b + 4q .. +3 of the wave's 32 x 32 block.
-      const StreamTile t = stream_tile(p, gt, j + ci * P);
+      const StreamTile t = stream_tile<BM>(p, gt, j + ci * P);
       const int64_t row_lim = t.start + t.mg;
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
-        const int64_t row = t.row0 + wm * 32 + a * 16 + i16;
+        const int64_t row = t.row0 + wm * (BM / 2) + a * 16 + i16;
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
           const v4f r = acc[a][b];

@@ -18,7 +18,7 @@ FP8_E4M3_TENSOR, FP8_E5M2_TENSOR = 16, 17
 PRESHUFFLED = 0x100
 NT, NN, TN = 0, 1, 2
 GROUPED_MAX_G = 1024
-GROUPED_STREAM, GROUPED_TILED = 0, 1
+GROUPED_STREAM64, GROUPED_TILED, GROUPED_STREAM128 = 0, 1, 2
 
 EXPORTS = (
     "mxgemm_init", "mxgemm_status_string", "mxgemm_run", "mxgemm_validate",
@@ -123,8 +123,8 @@ def grouped_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_pres
 
 
 def grouped_variant(G, totM, N, K):
-    """GROUPED_STREAM or GROUPED_TILED: the kernel grouped_run launches for
-    these shapes on the current device."""
+    """GROUPED_STREAM64, GROUPED_STREAM128 or GROUPED_TILED: the kernel
+    grouped_run launches for these shapes on the current device."""
     return _lib.grouped_fp8_gemm_variant(G, totM, N, K)
 
 

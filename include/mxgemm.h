@@ -157,13 +157,14 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
 /*
  * grouped_fp8_gemm_variant: which kernel grouped_fp8_gemm_run launches for
  * these static shapes on the current device (the choice never depends on
- * m_sizes' contents): MXG_GROUPED_STREAM, the persistent 64 x 64 kernel for
- * the weight-streaming regime (few rows per group), or MXG_GROUPED_TILED,
- * 128 x 128 tiles for the matrix-core regime.  Both compute the same
- * function; the results of the two may differ in the last bit of a BF16
- * output only where their FP32 sums do.  Never fails.
+ * m_sizes' contents): MXG_GROUPED_STREAM64 or MXG_GROUPED_STREAM128, the
+ * persistent kernel with 64 x 64 or 128 x 64 tiles for the weight-streaming
+ * regime (few rows per group), or MXG_GROUPED_TILED, 128 x 128 tiles for the
+ * matrix-core regime.  All compute the same function; their results may
+ * differ in the last bit of a BF16 output only where their FP32 sums do.
+ * Never fails.
  */
-enum { MXG_GROUPED_STREAM = 0, MXG_GROUPED_TILED = 1 };
+enum { MXG_GROUPED_STREAM64 = 0, MXG_GROUPED_TILED = 1, MXG_GROUPED_STREAM128 = 2 };
 int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K);
 
 /*

@@ -151,22 +151,34 @@ def test_grouped_tiled_kernel(preshuffled):
     H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped tiled kernel")
 
 
-def test_grouped_small_shapes_take_the_streaming_kernel():
-    """The parity cases above with few rows run the persistent kernel."""
+def test_grouped_small_shapes_take_the_streaming_kernels():
+    """The parity cases above with few rows run the persistent kernels, both
+    tile heights among them; the benchmark's 128-row shapes take 64 x 64."""
     from block_scaled_precision_03_amd import mxgemm
-    for split in SPLITS:
-        assert mxgemm.grouped_variant(len(split), int(sum(split)), 256, 640) == mxgemm.GROUPED_STREAM
-    assert mxgemm.grouped_variant(8, 128, 2048, 7168) == mxgemm.GROUPED_STREAM
+    got = {mxgemm.grouped_variant(len(split), int(sum(split)), 256, 640) for split in SPLITS}
+    assert got == {mxgemm.GROUPED_STREAM64, mxgemm.GROUPED_STREAM128}
+    assert mxgemm.grouped_variant(8, 128, 2048, 7168) == mxgemm.GROUPED_STREAM64
+    assert mxgemm.grouped_variant(8, 128, 7168, 2304) == mxgemm.GROUPED_STREAM64
 
 
-def test_grouped_many_groups():
-    """G = 150 (more than one 64-group chunk of the persistent kernel's group
-    table), most groups empty or short."""
-    rng = np.random.default_rng(31)
-    split = rng.integers(0, 40, 150)
-    split[rng.random(150) < 0.5] = 0
-    N, K = 128, 256
-    m_sizes, XQ, xs, WQ, ws, totM = _inputs(931, split, N, K)
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, True)
-    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
-    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped G=150")
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_stream128_kernel(preshuffled):
+    """Shapes for which the persistent kernel runs with 128 x 64 tiles: uneven
+    groups (one empty, none tile aligned), sampled entries and every group's
+    first and last rows against the oracle, every row written."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 512, 2048
+    split = [700, 0, 1, 1157, 129, 1013]
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(941, split, N, K)
+    assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_STREAM128
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    d = H.bf16_to_f64(D.view(torch.bfloat16))
+    assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
+    rng = np.random.default_rng(5)
+    im, inn = H.sample_indices(rng, totM, N, 4000)
+    starts = np.concatenate([[0], np.cumsum(m_sizes)])
+    edge = np.array([r for g in range(len(split)) if split[g] for r in (starts[g], starts[g + 1] - 1)])
+    im = np.concatenate([im, np.repeat(edge, N)])
+    inn = np.concatenate([inn, np.tile(np.arange(N), len(edge))])
+    ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
+    H.assert_close(d[im, inn], ref, "grouped 128-row tiles")
