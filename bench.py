@@ -248,31 +248,35 @@ def time_calls(torch, call, reps=20, warmup=3):
 
 
 def tensorwise_bench(torch, synth, mxgemm, dev):
-    """Tensor-wise FP8 (E4M3 A x E5M2 B, FP32 per-tensor scales) GEMMs of a
-    4096 -> 11008 linear layer at 8192 tokens in its three layouts."""
+    """Tensor-wise FP8 (FP32 per-tensor scales) GEMMs of a 4096 -> 11008
+    linear layer at 8192 tokens in its three layouts, each with both format
+    assignments: E4M3 A x E5M2 B, and E5M2 A x E4M3 B (for the data and
+    weight gradients A is the gradient, E5M2 in hybrid FP8 training)."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     out = []
+    fmt = {"e4m3": mxgemm.FP8_E4M3_TENSOR, "e5m2": mxgemm.FP8_E5M2_TENSOR}
     for idx, (name, layout, M, N, K) in enumerate(C3_CASES):
         a = synth.normal(synth.seed_for(3, 1, idx), (M, K))
         b = synth.normal(synth.seed_for(3, 2, idx), (N, K), 0.02)
-        qa, sa = synth.quant_tensor(a, "e4m3")
-        qb, sb = synth.quant_tensor(b, "e5m2")
+        for ea, eb in (("e4m3", "e5m2"), ("e5m2", "e4m3")):
+            qa, sa = synth.quant_tensor(a, ea)
+            qb, sb = synth.quant_tensor(b, eb)
+            if layout == mxgemm.TN:
+                qa = qa.T
+            if layout in (mxgemm.NN, mxgemm.TN):
+                qb = qb.T
+            A, B = t(qa), t(qb)
+            SA, SB = t(np.array([sa], np.float32)), t(np.array([sb], np.float32))
+            D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            us = time_calls(torch, lambda: mxgemm.run(fmt[ea], fmt[eb], layout, A, SA, B, SB, D, M, N, K))
+            tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            out.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "A": ea, "B": eb,
+                        "M": M, "N": N, "K": K, "us": us, "tflops": tf,
+                        "pct_peak": 100.0 * tf / PEAK_FP8_TFLOPS})
+            log("tensor-wise %s %s %s x %s (%d,%d,%d): %.1f us, %.0f TFLOP/s (%.1f%% of FP8 peak)" % (
+                name, out[-1]["layout"], ea, eb, M, N, K, us, tf, 100.0 * tf / PEAK_FP8_TFLOPS))
+            del A, B, D
         del a, b
-        if layout == mxgemm.TN:
-            qa = qa.T
-        if layout in (mxgemm.NN, mxgemm.TN):
-            qb = qb.T
-        A, B = t(qa), t(qb)
-        SA, SB = t(np.array([sa], np.float32)), t(np.array([sb], np.float32))
-        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        us = time_calls(torch, lambda: mxgemm.run(mxgemm.FP8_E4M3_TENSOR, mxgemm.FP8_E5M2_TENSOR,
-                                                  layout, A, SA, B, SB, D, M, N, K))
-        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
-        out.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "M": M, "N": N, "K": K,
-                    "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_FP8_TFLOPS})
-        log("tensor-wise %s %s (%d,%d,%d): %.1f us, %.0f TFLOP/s (%.1f%% of FP8 peak)" % (
-            name, out[-1]["layout"], M, N, K, us, tf, 100.0 * tf / PEAK_FP8_TFLOPS))
-        del A, B, D
     torch.cuda.empty_cache()
     return out
 

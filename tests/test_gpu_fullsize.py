@@ -56,18 +56,21 @@ C3 = [
 ]
 
 
+@pytest.mark.parametrize("fa,fb", [(T4, T5), (T5, T4)])
 @pytest.mark.parametrize("name,layout,M,N,K", C3)
-def test_tensorwise_linear_layer(name, layout, M, N, K):
+def test_tensorwise_linear_layer(name, layout, M, N, K, fa, fb):
+    """Both format assignments: E4M3 A x E5M2 B, and E5M2 A x E4M3 B (for
+    the data and weight gradients, A is the gradient dY)."""
     idx = [c[0] for c in C3].index(name)
     ta = layout == TN
     tb = layout in (NN, TN)
     a = synth.normal(synth.seed_for(3, 1, idx), (M, K))
     b = synth.normal(synth.seed_for(3, 2, idx), (N, K), 0.02)
-    opA = H.make_operand(T4, a, ta)
-    opB = H.make_operand(T5, b, tb)
+    opA = H.make_operand(fa, a, ta)
+    opB = H.make_operand(fb, b, tb)
     del a, b
     D = H.run_dense(layout, opA, opB, M, N, K)
-    _check_sampled(D, opA, opB, M, N, K, "tensor-wise %s" % name)
+    _check_sampled(D, opA, opB, M, N, K, "tensor-wise %s (%d, %d)" % (name, fa, fb))
 
 
 def test_mxfp4_8192_cube():
