@@ -205,6 +205,53 @@ def grouped_bench(torch, synth, mxgemm, dev, reps=50):
             b.record()
             torch.cuda.synchronize()
             res[name + "_us"] = a.elapsed_time(b) * 1000.0 / reps
+        # graph replay (the pages quote replay latency): one captured call,
+        # replayed with per-replay events; its output must equal the eager one
+        call_pre = lambda: mxgemm.grouped_run(G, dm, dx, dxs, wps[0], dws, D, totM, N, K,
+                                              b_preshuffled=True)
+        call_pre()
+        torch.cuda.synchronize()
+        eager = D.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                call_pre()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call_pre()
+        D.zero_()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+        for _ in range(10):
+            graph.replay()
+        for ea, eb in evs:
+            ea.record()
+            graph.replay()
+            eb.record()
+        torch.cuda.synchronize()
+        rep_us = np.array([ea.elapsed_time(eb) * 1000.0 for ea, eb in evs])
+        res["graph_replay_us"] = {"median": float(np.median(rep_us)), "p10": float(np.percentile(rep_us, 10)),
+                                  "p90": float(np.percentile(rep_us, 90))}
+        res["graph_replay_matches_eager"] = bool(torch.equal(D.view(torch.int16), eager.view(torch.int16)))
+        # ten calls per graph: the per-call time with the graph launch amortized
+        graph10 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph10):
+            for _ in range(10):
+                call_pre()
+        for _ in range(3):
+            graph10.replay()
+        torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        for _ in range(20):
+            graph10.replay()
+        eb.record()
+        torch.cuda.synchronize()
+        res["graph_replay_x10_us_per_call"] = ea.elapsed_time(eb) * 1000.0 / 200
+        del graph, graph10, eager
         # cold: rotate through weight copies totalling > 256 MB
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -224,8 +271,13 @@ def grouped_bench(torch, synth, mxgemm, dev, reps=50):
         res["algo_bytes"] = hbm
         res["gbs_cold"] = hbm / (res["preshuffled_cold_us"] * 1e-6) / 1e9
         out.append(res)
-        log("grouped %s: plain %.1f us, preshuffled %.1f us, cold %.1f us (%.0f GB/s)" % (
-            (totM, N, K), res["plain_us"], res["preshuffled_us"], res["preshuffled_cold_us"], res["gbs_cold"]))
+        res["kernel"] = ["persistent 64x64", "128x128", "persistent 128x64"][mxgemm.grouped_variant(G, totM, N, K)]
+        log("grouped %s: plain %.1f us, preshuffled %.1f us, graph replay median %.1f us (p10 %.1f, p90 %.1f%s), "
+            "10-call graph %.1f us/call, cold %.1f us (%.0f GB/s) [%s]" % (
+                (totM, N, K), res["plain_us"], res["preshuffled_us"], res["graph_replay_us"]["median"],
+                res["graph_replay_us"]["p10"], res["graph_replay_us"]["p90"],
+                "" if res["graph_replay_matches_eager"] else ", REPLAY OUTPUT DIFFERS",
+                res["graph_replay_x10_us_per_call"], res["preshuffled_cold_us"], res["gbs_cold"], res["kernel"]))
         del wps, wplain, dx, D
         torch.cuda.empty_cache()
     return out
