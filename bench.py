@@ -333,6 +333,33 @@ def tensorwise_bench(torch, synth, mxgemm, dev):
     return out
 
 
+def mfma_ceiling(torch, mxgemm, dev):
+    """What the scaled matrix-core instruction sustains with nothing else
+    running (FP8 and FP4 operands), and the shader clock meanwhile."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for name, fmt, iters in (("fp8", mxgemm.MXFP8_E4M3, 20000), ("fp4", mxgemm.MXFP4_E2M1, 40000)):
+        clk = torch.zeros(3, dtype=torch.int64, device=dev)
+        mxgemm.mfma_ceiling(fmt, 200, clk)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mxgemm.mfma_ceiling(fmt, iters, clk)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1000.0
+        flops = float(cus) * 8 * iters * 32 * 2 * 16 * 16 * 128
+        ticks, ref = [int(v) for v in clk[:2].cpu()]
+        mhz = 100.0 * ticks / ref if ref else None
+        peak = PEAK_MXFP4_TFLOPS if name == "fp4" else PEAK_MXFP8_TFLOPS
+        out[name] = {"tflops": flops / (us * 1e-6) / 1e12, "shader_clock_mhz": mhz,
+                     "pct_of_published_peak": 100.0 * flops / (us * 1e-6) / 1e12 / peak}
+        log("MFMA ceiling %s: %.0f TFLOP/s (%.1f%% of the published peak), shader clock %s MHz" % (
+            name, out[name]["tflops"], out[name]["pct_of_published_peak"],
+            "%.0f" % mhz if mhz else "n/a"))
+    return out
+
+
 def mxfp4_bench(torch, synth, mxgemm, dev):
     """MXFP4 NT GEMM, M = N = K = 8192, preshuffled B."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -457,6 +484,9 @@ def main():
         result["tensorwise_fp8"] = tensorwise_bench(torch, synth, mxgemm, dev)
         log("MXFP4 ...")
         result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
+        result["mfma_ceiling"] = mfma_ceiling(torch, mxgemm, dev)
+        result["roofline"]["frac_of_mfma_ceiling"] = (
+            result["roofline"]["achieved"] / result["mfma_ceiling"]["fp8"]["tflops"])
     if not args.only_step and not args.no_cpu:
         log("CPU oracle sample ...")
         result["cpu_baseline"] = cpu_baseline(synth)

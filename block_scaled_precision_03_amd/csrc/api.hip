@@ -12,6 +12,7 @@
 #include "dense.hpp"
 #include "grouped.hpp"
 #include "preshuffle.hpp"
+#include "diag.hpp"
 
 using namespace mxg;
 
@@ -382,3 +383,15 @@ extern "C" int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out, int
   return launch_status();
 }
 
+
+extern "C" int mxgemm_mfma_ceiling(int fmt, int64_t iters, void *clk, hipStream_t stream) {
+  const FmtInfo f = fmt_info(fmt);
+  if (!f.ok || iters < 0 || !clk) return MXG_ERR_INVALID_ARG;
+  if (!aligned(clk, 8)) return MXG_ERR_MISALIGNED;
+  const unsigned grid = (unsigned)cu_count();
+  if (f.elem == F_E2M1)
+    hipLaunchKernelGGL((mfma_ceiling_kernel<F_E2M1>), dim3(grid), dim3(512), 0, stream, iters, (uint64_t *)clk);
+  else
+    hipLaunchKernelGGL((mfma_ceiling_kernel<F_E4M3>), dim3(grid), dim3(512), 0, stream, iters, (uint64_t *)clk);
+  return launch_status();
+}

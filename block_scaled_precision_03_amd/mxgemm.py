@@ -25,7 +25,7 @@ EXPORTS = (
     "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate", "grouped_fp8_gemm_variant",
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
-    "grouped_fp8_preshuffle_b",
+    "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -56,6 +56,8 @@ _lib.mxgemm_preshuffle_scales_bytes.restype = _i64
 _lib.mxgemm_preshuffle_scales_bytes.argtypes = [_i64, _i64]
 _lib.mxgemm_preshuffle_scales.restype = _i
 _lib.mxgemm_preshuffle_scales.argtypes = [_p, _p, _i64, _i64, _p]
+_lib.mxgemm_mfma_ceiling.restype = _i
+_lib.mxgemm_mfma_ceiling.argtypes = [_i, _i64, _p, _p]
 _lib.grouped_fp8_preshuffle_b.restype = _i
 _lib.grouped_fp8_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
 
@@ -149,3 +151,9 @@ def preshuffle_scales(s, s_out, rows, K, stream=None):
 def grouped_preshuffle_b(G, WQ, WQ_out, N, K, stream=None):
     _check(_lib.grouped_fp8_preshuffle_b(G, _ptr(WQ), _ptr(WQ_out), N, K, _stream(stream)),
            "grouped_fp8_preshuffle_b")
+
+
+def mfma_ceiling(fmt, iters, clk, stream=None):
+    """Matrix-core throughput probe (see include/mxgemm.h); clk: device
+    tensor of three int64."""
+    _check(_lib.mxgemm_mfma_ceiling(fmt, iters, _ptr(clk), _stream(stream)), "mxgemm_mfma_ceiling")

@@ -200,6 +200,21 @@ int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K
 int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out,
                              int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * mxgemm_mfma_ceiling -- a measurement aid, not part of the GEMM path: one
+ * workgroup per compute unit, eight waves each running 32 independent chains
+ * of the scaled 16x16x128 matrix-core instruction for `iters` iterations
+ * (2 * 16 * 16 * 128 FLOP per instruction), E4M3 operands for an FP8 fmt and
+ * E2M1 for MXG_MXFP4_E2M1, neutral scales.  Its time gives the throughput the
+ * instruction sustains on this device with nothing else running.  clk: device
+ * memory for three uint64 (8-byte aligned); the call writes the shader-clock
+ * ticks (s_memtime) and 100 MHz reference ticks (s_memrealtime) that wave 0
+ * of workgroup 0 spent in the loop to clk[0] and clk[1] (their ratio times
+ * 100 MHz is the shader clock under that load).  Errors: MXG_ERR_INVALID_ARG
+ * (unknown fmt, iters < 0, null clk), MXG_ERR_MISALIGNED.
+ */
+int mxgemm_mfma_ceiling(int fmt, int64_t iters, void *clk, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
