@@ -144,7 +144,8 @@ def c2_inputs(torch, synth, mxgemm, dev, preshuffle):
 
 def time_step(torch, mxgemm, calls, steps, warmup):
     """Run `calls` (list of closures) per step; per-launch HIP events on the
-    launch stream.  Returns (ms_per_step, per-call mean ms)."""
+    launch stream.  Returns (ms_per_step, per-call mean ms, wall seconds,
+    [steps, calls] per-launch ms)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         for c in calls:
@@ -167,7 +168,7 @@ def time_step(torch, mxgemm, calls, steps, warmup):
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
     per = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
-    return total_ms / steps, per.mean(axis=0), wall
+    return total_ms / steps, per.mean(axis=0), wall, per
 
 
 def grouped_bench(torch, synth, mxgemm, dev, reps=50):
@@ -441,15 +442,18 @@ def main():
                       mxgemm.run(mxgemm.MXFP8_E4M3, fmtB, mxgemm.NT, qa, sa, qb, sb, D, M, N, K)))
         flops.append(2.0 * M * N * K)
     log("timing %d steps (+%d warmup) ..." % (args.steps, args.warmup))
-    ms, per_ms, wall = time_step(torch, mxgemm, calls, args.steps, args.warmup)
+    ms, per_ms, wall, per_all = time_step(torch, mxgemm, calls, args.steps, args.warmup)
     step_flops = sum(flops)
     value = step_flops / (ms * 1e-3) / 1e12
     kernel_ms = float(per_ms.sum())
     achieved = step_flops / (kernel_ms * 1e-3) / 1e12
     per_gemm = []
-    for (shape, f, pm) in zip(C2_SHAPES, flops, per_ms):
+    for i, (shape, f, pm) in enumerate(zip(C2_SHAPES, flops, per_ms)):
         tf = f / (pm * 1e-3) / 1e12
+        col = per_all[:, i] * 1000.0
         per_gemm.append({"M": shape[0], "N": shape[1], "K": shape[2], "us": pm * 1000.0,
+                         "us_median": float(np.median(col)), "us_p10": float(np.percentile(col, 10)),
+                         "us_p90": float(np.percentile(col, 90)),
                          "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP8_TFLOPS})
         log("  %s: %.1f us, %.0f TFLOP/s (%.1f%% of peak)" % (shape, pm * 1000, tf, 100 * tf / PEAK_MXFP8_TFLOPS))
     log("step: %.3f ms -> %.0f TFLOP/s" % (ms, value))
