@@ -17,6 +17,8 @@
 //   k-block kb) sits at i + kb*M_g.
 // * B is either plain [G, N, K] (staged through XOR-swizzled LDS like A) or
 //   preshuffled per group (copied linearly into LDS).
+// This file holds two kernels: grouped_kernel (128 x 128 tiles, one tile per
+// workgroup, for many rows per group) and grouped_stream_kernel (below).
 #pragma once
 #include "../../include/mxgemm.h"
 #include "dense.hpp"
@@ -150,26 +152,26 @@ namespace mxg {
 // Grouped kernel for few rows per group (the weight-streaming regime: the
 // weights dominate the bytes and HBM, not the matrix cores, sets the time).
 //
-// * 64 x 64 output tiles.  The real tiles (groups with rows only, none
-//   spanning two groups) are numbered group by group, N-tile major and M-tile
-//   minor, so that consecutive tiles share one weight tile.
-// * Persistent grid of P workgroups, one per compute unit: workgroup j walks
+// * BM x 64 output tiles (BM = 64 or 128).  The real tiles (groups with rows
+//   only, none spanning two groups) are numbered group by group, N-tile
+//   major and M-tile minor, so that consecutive tiles share one weight tile.
+//   Each workgroup finds a tile's group by binary search in a table of the
+//   groups' first rows and first tiles that wave 0 builds in LDS once.
+// * Persistent grid of P workgroups, two per compute unit: workgroup j walks
 //   tiles j, j + P, j + 2P, ...; workgroups are renumbered so that
 //   consecutive j run on one XCD (one L2), and tiles that read the same
 //   weights at the same time share it.
-// * An eight-slot ring of 128-K stages (A rows, weight rows, the tile's
-//   activation scales and weight block scale: 16.5 KiB) is filled by
+// * A two-slot ring of stages of KS 128-K steps (per step: A rows, weight
+//   rows, the tile's activation scales and weight block scale) is filled by
 //   buffer-load-to-LDS DMA issued from inline assembly with explicit waits.
-//   The ring runs across tile boundaries: seven stages stay in flight from
-//   the first K step of a workgroup's first tile to the last of its last,
-//   so each compute unit keeps about 56 KiB of weights outstanding.
-// * Per stage, four waves (2 x 2, 32 x 32 each) run the scaled matrix-core
-//   instruction with the neutral E8M0 scale into a zeroed accumulator and
-//   add the partial times xs(row, kb) * ws(g, n/128, kb) in FP32.  A tile's
-//   result is stored as BF16 straight from the accumulators.
+//   The ring runs across tile boundaries, so a workgroup's stream never
+//   drains between its tiles; the second workgroup on the compute unit
+//   covers this one's wait-barrier-compute chain.
+// * Per K step, four waves (2 x 2, (BM/2) x 32 each) run the scaled
+//   matrix-core instruction with the neutral E8M0 scale into a zeroed
+//   accumulator and add the partial times xs(row, kb) * ws(g, n/128, kb) in
+//   FP32.  A tile's result is stored as BF16 straight from the accumulators.
 // * 8-row blocks of A past the tile's group read nothing (empty range).
-// Tile BM x 64 (BM = 64 or 128), four waves in a 2 x 2 grid of
-// (BM/2) x 32 each.
 template <int BM_>
 struct GroupedStream {
   static constexpr int BM = BM_, BN = 64;

@@ -128,8 +128,9 @@ def test_grouped_precondition_violation_is_contained():
 
 @pytest.mark.parametrize("preshuffled", [False, True])
 def test_grouped_long_k(preshuffled):
-    """K = 2304 (18 steps of 128): the skinny kernel's eight-slot DMA ring
-    wraps twice, and its stages past the last K step read nothing."""
+    """K = 2304 (18 steps of 128): the persistent kernel's DMA ring wraps
+    many times within a tile and across tiles, and its stages past the last
+    K step read nothing."""
     N, K = 384, 2304
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(911, [90, 7, 0, 160, 33], N, K)
     D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
