@@ -396,11 +396,16 @@ def cpu_baseline(synth, target_s=12.0):
         t0 = time.perf_counter()
         oracle.gemm((oracle.E4M3, oracle.SCALE_MX, 0, qa, sa), opB, rows, N, K)
         return time.perf_counter() - t0
-    probe_rows = 16
+    # size the sample from a probe, and once more from the first sample if
+    # the probe (thread start-up included) misjudged it by more than 2x
+    probe_rows = 128
     tp = run(probe_rows)
     rows = int(max(probe_rows, min(16384, probe_rows * target_s / max(tp, 1e-3))))
     rows = max(16, rows // 16 * 16)
     dt = run(rows)
+    if dt < 0.5 * target_s and rows < 16384:
+        rows = max(16, int(min(16384, rows * target_s / max(dt, 1e-3))) // 16 * 16)
+        dt = run(rows)
     flops = 2.0 * rows * N * K
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
