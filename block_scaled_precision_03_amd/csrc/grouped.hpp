@@ -296,14 +296,9 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   const u32x4 rx = rsrc4(p.xs, clamp_records(p.totM * kb_n * 4));
   const u32x4 rw = rsrc4(p.ws, clamp_records((int64_t)p.G * (N / 128) * kb_n * 4));
   const u32x4 rzero = rsrc4(p.xs, 0);
-  // lane offsets of the row-tile DMAs (8 rows x 128 B per DMA; row r keeps
-  // 16-byte piece c at position c ^ (r%8) ^ ((r/8)%2))
-  uint32_t vo[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int r8 = lane >> 3;
-    vo[par] = (uint32_t)(r8 * K) + (uint32_t)(((lane & 7) ^ r8 ^ par) << 4);
-  }
+  // lane offset of the row-tile DMAs (8 rows x 128 B per DMA; row r keeps
+  // 16-byte piece c at position c ^ kswz(r))
+  const uint32_t vo = (uint32_t)((lane >> 3) * K) + (uint32_t)(((lane & 7) ^ kswz(lane >> 3)) << 4);
   const uint32_t lds0 = lds_addr(smem);
 
   // Issue side: the tile whose stages are being issued.
@@ -348,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
         constexpr int jj = decltype(jc)::value;
         const int blk = ABLK * w + jj;
         const u32x4 r = (live && blk * 8 < src.vrows) ? src.ra : rzero;
-        dma_asm_v<16>(ka + (uint32_t)blk * 1024u, r, vo[jj & 1], (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
+        dma_asm_v<16>(ka + (uint32_t)blk * 1024u, r, vo, (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
       });
       const u32x4 rb = live ? src.rb : rzero;
       static_for<0, 2>([&](auto jc) {
@@ -358,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
           dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, (uint32_t)lane * 16u,
                       (uint32_t)(st * 8192 + blk * 1024));
         else
-          dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, vo[jj],
+          dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, vo,
                       (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
       });
       // activation scales of rows 64h .. 64h + 63 by wave 2h
@@ -389,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // fragment lane offsets
-  const int f = (i16 & 7) ^ (i16 >> 3);
+  const int f = kswz(i16);
   const uint32_t oa0 = (uint32_t)((wm * (BM / 2) + i16) * 128 + ((q ^ f) << 4));
   const uint32_t oa1 = (uint32_t)((wm * (BM / 2) + i16) * 128 + (((q + 4) ^ f) << 4));
   const uint32_t ob0 = PSB ? (uint32_t)(wn * 2 * 2048 + lane * 16)
