@@ -134,12 +134,19 @@ typedef void (*dense_fn)(DenseArgs);
 
 template <int FA, int FB>
 dense_fn pick_layout(bool mx, int layout, bool psb) {
-  if (mx) {
-    if (layout != MXG_NT) return nullptr;
-    return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
-  }
   if constexpr (FA == F_E2M1 || FB == F_E2M1) {
-    return nullptr;
+    if (!mx || layout != MXG_NT) return nullptr;
+    return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
+  } else if (mx) {
+    // MX scales are blocked along K whatever the code layout, so the
+    // transposed variants load them exactly as NT does.
+    switch (layout) {
+      case MXG_NT:
+        return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
+      case MXG_NN: return dense_kernel<FA, FB, SM_MX, false, true, false>;
+      case MXG_TN: return dense_kernel<FA, FB, SM_MX, true, true, false>;
+      default: return nullptr;
+    }
   } else {
     switch (layout) {
       case MXG_NT:

@@ -191,3 +191,49 @@ def test_degenerate_sizes():
     with pytest.raises(mxgemm.MxgemmError):
         mxgemm.run(E4, E4, NT, a, s, a, s, D, 64, 40, 100)    # K % 128 != 0
     assert torch.all(D == 0)
+
+
+# MXFP8 backward layouts: the data gradient (NN: B stored [K, N]) and weight
+# gradient (TN: A stored [K, M], B stored [K, N]) of a linear layer, with the
+# E8M0 scales blocked along K whatever the code layout.
+MX_T_CASES = [(NN, False, True), (TN, True, True)]
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4), (E4, E5)])
+@pytest.mark.parametrize("layout,ta,tb", MX_T_CASES)
+@pytest.mark.parametrize("M,N,K", [(272, 400, 384), (96, 48, 640), (528, 512, 1024)])
+def test_mxfp8_backward_layouts(fa, fb, layout, ta, tb, M, N, K):
+    x = synth.normal(600 + M + layout, (M, K))
+    w = synth.normal(601 + N + layout, (N, K), 0.02)
+    opA = H.make_operand(fa, x, ta)
+    opB = H.make_operand(fb, w, tb)
+    _check(layout, opA, opB, M, N, K, "mx fmt %d/%d layout %d %dx%dx%d" % (fa, fb, layout, M, N, K))
+
+
+def test_mxfp8_layout_equivalence_bit_exact():
+    """MX operands stored three ways (same codes, same K-blocked scales) give
+    identical bits: the transposing fragment reads feed the matrix cores in
+    the same K order as the row reads, so each E8M0 scale meets its block."""
+    M, N, K = 272, 400, 1024
+    x = synth.normal(21, (M, K))
+    w = synth.normal(22, (N, K), 0.02)
+    outs = []
+    for layout, ta, tb in LAYOUT_CASES:
+        opA = H.make_operand(E4, x, ta)
+        opB = H.make_operand(E5, w, tb)
+        outs.append(H.bits(H.run_dense(layout, opA, opB, M, N, K)))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("layout,ta,tb", MX_T_CASES)
+def test_integer_valued_bit_exact_mx_backward(layout, ta, tb):
+    """Integer-valued codes with E8M0 scales 2^0..2^2 in random blocks: every
+    partial sum is exact in FP32, so D equals the rounded exact result bit
+    for bit, which pins each scale to its 32-K block and row."""
+    rng = np.random.default_rng(91 + layout)
+    M, N, K = 400, 272, 1152
+    opA = _int_operand(rng, E4, M, K, ta)
+    opB = _int_operand(rng, E5, N, K, tb)
+    D = H.run_dense(layout, opA, opB, M, N, K)
+    ref = oracle.gemm(opA.orc(), opB.orc(), M, N, K)
+    assert np.array_equal(H.bits(D), oracle.bf16_rne(ref))

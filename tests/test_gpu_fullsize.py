@@ -73,6 +73,25 @@ def test_tensorwise_linear_layer(name, layout, M, N, K, fa, fb):
     _check_sampled(D, opA, opB, M, N, K, "tensor-wise %s (%d, %d)" % (name, fa, fb))
 
 
+# MXFP8 data and weight gradients of the same linear layer (dY in E5M2, the
+# weight and the activations in E4M3, E8M0 per 32 K values along each GEMM's
+# K): dgrad NN 8192 x 4096 x 11008 and wgrad TN 11008 x 4096 x 8192.
+MX_BWD = [("dgrad", NN, 8192, 4096, 11008), ("wgrad", TN, 11008, 4096, 8192)]
+
+
+@pytest.mark.parametrize("name,layout,M,N,K", MX_BWD)
+def test_mxfp8_backward_full_size(name, layout, M, N, K):
+    idx = 1 if name == "dgrad" else 2
+    a = synth.normal(synth.seed_for(6, 1, idx), (M, K))
+    b = synth.normal(synth.seed_for(6, 2, idx), (N, K), 0.02 if name == "dgrad" else 1.0)
+    opA = H.make_operand(E5, a, layout == TN)
+    opB = H.make_operand(E4, b, True)
+    del a, b
+    D = H.run_dense(layout, opA, opB, M, N, K, d_fill=float("nan"))
+    _check_sampled(D, opA, opB, M, N, K, "mxfp8 %s" % name)
+    assert np.isfinite(H.bf16_to_f64(D)).all(), "unwritten or non-finite outputs in %s" % name
+
+
 def test_mxfp4_8192_cube():
     M = N = K = 8192
     x = synth.normal(synth.seed_for(5, 1), (M, K))

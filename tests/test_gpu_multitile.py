@@ -106,3 +106,14 @@ def test_every_output_written_repeatedly(fa, fb, M, N, K):
         if first is None:
             first = b
         assert np.array_equal(first, b), "call %d differs from call 0" % rep
+
+
+@pytest.mark.parametrize("layout,ta,tb", [(NN, False, True), (TN, True, True)])
+@pytest.mark.parametrize("K", [384, 512])
+def test_mxfp8_backward_layouts_multitile(layout, ta, tb, K):
+    M, N = 4352, 4112
+    x = synth.normal(7051 + K, (M, K))
+    w = synth.normal(7052 + K, (N, K), 0.02)
+    opA = H.make_operand(E5, x, ta)
+    opB = H.make_operand(E4, w, tb)
+    _sampled(layout, opA, opB, M, N, K, "mx layout %d K=%d" % (layout, K))
