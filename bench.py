@@ -9,8 +9,9 @@ seeded synthetic data resident in HBM before the timed region.
 Also measured (reported beside the headline, not part of `value`): the
 grouped groupwise FP8 GEMM (G=8) in microseconds per call, tensor-wise FP8
 GEMMs of a 4096 -> 11008 linear layer at 8192 tokens (forward NT, data
-gradient NN, weight gradient TN), the MXFP4 8192^3 GEMM, and the CPU oracle
-on a bounded sample of the MXFP8 workload.
+gradient NN, weight gradient TN), the MXFP8 data and weight gradients of the
+same layer (NN, TN), the MXFP4 8192^3 GEMM, and the CPU oracle on a bounded
+sample of the MXFP8 workload.
 
 `roofline` describes the dominant kernel (the MXFP8 NT kernel with
 preshuffled B): algorithmic FLOPs per launch (2MNK) over its mean launch
@@ -334,6 +335,37 @@ def tensorwise_bench(torch, synth, mxgemm, dev):
     return out
 
 
+def mx_backward_bench(torch, synth, mxgemm, dev):
+    """MXFP8 data and weight gradients of the same 4096 -> 11008 linear layer
+    (E8M0 per 32 values along each GEMM's K): dgrad NN 8192 x 4096 x 11008
+    and wgrad TN 11008 x 4096 x 8192, the gradient dY in E5M2, weights and
+    activations in E4M3."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = []
+    for idx, (name, layout, M, N, K) in enumerate(C3_CASES):
+        if layout == mxgemm.NT:
+            continue
+        a = synth.normal(synth.seed_for(6, 1, idx), (M, K))
+        b = synth.normal(synth.seed_for(6, 2, idx), (N, K), 0.02 if name == "dgrad" else 1.0)
+        qa, sa = synth.quant_mx(a, "e5m2")
+        qb, sb = synth.quant_mx(b, "e4m3")
+        if layout == mxgemm.TN:
+            qa = qa.T
+        qb = qb.T
+        A, SA, B, SB = t(qa), t(sa), t(qb), t(sb)
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = time_calls(torch, lambda: mxgemm.run(mxgemm.MXFP8_E5M2, mxgemm.MXFP8_E4M3, layout, A, SA, B, SB,
+                                                  D, M, N, K))
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "A": "e5m2", "B": "e4m3",
+                    "M": M, "N": N, "K": K, "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP8_TFLOPS})
+        log("mxfp8 %s %s (%d,%d,%d): %.1f us, %.0f TFLOP/s (%.1f%% of MXFP8 peak)" % (
+            name, out[-1]["layout"], M, N, K, us, tf, out[-1]["pct_peak"]))
+        del A, B, D, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def mfma_ceiling(torch, mxgemm, dev):
     """What the scaled matrix-core instruction sustains with nothing else
     running (FP8 and FP4 operands), and the shader clock meanwhile."""
@@ -491,6 +523,8 @@ def main():
     if not args.only_step and not args.no_extra:
         log("tensor-wise FP8 ...")
         result["tensorwise_fp8"] = tensorwise_bench(torch, synth, mxgemm, dev)
+        log("MXFP8 backward layouts ...")
+        result["mxfp8_backward"] = mx_backward_bench(torch, synth, mxgemm, dev)
         log("MXFP4 ...")
         result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
         result["mfma_ceiling"] = mfma_ceiling(torch, mxgemm, dev)

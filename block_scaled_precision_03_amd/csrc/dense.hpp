@@ -370,7 +370,7 @@ struct DenseLoop {
   struct Lanes {
     uint32_t a[2], b[2];           // FP8 K-contiguous / preshuffled: the two 16-byte halves;
                                    // FP4: the two k steps of the stage
-    uint32_t at[4], bt[4];         // transposed: per 8-byte piece t, tile 0
+    uint32_t at, bt;               // transposed: 8-byte piece 0 of tile 0
     uint32_t sa, sb;               // scale words
   };
 
@@ -386,16 +386,20 @@ struct DenseLoop {
       if constexpr (PSB) L.b[h] = ((uint32_t)(B_REG + c.wn * 8192 + (FP4 ? 0 : h * 1024) + c.lane * 16)) & LMASK;
       else L.b[h] = ((uint32_t)(B_REG + (c.wn * 64 + i) * 128 + ((piece ^ f) << 4))) & LMASK;
     }
-    // Transposed tiles (256 B per k-row): piece t of tile 0.  Tile x sits x
-    // 16-byte chunks further; the chunk index is XOR-swizzled by tswz(kk) and
-    // the wave's first chunk (8wm or 4wn) is aligned to the tile count, so
-    // its offset is the tile-0 offset ^ (x << 4).
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kk = 16 * q + 8 * (t & 1) + 64 * (t >> 1) + (i >> 1);
+    // Transposed tiles (256 B per k-row): piece 0 of tile 0.  Piece t sits
+    // in k-row kk + 8 (t & 1) + 64 (t >> 1), whose swizzle tswz is that of kk
+    // (neither step reaches bits 0-2 or bit 4 of kk = 16 q + i / 2), so it is
+    // 0, 2048, 16384 or 18432 bytes further (rdt).  Tile x sits x 16-byte
+    // chunks further; the
+    // chunk index is XOR-swizzled by tswz(kk) and the wave's first chunk (8wm
+    // or 4wn) is aligned to the tile count, so its offset is the tile-0
+    // offset ^ (x << 4), and XOR on bits 4-6 commutes with adding those
+    // distances (multiples of 2048).
+    {
+      const int kk = 16 * q + (i >> 1);
       const int ca = c.wm * 8, cb = c.wn * 4;
-      L.at[t] = ((uint32_t)(kk * 256 + ((ca ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
-      L.bt[t] = ((uint32_t)(B_REG + kk * 256 + ((cb ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
+      L.at = ((uint32_t)(kk * 256 + ((ca ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
+      L.bt = ((uint32_t)(B_REG + kk * 256 + ((cb ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
     }
     L.sa = ((uint32_t)(S_REG + SA_OFF + (c.wm * 128 + i) * 16)) & LMASK;
     if constexpr (PSB) L.sb = ((uint32_t)(S_REG + SB_OFF + c.wn * 1024 + c.lane * 4)) & LMASK;
@@ -408,11 +412,13 @@ struct DenseLoop {
     return (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
   }
 
-  __device__ static inline v8i rdt(const uint8_t *base, const uint32_t (&off)[4]) {
-    v2i p0 = lds_read_tr8(base + off[0]);
-    v2i p1 = lds_read_tr8(base + off[1]);
-    v2i p2 = lds_read_tr8(base + off[2]);
-    v2i p3 = lds_read_tr8(base + off[3]);
+  // The four 8-byte pieces t of a transposed fragment: k-rows 8 (t & 1) +
+  // 64 (t >> 1) after the lane's first, at fixed distances from it.
+  __device__ static inline v8i rdt(const uint8_t *base, uint32_t off) {
+    v2i p0 = lds_read_tr8(base + off);
+    v2i p1 = lds_read_tr8(base + off + 2048);
+    v2i p2 = lds_read_tr8(base + off + 16384);
+    v2i p3 = lds_read_tr8(base + off + 18432);
     return (v8i){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   }
 
@@ -504,9 +510,7 @@ struct DenseLoop {
     auto read_a = [&](int s, int a) -> v8i {
       if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
       else if constexpr (TA) {
-        const uint32_t x = (uint32_t)a << 4;
-        const uint32_t o[4] = {L.at[0] ^ x, L.at[1] ^ x, L.at[2] ^ x, L.at[3] ^ x};
-        return rdt(la, o);
+        return rdt(la, L.at ^ ((uint32_t)a << 4));
       } else return rd8(la, L.a[0], L.a[1], a * 2048);
     };
     auto read_b = [&](int s, int b) -> v8i {
@@ -516,9 +520,7 @@ struct DenseLoop {
       } else if constexpr (FP4) {
         return widen(lds_read16(lb + L.b[s] + b * 2048));
       } else if constexpr (TB) {
-        const uint32_t x = (uint32_t)b << 4;
-        const uint32_t o[4] = {L.bt[0] ^ x, L.bt[1] ^ x, L.bt[2] ^ x, L.bt[3] ^ x};
-        return rdt(lb, o);
+        return rdt(lb, L.bt ^ ((uint32_t)b << 4));
       } else return rd8(lb, L.b[0], L.b[1], b * 2048);
     };
 #pragma unroll
@@ -540,21 +542,33 @@ struct DenseLoop {
           }
         }
       }
-      // All A scale words of the step up front: read beside the matrix-core
-      // tile that needs them, each would stall its tile on an LDS round trip.
-      uint32_t saw[FM];
+      // A scale words: with K-contiguous operands all of the step's up front
+      // (read beside the matrix-core tile that needs them, each would stall
+      // its tile on an LDS round trip); with a transposed operand, whose
+      // fragment addressing needs more registers, one tile ahead with the A
+      // fragment, so that two words are live instead of eight.
+      constexpr bool SA_AHEAD = TA || TB;
+      auto scale_word = [&](int a) -> uint32_t {
+        return MX ? lds_u32(ls + L.sa + a * 256 + ((st * KS + s) & 3) * 4) : 0u;
+      };
+      uint32_t saw[SA_AHEAD ? 1 : FM];
+      if constexpr (SA_AHEAD) {
+        saw[0] = scale_word(0);
+      } else {
 #pragma unroll
-      for (int a = 0; a < FM; ++a) {
-        saw[a] = 0;
-        if constexpr (MX) saw[a] = lds_u32(ls + L.sa + a * 256 + ((st * KS + s) & 3) * 4);
+        for (int a = 0; a < FM; ++a) saw[a] = scale_word(a);
       }
       v8i af = read_a(s, 0);
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         v8i af_next;
-        if (a + 1 < FM) af_next = read_a(s, a + 1);
+        uint32_t sw_next = 0;
+        if (a + 1 < FM) {
+          af_next = read_a(s, a + 1);
+          if constexpr (SA_AHEAD) sw_next = scale_word(a + 1);
+        }
         int sa = E8M0_ONE_X4;
-        if constexpr (MX) sa = (int)(saw[a] >> (8 * c.q));
+        if constexpr (MX) sa = (int)((SA_AHEAD ? saw[0] : saw[a]) >> (8 * c.q));
         if (EPI && s == 0) {
           if (e.on) store_rows(c, e, a, acc[a]);
 #pragma unroll
@@ -566,7 +580,10 @@ struct DenseLoop {
             // First operand = B tile: the result lane holds 4 consecutive n.
             acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb[b], sa);
         }
-        if (a + 1 < FM) af = af_next;
+        if (a + 1 < FM) {
+          af = af_next;
+          if constexpr (SA_AHEAD) saw[0] = sw_next;
+        }
         // keep the A reads one tile ahead, not hoisted further (registers)
         __builtin_amdgcn_sched_barrier(0);
       }
