@@ -45,6 +45,12 @@ def lib():
         L.oracle_grouped_gemm.argtypes = [i, p, p, p, p, p, i64, i64, i64, p]
         L.oracle_grouped_entries.restype = i
         L.oracle_grouped_entries.argtypes = [i, p, p, p, p, p, i64, i64, i64, p, p, i64, p]
+        L.oracle_nearest_code.restype = ctypes.c_uint
+        L.oracle_nearest_code.argtypes = [i, d]
+        L.oracle_quant_mx.restype = i
+        L.oracle_quant_mx.argtypes = [i, p, i64, i64, p, p]
+        L.oracle_quant_group_act.restype = i
+        L.oracle_quant_group_act.argtypes = [i, p, p, i64, i64, p, p]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_bf16_rne.argtypes = [d]
         L.oracle_bf16_rne_array.restype = None
@@ -189,3 +195,36 @@ def within_tolerance(d, ref):
                          np.where(err > 0, np.inf, 0.0))
     worst = float(np.max(ratio)) if ratio.size else 0.0
     return ok, worst
+
+
+def nearest_code(fmt, v):
+    """The code of the representable value nearest to v (ties to the even
+    code, saturating at +-fmt_max, sign kept)."""
+    return int(lib().oracle_nearest_code(fmt, float(v)))
+
+
+def quant_mx(fmt, x):
+    """FP32 [rows, K] -> (codes, E8M0 scales [rows, K/32]); codes [rows, K]
+    bytes, or [rows, K/2] packed nibbles for E2M1.  Exact E8M0 exponent
+    floor(log2(amax / fmt_max)), nearest-value element rounding."""
+    x = _c(x, np.float32)
+    rows, K = x.shape
+    codes = np.zeros((rows, K // 2 if fmt == E2M1 else K), np.uint8)
+    scales = np.zeros((rows, K // 32), np.uint8)
+    if lib().oracle_quant_mx(fmt, _ptr(x), rows, K, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("oracle_quant_mx: unsupported format or K")
+    return codes, scales
+
+
+def quant_group_act(m_sizes, x, codes_fill=0, xs_fill=np.nan):
+    """Groupwise E4M3 activations: FP32 [totM, K] -> (codes [totM, K], FP32
+    scales in the per-group block layout, totM*K/128).  Rows in no group keep
+    the fill values."""
+    x = _c(x, np.float32)
+    totM, K = x.shape
+    ms = _c(np.asarray(m_sizes), np.int64)
+    codes = np.full((totM, K), codes_fill, np.uint8)
+    xs = np.full(totM * (K // 128), xs_fill, np.float32)
+    if lib().oracle_quant_group_act(len(ms), _ptr(ms), _ptr(x), totM, K, _ptr(codes), _ptr(xs)) != 0:
+        raise ValueError("oracle_quant_group_act: K % 128 != 0")
+    return codes, xs

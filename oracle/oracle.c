@@ -329,3 +329,136 @@ void oracle_bf16_rne_array(const double *x, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(x[i]);
 }
+
+/* ---- quantizers: FP32 data -> codes + scales (the step before the GEMM) --
+ *
+ * "PyTorch on AMD GPUs gains a FlyDSL backend" (Interpretation): MX operands
+ * carry one E8M0 power-of-two scale per 32 values along K.  "Add FlyDSL
+ * grouped groupwise FP8 GEMM for ROCm" (PR body; commit messages): E4M3
+ * activations with one FP32 scale per row and 128-value K block, stored in
+ * the per-group block layout.  The pages give formats and granularities;
+ * the scale rules are this project's readings:
+ *   MX:        X = floor(log2(amax / fmt_max)) exactly (X = -127 for an
+ *              all-zero block), clamped to [-127, 127]; scale code X + 127;
+ *              element code = nearest(x / 2^X).
+ *   groupwise: s = amax / 448 as an FP32 quotient (1.0 for an all-zero
+ *              block); element code = nearest(FP32 quotient x / s).
+ * nearest(v) is the format's representable value closest to v, ties to the
+ * even code (mantissa LSB 0), saturating at +-fmt_max; the sign of v is kept
+ * (a negative value that rounds to zero gives the negative-zero code).
+ */
+
+/* Largest positive finite code of each format; the positive codes 0..max
+ * decode to strictly increasing values. */
+static unsigned orc_max_code(int fmt)
+{
+    return fmt == ORC_E4M3 ? 0x7Eu : (fmt == ORC_E5M2 ? 0x7Bu : 0x7u);
+}
+
+static unsigned orc_nearest(int fmt, double v)
+{
+    const unsigned top = orc_max_code(fmt);
+    const unsigned neg = signbit(v) ? 1u : 0u;
+    const double a = fabs(v);
+    unsigned c;
+    if (a >= oracle_decode(fmt, top)) {
+        c = top;
+    } else {
+        /* dec(lo) <= a < dec(hi), by bisection over the ordered codes */
+        unsigned lo = 0u, hi = top;
+        while (hi - lo > 1u) {
+            const unsigned mid = (lo + hi) / 2u;
+            if (oracle_decode(fmt, mid) <= a) lo = mid; else hi = mid;
+        }
+        const double dl = a - oracle_decode(fmt, lo), dh = oracle_decode(fmt, hi) - a;
+        c = dl < dh ? lo : (dh < dl ? hi : ((lo & 1u) ? hi : lo));
+    }
+    if (neg) c |= (fmt == ORC_E2M1) ? 0x8u : 0x80u;
+    return c;
+}
+
+unsigned oracle_nearest_code(int fmt, double v) { return orc_nearest(fmt, v); }
+
+static double orc_fmt_max(int fmt)
+{
+    return oracle_decode(fmt, orc_max_code(fmt));
+}
+
+/* X = floor(log2(amax / fmt_max)), by exact comparisons in FP64. */
+static int orc_e8m0_exponent(double amax, double fmt_max)
+{
+    if (!(amax > 0.0)) return -127;
+    int X = ilogb(amax) - ilogb(fmt_max);
+    while (ldexp(fmt_max, X) > amax) --X;
+    while (ldexp(fmt_max, X + 1) <= amax) ++X;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    return X;
+}
+
+/* x: FP32 [rows, K] row-major, K % 32 == 0.  codes: [rows, K] bytes (E4M3,
+ * E5M2) or [rows, K/2] (E2M1, element 2j in the low nibble); scales: E8M0
+ * [rows, K/32]. */
+int oracle_quant_mx(int fmt, const float *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales)
+{
+    if (K % 32 != 0 || (fmt != ORC_E4M3 && fmt != ORC_E5M2 && fmt != ORC_E2M1)) return -1;
+    const double fmax = orc_fmt_max(fmt);
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const float *blk = x + r * K + 32 * b;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) if (fabs((double)blk[j]) > amax) amax = fabs((double)blk[j]);
+            const int X = orc_e8m0_exponent(amax, fmax);
+            scales[r * (K / 32) + b] = (uint8_t)(X + 127);
+            for (int j = 0; j < 32; ++j) {
+                const unsigned c = orc_nearest(fmt, ldexp((double)blk[j], -X));
+                const int64_t k = 32 * b + j;
+                if (fmt == ORC_E2M1) {
+                    uint8_t *p = codes + r * (K / 2) + k / 2;
+                    if (k % 2 == 0) *p = (uint8_t)((*p & 0xF0u) | c);
+                    else *p = (uint8_t)((*p & 0x0Fu) | (c << 4));
+                } else {
+                    codes[r * K + k] = (uint8_t)c;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Groupwise E4M3 activations: x FP32 [totM, K], K % 128 == 0; group g owns
+ * rows [start_g, start_g + m_sizes[g]).  codes: [totM, K]; xs: FP32 scale of
+ * (row r of group g, k block kb) at start_g*(K/128) + (r - start_g) +
+ * kb*m_sizes[g] ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", commit
+ * fixing the activation-scale addressing).  Rows in no group are not
+ * written. */
+int oracle_quant_group_act(int G, const int64_t *m_sizes, const float *x, int64_t totM, int64_t K,
+                           uint8_t *codes, float *xs)
+{
+    if (K % 128 != 0) return -1;
+    const int64_t nkb = K / 128;
+    int64_t start = 0;
+    for (int g = 0; g < G; ++g) {
+        int64_t mg = m_sizes[g] < 0 ? 0 : m_sizes[g];
+        if (mg > totM - start) mg = totM - start;
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < mg; ++i) {
+            const int64_t r = start + i;
+            for (int64_t kb = 0; kb < nkb; ++kb) {
+                const float *blk = x + r * K + 128 * kb;
+                float amax = 0.0f;
+                for (int j = 0; j < 128; ++j) if (fabsf(blk[j]) > amax) amax = fabsf(blk[j]);
+                volatile float s = amax / 448.0f;          /* FP32 quotient */
+                const float sc = amax > 0.0f ? s : 1.0f;
+                xs[start * nkb + i + kb * mg] = sc;
+                for (int j = 0; j < 128; ++j) {
+                    volatile float q = blk[j] / sc;         /* FP32 quotient */
+                    codes[r * K + 128 * kb + j] = (uint8_t)orc_nearest(ORC_E4M3, (double)q);
+                }
+            }
+        }
+        start += mg;
+    }
+    return 0;
+}
