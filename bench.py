@@ -10,8 +10,8 @@ Also measured (reported beside the headline, not part of `value`): the
 grouped groupwise FP8 GEMM (G=8) in microseconds per call, tensor-wise FP8
 GEMMs of a 4096 -> 11008 linear layer at 8192 tokens (forward NT, data
 gradient NN, weight gradient TN), the MXFP8 data and weight gradients of the
-same layer (NN, TN), the MXFP4 8192^3 GEMM, and the CPU oracle on a bounded
-sample of the MXFP8 workload.
+same layer (NN, TN), the on-device quantizers (GB/s), the MXFP4 8192^3 GEMM,
+and the CPU oracle on a bounded sample of the MXFP8 workload.
 
 `roofline` describes the dominant kernel (the MXFP8 NT kernel with
 preshuffled B): algorithmic FLOPs per launch (2MNK) over its mean launch
@@ -366,6 +366,37 @@ def mx_backward_bench(torch, synth, mxgemm, dev):
     return out
 
 
+def quant_bench(torch, synth, mxgemm, dev):
+    """The on-device quantizers at the workloads' activation shapes: MX E4M3
+    of the [16384, 4096] activation (E8M0 per 32) and groupwise E4M3 of the
+    grouped GEMM's [16384, 7168] activation (G = 8, per-group block scales).
+    HBM-bound: algorithmic bytes = 4 per value read + 1 per code + scales."""
+    out = []
+    x = torch.from_numpy(synth.normal(synth.seed_for(2, 1, 0), (16384, 4096))).to(dev)
+    codes = torch.empty((16384, 4096), dtype=torch.uint8, device=dev)
+    scales = torch.empty((16384, 128), dtype=torch.uint8, device=dev)
+    us = time_calls(torch, lambda: mxgemm.quantize_mx(mxgemm.MXFP8_E4M3, x, codes, scales, 16384, 4096))
+    nbytes = 16384 * 4096 * 5 + 16384 * 128
+    out.append({"name": "quantize_mx e4m3", "rows": 16384, "K": 4096, "us": us, "bytes": nbytes,
+                "gbs": nbytes / us / 1e3, "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
+    del x, codes, scales
+    totM, K = 16384, 7168
+    ms = torch.from_numpy(synth.m_sizes_for(totM, 8, synth.seed_for(4, 4, 2))).to(dev)
+    x = torch.from_numpy(synth.normal(synth.seed_for(4, 1, 2), (totM, K))).to(dev)
+    codes = torch.empty((totM, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((totM * K // 128,), dtype=torch.float32, device=dev)
+    us = time_calls(torch, lambda: mxgemm.grouped_quantize_act(8, ms, x, codes, xs, totM, K))
+    nbytes = totM * K * 5 + totM * K // 128 * 4 + 8 * 8
+    out.append({"name": "grouped_quantize_act e4m3 G=8", "rows": totM, "K": K, "us": us, "bytes": nbytes,
+                "gbs": nbytes / us / 1e3, "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
+    for r in out:
+        log("%s [%d, %d]: %.1f us, %.0f GB/s (%.1f%% of HBM)" % (r["name"], r["rows"], r["K"], r["us"], r["gbs"],
+                                                                r["pct_hbm"]))
+    del x, codes, xs
+    torch.cuda.empty_cache()
+    return out
+
+
 def mfma_ceiling(torch, mxgemm, dev):
     """What the scaled matrix-core instruction sustains with nothing else
     running (FP8 and FP4 operands), and the shader clock meanwhile."""
@@ -525,6 +556,8 @@ def main():
         result["tensorwise_fp8"] = tensorwise_bench(torch, synth, mxgemm, dev)
         log("MXFP8 backward layouts ...")
         result["mxfp8_backward"] = mx_backward_bench(torch, synth, mxgemm, dev)
+        log("quantizers ...")
+        result["quantizers"] = quant_bench(torch, synth, mxgemm, dev)
         log("MXFP4 ...")
         result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
         result["mfma_ceiling"] = mfma_ceiling(torch, mxgemm, dev)

@@ -12,6 +12,7 @@
 #include "dense.hpp"
 #include "grouped.hpp"
 #include "preshuffle.hpp"
+#include "quant.hpp"
 #include "diag.hpp"
 
 using namespace mxg;
@@ -400,5 +401,46 @@ extern "C" int mxgemm_mfma_ceiling(int fmt, int64_t iters, void *clk, hipStream_
     hipLaunchKernelGGL((mfma_ceiling_kernel<F_E2M1>), dim3(grid), dim3(512), 0, stream, iters, (uint64_t *)clk);
   else
     hipLaunchKernelGGL((mfma_ceiling_kernel<F_E4M3>), dim3(grid), dim3(512), 0, stream, iters, (uint64_t *)clk);
+  return launch_status();
+}
+
+extern "C" int mxgemm_quantize_mx(int fmt, const float *x, void *codes, void *scales, int64_t rows, int64_t K,
+                                  hipStream_t stream) {
+  const FmtInfo f = fmt_info(fmt);
+  if (!f.ok || !f.mx || rows < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MXG_ERR_UNSUPPORTED;
+  if (rows == 0 || K == 0) return MXG_OK;
+  if (!x || !codes || !scales) return MXG_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return MXG_ERR_MISALIGNED;
+  const int64_t n8 = rows * K / 8;
+  const int64_t blocks = cdiv(n8, 256);
+  if (rows >= MAX_DIM || K > MAX_ROW_BYTES || blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  const float *xf = x;
+  uint8_t *c = (uint8_t *)codes, *s = (uint8_t *)scales;
+  if (f.elem == F_E4M3)
+    hipLaunchKernelGGL((quant_mx_kernel<F_E4M3>), dim3((unsigned)blocks), dim3(256), 0, stream, xf, c, s, n8);
+  else if (f.elem == F_E5M2)
+    hipLaunchKernelGGL((quant_mx_kernel<F_E5M2>), dim3((unsigned)blocks), dim3(256), 0, stream, xf, c, s, n8);
+  else
+    hipLaunchKernelGGL((quant_mx_kernel<F_E2M1>), dim3((unsigned)blocks), dim3(256), 0, stream, xf, c, s, n8);
+  return launch_status();
+}
+
+static_assert(QG_MAX == MXG_GROUPED_MAX_G, "group table of the activation quantizer");
+
+extern "C" int grouped_fp8_quantize_act(int G, const int64_t *m_sizes, const float *x, void *codes,
+                                        float *x_scale, int64_t totM, int64_t K, hipStream_t stream) {
+  if (G < 1 || G > MXG_GROUPED_MAX_G) return MXG_ERR_UNSUPPORTED;
+  if (totM < 0 || K < 0 || !m_sizes) return MXG_ERR_INVALID_ARG;
+  if (K % 128 != 0) return MXG_ERR_UNSUPPORTED;
+  if (totM >= MAX_DIM || K > MAX_ROW_BYTES || totM * (K / 128) * 4 >= (1ll << 31)) return MXG_ERR_UNSUPPORTED;
+  if (totM == 0 || K == 0) return MXG_OK;
+  if (!x || !codes || !x_scale) return MXG_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(x_scale, 4) || !aligned(m_sizes, 8))
+    return MXG_ERR_MISALIGNED;
+  const int64_t nblk = totM * (K / 128);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(nblk, 16), 8ll * cu_count());
+  hipLaunchKernelGGL(quant_group_act_kernel, dim3(grid), dim3(256), 0, stream, m_sizes, G, x,
+                     (uint8_t *)codes, x_scale, totM, K);
   return launch_status();
 }

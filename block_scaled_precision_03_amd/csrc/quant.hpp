@@ -1,0 +1,186 @@
+// On-device quantizers: FP32 data -> element codes + block scales, the step
+// that feeds the GEMM operands.
+//
+// MX ("PyTorch on AMD GPUs gains a FlyDSL backend", Interpretation): one E8M0
+// power-of-two scale per 32 consecutive values along K.  The exponent is
+// X = floor(log2(amax / fmt_max)) taken exactly (X = -127 for an all-zero
+// block, clamped to [-127, 127]); elements are x * 2^-X (exact in FP32)
+// rounded to the nearest code, ties to the even code, saturating at
+// +-fmt_max.
+//
+// Groupwise ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", PR body and
+// commit messages): E4M3 with one FP32 scale per row and 128-value K block,
+// s = amax / 448 (an FP32 quotient, 1.0 for an all-zero block), elements the
+// FP32 quotient x / s rounded to the nearest E4M3 code; the scales are
+// written in the per-group block layout the grouped GEMM reads: (row r of
+// group g, k block kb) at start_g * (K/128) + (r - start_g) + kb * M_g.
+//
+// Both are HBM-bound streams: 4 bytes read per element, 1 (FP8) or 1/2
+// (FP4) written, plus the scales.
+#pragma once
+#include "common.hpp"
+
+namespace mxg {
+
+// Nearest code of y (FP32, finite) in format FMT, ties to the even code,
+// saturating; the sign bit is kept (a negative value that rounds to zero
+// gives the negative-zero code).  The quotient a * 2^(MB - E) of a normal
+// magnitude a with exponent E is exact and lies in [2^MB, 2^(MB+1)); its
+// round-to-nearest-even integer is the mantissa with the implicit bit, and a
+// carry to 2^(MB+1) moves to the next exponent through the plain addition.
+template <int FMT>
+__device__ inline uint32_t encode_nearest(float y) {
+  constexpr int MB = FMT == F_E4M3 ? 3 : (FMT == F_E5M2 ? 2 : 1);         // mantissa bits
+  constexpr int BIAS = FMT == F_E4M3 ? 7 : (FMT == F_E5M2 ? 15 : 1);
+  constexpr uint32_t TOP = FMT == F_E4M3 ? 0x7Eu : (FMT == F_E5M2 ? 0x7Bu : 0x7u);
+  constexpr float FMAX = FMT == F_E4M3 ? 448.0f : (FMT == F_E5M2 ? 57344.0f : 6.0f);
+  constexpr int EMIN = 1 - BIAS;                                            // smallest normal exponent
+  const uint32_t neg = __float_as_uint(y) >> 31;
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a >= FMAX) {
+    c = TOP;
+  } else if (a < ldexpf(1.0f, EMIN)) {
+    // subnormal codes m * 2^(EMIN - MB); m = 2^MB is the smallest normal
+    c = (uint32_t)rintf(ldexpf(a, MB - EMIN));
+  } else {
+    const int E = ilogbf(a);
+    const uint32_t q = (uint32_t)rintf(ldexpf(a, MB - E));
+    c = ((uint32_t)(E + BIAS) << MB) + (q - (1u << MB));
+    if (c > TOP) c = TOP;
+  }
+  return c | (neg << (FMT == F_E2M1 ? 3 : 7));
+}
+
+// X = floor(log2(amax / fmt_max)), exactly: with amax = f 2^e (f in
+// [0.5, 1)) and fmt_max = g 2^h (g in [0.5, 1)), the ratio is (f/g) 2^(e-h)
+// with f/g in (0.5, 2), so X = e - h, less one when f < g.
+template <int FMT>
+__device__ inline int e8m0_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  constexpr float G = FMT == F_E2M1 ? 0.75f : 0.875f;                      // 6 = 0.75 2^3; 448 = 0.875 2^9
+  constexpr int H = FMT == F_E4M3 ? 9 : (FMT == F_E5M2 ? 16 : 3);           // 57344 = 0.875 2^16
+  int e;
+  const float f = frexpf(amax, &e);
+  int X = e - H - (f < G ? 1 : 0);
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+__device__ inline float max4(float a, float b, float c, float d) { return fmaxf(fmaxf(a, b), fmaxf(c, d)); }
+
+// One thread per 8 consecutive values (two 16-byte loads); the four threads
+// of a 32-value block are consecutive lanes and exchange their partial
+// maxima by shuffles.  rows * K % 32 == 0, so a block's four lanes are in or
+// out of range together.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__ x, uint8_t *__restrict__ codes,
+                                                       uint8_t *__restrict__ scales, int64_t n8) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;
+  const float4 u = ((const float4 *)x)[2 * t];
+  const float4 v = ((const float4 *)x)[2 * t + 1];
+  float m = fmaxf(max4(fabsf(u.x), fabsf(u.y), fabsf(u.z), fabsf(u.w)),
+                  max4(fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w)));
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  m = fmaxf(m, __shfl_xor(m, 2, 4));
+  const int X = e8m0_exponent<FMT>(m);
+  const float inv = ldexpf(1.0f, -X);
+  const float y[8] = {u.x * inv, u.y * inv, u.z * inv, u.w * inv, v.x * inv, v.y * inv, v.z * inv, v.w * inv};
+  if constexpr (FMT == F_E2M1) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= encode_nearest<FMT>(y[j]) << (4 * j);
+    ((uint32_t *)codes)[t] = w;
+  } else {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= encode_nearest<FMT>(y[j]) << (8 * j);
+      hi |= encode_nearest<FMT>(y[4 + j]) << (8 * j);
+    }
+    ((uint2 *)codes)[t] = make_uint2(lo, hi);
+  }
+  if ((t & 3) == 0) scales[t >> 2] = (uint8_t)(X + 127);
+}
+
+// Groupwise activations.  Each workgroup first builds the clamped prefix
+// sums of m_sizes in LDS (pre[g] = min(sum of max(m_h, 0) over h < g, totM),
+// g = 0..G, by one wave: each lane sums a run of groups, then a 64-lane
+// inclusive scan); rows at or past pre[G] belong to no group and are not
+// written.  Then it walks 1 x 128 blocks, 16 per pass (16 lanes per block,
+// 8 values each), finding a row's group by binary search over pre.
+constexpr int QG_MAX = 1024;
+
+__global__ __launch_bounds__(256) void quant_group_act_kernel(const int64_t *__restrict__ m_sizes, int G,
+                                                              const float *__restrict__ x,
+                                                              uint8_t *__restrict__ codes, float *__restrict__ xs,
+                                                              int64_t totM, int64_t K) {
+  __shared__ int pre[QG_MAX + 1];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (G + 63) / 64;
+    const int g0 = lane * per;
+    int64_t run = 0;
+    for (int j = 0; j < per; ++j) {
+      const int g = g0 + j;
+      if (g < G) {
+        const int64_t s = m_sizes[g];
+        run += s > 0 ? s : 0;
+      }
+    }
+    // inclusive scan of the lanes' run sums
+    int64_t inc = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t o = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += o;
+    }
+    int64_t acc = inc - run;                    // exclusive prefix at g0
+    for (int j = 0; j < per; ++j) {
+      const int g = g0 + j;
+      if (g <= G) pre[g] = (int)(acc < totM ? acc : totM);
+      if (g < G) {
+        const int64_t s = m_sizes[g];
+        acc += s > 0 ? s : 0;
+      }
+    }
+    if (lane == 63 && g0 + per <= G) pre[G] = (int)(acc < totM ? acc : totM);
+  }
+  __syncthreads();
+  const int covered = pre[G];
+  const int64_t nkb = K / 128;
+  const int64_t nblk = (int64_t)covered * nkb;
+  const int sub = threadIdx.x & 15;
+  for (int64_t b = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); b < nblk; b += (int64_t)gridDim.x * 16) {
+    const int r = (int)(b / nkb);
+    const int64_t kb = b - (int64_t)r * nkb;
+    // group of row r: the last g with pre[g] <= r (pre[g+1] > r then)
+    int lo = 0, hi = G;                          // pre[lo] <= r < pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= r) lo = mid; else hi = mid;
+    }
+    const int start = pre[lo], mg = pre[lo + 1] - pre[lo];
+    const float4 *src = (const float4 *)(x + (int64_t)r * K + 128 * kb + 8 * sub);
+    const float4 u = src[0], v = src[1];
+    float m = fmaxf(max4(fabsf(u.x), fabsf(u.y), fabsf(u.z), fabsf(u.w)),
+                    max4(fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w)));
+    m = fmaxf(m, __shfl_xor(m, 1, 16));
+    m = fmaxf(m, __shfl_xor(m, 2, 16));
+    m = fmaxf(m, __shfl_xor(m, 4, 16));
+    m = fmaxf(m, __shfl_xor(m, 8, 16));
+    const float s = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    const float q[8] = {__fdiv_rn(u.x, s), __fdiv_rn(u.y, s), __fdiv_rn(u.z, s), __fdiv_rn(u.w, s),
+                        __fdiv_rn(v.x, s), __fdiv_rn(v.y, s), __fdiv_rn(v.z, s), __fdiv_rn(v.w, s)};
+    uint32_t lo4 = 0, hi4 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo4 |= encode_nearest<F_E4M3>(q[j]) << (8 * j);
+      hi4 |= encode_nearest<F_E4M3>(q[4 + j]) << (8 * j);
+    }
+    *(uint2 *)(codes + (int64_t)r * K + 128 * kb + 8 * sub) = make_uint2(lo4, hi4);
+    if (sub == 0) xs[(int64_t)start * nkb + (r - start) + kb * mg] = s;
+  }
+}
+
+}  // namespace mxg

@@ -26,6 +26,7 @@ EXPORTS = (
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
+    "mxgemm_quantize_mx", "grouped_fp8_quantize_act",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -60,6 +61,10 @@ _lib.mxgemm_mfma_ceiling.restype = _i
 _lib.mxgemm_mfma_ceiling.argtypes = [_i, _i64, _p, _p]
 _lib.grouped_fp8_preshuffle_b.restype = _i
 _lib.grouped_fp8_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
+_lib.mxgemm_quantize_mx.restype = _i
+_lib.mxgemm_quantize_mx.argtypes = [_i, _p, _p, _p, _i64, _i64, _p]
+_lib.grouped_fp8_quantize_act.restype = _i
+_lib.grouped_fp8_quantize_act.argtypes = [_i, _p, _p, _p, _p, _i64, _i64, _p]
 
 
 class MxgemmError(RuntimeError):
@@ -157,3 +162,15 @@ def mfma_ceiling(fmt, iters, clk, stream=None):
     """Matrix-core throughput probe (see include/mxgemm.h); clk: device
     tensor of three int64."""
     _check(_lib.mxgemm_mfma_ceiling(fmt, iters, _ptr(clk), _stream(stream)), "mxgemm_mfma_ceiling")
+
+
+def quantize_mx(fmt, x, codes, scales, rows, K, stream=None):
+    """FP32 [rows, K] -> MX codes and E8M0 scales (see include/mxgemm.h)."""
+    _check(_lib.mxgemm_quantize_mx(fmt, _ptr(x), _ptr(codes), _ptr(scales), rows, K, _stream(stream)),
+           "mxgemm_quantize_mx")
+
+
+def grouped_quantize_act(G, m_sizes, x, codes, x_scale, totM, K, stream=None):
+    """FP32 activations -> E4M3 codes and per-group block-layout FP32 scales."""
+    _check(_lib.grouped_fp8_quantize_act(G, _ptr(m_sizes), _ptr(x), _ptr(codes), _ptr(x_scale), totM, K,
+                                         _stream(stream)), "grouped_fp8_quantize_act")

@@ -201,6 +201,52 @@ int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out,
                              int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * mxgemm_quantize_mx -- FP32 data -> MX operand (codes + E8M0 scales), the
+ * step that produces mxgemm_run's MX inputs ("PyTorch on AMD GPUs gains a
+ * FlyDSL backend", Interpretation: one E8M0 scale per 32 values along K).
+ *
+ * fmt     MXG_MXFP8_E4M3, MXG_MXFP8_E5M2 or MXG_MXFP4_E2M1.
+ * x       device FP32 [rows, K] row-major (K contiguous), 16-byte aligned.
+ * codes   device out: [rows, K] bytes (FP8) or [rows, K/2] (E2M1, element
+ *         2j in bits 3:0), 16-byte aligned.
+ * scales  device out: E8M0 [rows, K/32] bytes.
+ * Per 32-value block: X = floor(log2(amax / fmt_max)) exactly (fmt_max 448,
+ * 57344 or 6; X = -127 for an all-zero block; clamped to [-127, 127]),
+ * scale code X + 127, element code = nearest representable value of
+ * x * 2^-X, ties to the even code, saturating at +-fmt_max.  Inputs must be
+ * finite.  The caller owns every buffer; nothing is allocated.
+ * Errors (before anything is enqueued): MXG_ERR_INVALID_ARG (not an MX fmt,
+ * negative size, null pointer), MXG_ERR_UNSUPPORTED (K % 32 != 0, sizes
+ * past the 32-bit grid), MXG_ERR_MISALIGNED.  rows or K = 0: no-op.
+ */
+int mxgemm_quantize_mx(int fmt, const float *x, void *codes, void *scales,
+                       int64_t rows, int64_t K, hipStream_t stream);
+
+/*
+ * grouped_fp8_quantize_act -- FP32 activations -> the XQ and x_scale inputs
+ * of grouped_fp8_gemm_run: E4M3 codes with one FP32 scale per row and
+ * 128-value K block ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", PR
+ * body), the scales in the per-group block layout (commit message fixing
+ * the scale_a addressing): (row r of group g, block kb) at
+ * start_g * (K/128) + (r - start_g) + kb * m_sizes[g].
+ *
+ * G, m_sizes   as for grouped_fp8_gemm_run (device int64[G], 8-byte aligned;
+ *              the host does not read it).  Negative sizes count as 0 and
+ *              the groups are cut at totM; rows in no group are not written.
+ * x            device FP32 [totM, K] row-major, 16-byte aligned.
+ * codes        device out: E4M3 [totM, K], 16-byte aligned.
+ * x_scale      device out: FP32, totM * K / 128 entries, 4-byte aligned.
+ * Per block: s = amax / 448 as an FP32 quotient (1.0 for an all-zero
+ * block); element code = nearest E4M3 value of the FP32 quotient x / s,
+ * ties to the even code, saturating at +-448.  Inputs must be finite.
+ * Errors: MXG_ERR_UNSUPPORTED (G outside [1, MXG_GROUPED_MAX_G],
+ * K % 128 != 0, sizes past the 32-bit scale offsets), MXG_ERR_INVALID_ARG,
+ * MXG_ERR_MISALIGNED.  totM or K = 0: no-op.
+ */
+int grouped_fp8_quantize_act(int G, const int64_t *m_sizes, const float *x, void *codes,
+                             float *x_scale, int64_t totM, int64_t K, hipStream_t stream);
+
+/*
  * mxgemm_mfma_ceiling -- a measurement aid, not part of the GEMM path: one
  * workgroup per compute unit, eight waves each running 32 independent chains
  * of the scaled 16x16x128 matrix-core instruction for `iters` iterations

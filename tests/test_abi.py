@@ -105,6 +105,14 @@ def test_ops_reject_bad_args_before_device_use():
     assert lib.mxgemm_preshuffle_b(0, 0, P, P, 256, 100, None) == -2
     assert lib.mxgemm_preshuffle_scales(P, P, 256, 100, None) == -2
     assert lib.grouped_fp8_preshuffle_b(8, P, P, 2000, 128, None) == -2
+    assert lib.mxgemm_quantize_mx(16, P, P, P, 4, 32, None) == -1        # tensor-wise fmt
+    assert lib.mxgemm_quantize_mx(0, P, P, P, 4, 48, None) == -2         # K % 32
+    assert lib.mxgemm_quantize_mx(0, P + 4, P, P, 4, 32, None) == -3     # misaligned x
+    assert lib.mxgemm_quantize_mx(0, P, P, P, 0, 32, None) == 0          # rows = 0: no-op
+    assert lib.grouped_fp8_quantize_act(0, P, P, P, P, 128, 128, None) == -2    # G < 1
+    assert lib.grouped_fp8_quantize_act(8, P, P, P, P, 128, 200, None) == -2    # K % 128
+    assert lib.grouped_fp8_quantize_act(8, 0, P, P, P, 128, 128, None) == -1    # null m_sizes
+    assert lib.grouped_fp8_quantize_act(8, P, P, P, P + 2, 128, 128, None) == -3  # misaligned scales
 
 
 def test_package_has_no_cpu_fallback():

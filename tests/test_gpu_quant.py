@@ -1,0 +1,126 @@
+"""GPU parity of the on-device quantizers against the oracle's, bit for bit
+(codes and scales are integer decisions; both sides take them from the same
+FP32 values: x * 2^-X for MX, the FP32 quotient x / s for groupwise).
+
+Covered: every MX format, shapes from one block to full activation sizes,
+all-zero and tiny blocks, exact midpoints between neighbouring codes (ties
+to the even code), negative values rounding to zero, saturation; groupwise
+activations with uneven and empty groups, G = 1 and G = 1024, rows in no
+group left untouched, and the full grouped workload shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_precision_03_amd import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+E4, E5, F4 = 0, 1, 4
+ORC = {E4: oracle.E4M3, E5: oracle.E5M2, F4: oracle.E2M1}
+FMAX = {E4: 448.0, E5: 57344.0, F4: 6.0}
+
+
+def _special_blocks(fmt, x):
+    """Overwrite the first blocks of x with edge cases (x has >= 4 rows of
+    K >= 256)."""
+    of = ORC[fmt]
+    top = {E4: 0x7E, E5: 0x7B, F4: 0x7}[fmt]
+    vals = oracle.decode(of, np.arange(top + 1, dtype=np.uint8)).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    x[0, :32] = 0.0                                               # all-zero block
+    x[0, 32:64] *= np.float32(1e-30)                              # tiny block
+    for blk, X in ((2, 0), (3, -3), (4, 5)):                      # ties at three exponents
+        b = np.resize(mids, 31) * 2.0 ** X
+        x[1, 32 * blk:32 * blk + 32] = np.concatenate([[FMAX[fmt] * 2.0 ** X], b]).astype(np.float32)
+        x[2, 32 * blk:32 * blk + 32] = -x[1, 32 * blk:32 * blk + 32]
+    x[3, :32] = np.float32(FMAX[fmt])                             # saturated block
+    x[3, 32:64] = np.float32(-1e-6)
+    x[3, 32] = np.float32(FMAX[fmt])                              # negatives that round to -0
+    return x
+
+
+@pytest.mark.parametrize("fmt", [E4, E5, F4])
+@pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (4, 256), (256, 4096), (1000, 1024)])
+def test_quantize_mx_bit_exact(fmt, rows, K):
+    x = synth.normal(900 + rows + fmt, (rows, K))
+    if rows >= 4 and K >= 256:
+        x = _special_blocks(fmt, x)
+    want_c, want_s = oracle.quant_mx(ORC[fmt], x)
+    X = H.dev(x)
+    codes = torch.full(want_c.shape, 0xAB, dtype=torch.uint8, device=H.DEV)
+    scales = torch.full(want_s.shape, 0xCD, dtype=torch.uint8, device=H.DEV)
+    from block_scaled_precision_03_amd import mxgemm
+    mxgemm.quantize_mx(fmt, X, codes, scales, rows, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+
+
+def test_quantize_mx_full_size_activation():
+    """The MXFP8 activation of the LLM-shaped GEMMs, [16384, 4096]."""
+    x = synth.normal(synth.seed_for(2, 1, 0), (16384, 4096))
+    want_c, want_s = oracle.quant_mx(oracle.E4M3, x)
+    from block_scaled_precision_03_amd import mxgemm
+    codes = torch.empty(want_c.shape, dtype=torch.uint8, device=H.DEV)
+    scales = torch.empty(want_s.shape, dtype=torch.uint8, device=H.DEV)
+    mxgemm.quantize_mx(E4, H.dev(x), codes, scales, 16384, 4096)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+
+
+def _group_case(G, totM, K, seed, m_sizes=None):
+    if m_sizes is None:
+        m_sizes = np.array([totM], np.int64) if G == 1 else synth.m_sizes_for(totM, G, seed)
+    x = synth.normal(seed, (totM, K))
+    if totM >= 3 and K >= 256:
+        x[1, 128:256] = 0.0
+        x[2, :128] = np.float32(448.0 * 3.5)                      # s = 3.5, quotients on the grid
+        x[2, 5] = np.float32(-448.0 * 3.5)
+    return m_sizes, x
+
+
+def _run_group(m_sizes, x, fill_c=0xAB, fill_s=-1.0):
+    from block_scaled_precision_03_amd import mxgemm
+    totM, K = x.shape
+    codes = torch.full((totM, K), fill_c, dtype=torch.uint8, device=H.DEV)
+    xs = torch.full((totM * (K // 128),), fill_s, dtype=torch.float32, device=H.DEV)
+    ms = H.dev(np.asarray(m_sizes, np.int64))
+    mxgemm.grouped_quantize_act(len(m_sizes), ms, H.dev(x), codes, xs, totM, K)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), xs.cpu().numpy()
+
+
+@pytest.mark.parametrize("G,totM,K", [(8, 128, 7168), (8, 1024, 2304), (1, 300, 384), (1024, 5000, 256),
+                                      (3, 17, 128)])
+def test_group_act_bit_exact(G, totM, K):
+    m_sizes, x = _group_case(G, totM, K, 40 + G + totM)
+    got_c, got_s = _run_group(m_sizes, x)
+    want_c, want_s = oracle.quant_group_act(m_sizes, x, codes_fill=0xAB, xs_fill=-1.0)
+    assert np.array_equal(got_c, want_c)
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+
+
+def test_group_act_rows_outside_groups_untouched():
+    """Sizes summing to less than totM (and a negative size, counted as 0):
+    the rows past the last group keep their sentinel codes and scales."""
+    totM, K = 700, 512
+    m_sizes = np.array([100, -5, 0, 333, 90], np.int64)          # covers 523 rows
+    x = synth.normal(71, (totM, K))
+    got_c, got_s = _run_group(m_sizes, x)
+    want_c, want_s = oracle.quant_group_act(m_sizes, x, codes_fill=0xAB, xs_fill=-1.0)
+    assert np.array_equal(got_c, want_c)
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+    assert np.all(got_c[523:] == 0xAB) and np.all(got_s[523 * 4:] == -1.0)
+
+
+@pytest.mark.parametrize("totM,K", [(16384, 7168), (16384, 2304)])
+def test_group_act_full_size(totM, K):
+    m_sizes = synth.m_sizes_for(totM, 8, synth.seed_for(4, 4, 2))
+    x = synth.normal(synth.seed_for(4, 1, 2), (totM, K))
+    got_c, got_s = _run_group(m_sizes, x)
+    want_c, want_s = oracle.quant_group_act(m_sizes, x, codes_fill=0xAB, xs_fill=-1.0)
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(got_c, want_c)
