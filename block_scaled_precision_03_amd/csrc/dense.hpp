@@ -316,10 +316,9 @@ struct DenseLoop {
   }
 
   // DMA of stage st of tile t (operands and MX scales) into ring slot si
-  // (operands) and scale slot gs.  PART selects a quarter of it (0, 1: the A
+  // (operands) and scale slot gs.  PART selects a part of it (0, 1: the A
   // tile's first and second halves; 2: B's first half; 3: B's second half
-  // and the scales) so that the issue can be spread over the K step; -1
-  // issues everything.
+  // and the scales; 4: the scales alone); -1 issues everything.
   template <int PART = -1>
   __device__ static inline void issue(const Ctx &c, const Tile &t, int st, int si, int gs) {
     const DenseArgs &p = *c.p;
@@ -327,7 +326,7 @@ struct DenseLoop {
     constexpr bool ALL = PART < 0;
     if constexpr (ALL || PART == 0) load_tile<TA, 0, 2>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
     if constexpr (ALL || PART == 1) load_tile<TA, 2, 4>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
-    if constexpr (ALL || PART >= 2) {
+    if constexpr (ALL || PART == 2 || PART == 3) {
       constexpr int J0 = (PART == 3) ? 2 : 0, J1 = (PART == 2) ? 2 : 4;
       if constexpr (PSB) {
         // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
@@ -343,7 +342,7 @@ struct DenseLoop {
         load_tile<TB, J0, J1>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
       }
     }
-    if constexpr (MX && (ALL || PART == 3)) {
+    if constexpr (MX && (ALL || PART == 3 || PART == 4)) {
       // With the first stage of each group of four K steps, scale slot gs
       // receives the group's scales: waves 0-3 the A rows 64w.. (16 bytes
       // each), waves 4-7 the B rows 64(w-4).. or, preshuffled, column group
@@ -356,6 +355,41 @@ struct DenseLoop {
         dma_asm<16>(dst, t.rs, c.vo_s, soff);
       }
     }
+  }
+
+  // The same stage DMA with the operand tiles issued by waves 4-7 alone
+  // (K-contiguous operands): wave 4 + v takes A blocks 8v .. 8v + 7 and, of
+  // B, blocks 8v .. 8v + 7 or preshuffled column group v.  The MX scales stay
+  // one DMA per wave.  Each SIMD runs one wave of each half of the
+  // workgroup, so one of its two waves reaches its first matrix-core
+  // instruction right after the barrier while the other queues the ~16
+  // DMAs of 1 KiB whose issue the address path paces.
+  __device__ static inline void issue_hi(const Ctx &c, const Tile &t, int st, int si, int gs) {
+    static_assert(!TA && !TB, "K-contiguous operands");
+    const uint32_t slot = c.lds0 + (uint32_t)si * AB;
+    if (c.w >= 4) {
+      const int v = c.w - 4;
+      const uint32_t abase = slot + (uint32_t)v * 8192u;
+      static_for<0, 8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        dma_asm_v<16, j * 1024>(abase, t.ra, c.vo_a[0], (uint32_t)((v * 8 + j) * 8 * c.KB + 128 * (int64_t)st));
+      });
+      const uint32_t bbase = slot + B_REG + (uint32_t)v * 8192u;
+      if constexpr (PSB) {
+        const uint32_t soff0 = (uint32_t)(((t.n0 / 64 + v) * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB);
+        const u32x4 rb = t.rb;
+        static_for<0, 8>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          dma_asm<16, j * 1024>(bbase, rb, (uint32_t)(c.lane * 16), soff0 + j * 1024);
+        });
+      } else {
+        static_for<0, 8>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          dma_asm_v<16, j * 1024>(bbase, t.rb, c.vo_b[0], (uint32_t)((v * 8 + j) * 8 * c.KB + 128 * (int64_t)st));
+        });
+      }
+    }
+    issue<4>(c, t, st, si, gs);               // the MX scales only
   }
 
   __device__ static inline uint32_t lds_u32(const uint8_t *p) { return lds_load_u32(p); }
@@ -644,14 +678,18 @@ struct DenseLoop {
       auto step = [&](auto epi, auto slot, int k) {
         constexpr bool EPI = decltype(epi)::value;
         constexpr int SC = decltype(slot)::value, SN = 1 - SC;
+        auto issue_any = [&](const Tile &src, int st, int gs) {
+          if constexpr (!TA && !TB) issue_hi(c, src, st, SN, gs);
+          else issue(c, src, st, SN, gs);
+        };
         if (k + 1 < nst) {
-          issue(c, cur, k + 1, SN, (g0 + (k + 1) * KS / 4) & 1);
+          issue_any(cur, k + 1, (g0 + (k + 1) * KS / 4) & 1);
         } else if (more && !odd) {
           // first stage of the next tile into slot 0 (this step reads slot 1);
           // its sources are built here, not kept live through the K loop
           Tile nxt;
           set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, nxt);
-          issue(c, nxt, 0, SN, (g0 + ngrp) & 1);
+          issue_any(nxt, 0, (g0 + ngrp) & 1);
         }
         compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
         // Only where registers allow: for the transposed variants and MX FP8
