@@ -49,6 +49,8 @@ def lib():
         L.oracle_nearest_code.argtypes = [i, d]
         L.oracle_quant_mx.restype = i
         L.oracle_quant_mx.argtypes = [i, p, i64, i64, p, p]
+        L.oracle_quant_group_weight.restype = i
+        L.oracle_quant_group_weight.argtypes = [i, p, i64, i64, p, p]
         L.oracle_quant_group_act.restype = i
         L.oracle_quant_group_act.argtypes = [i, p, p, i64, i64, p, p]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
@@ -228,3 +230,15 @@ def quant_group_act(m_sizes, x, codes_fill=0, xs_fill=np.nan):
     if lib().oracle_quant_group_act(len(ms), _ptr(ms), _ptr(x), totM, K, _ptr(codes), _ptr(xs)) != 0:
         raise ValueError("oracle_quant_group_act: K % 128 != 0")
     return codes, xs
+
+
+def quant_group_weight(w):
+    """Groupwise E4M3 weights: FP32 [G, N, K] -> (codes [G, N, K], FP32
+    scales [G, N/128, K/128]), one scale per 128 x 128 block."""
+    w = _c(w, np.float32)
+    G, N, K = w.shape
+    codes = np.zeros((G, N, K), np.uint8)
+    ws = np.zeros((G, N // 128, K // 128), np.float32)
+    if lib().oracle_quant_group_weight(G, _ptr(w), N, K, _ptr(codes), _ptr(ws)) != 0:
+        raise ValueError("oracle_quant_group_weight: N or K not a multiple of 128")
+    return codes, ws

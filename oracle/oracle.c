@@ -462,3 +462,34 @@ int oracle_quant_group_act(int G, const int64_t *m_sizes, const float *x, int64_
     }
     return 0;
 }
+
+/* Groupwise E4M3 weights: w FP32 [G, N, K], N % 128 == 0, K % 128 == 0; one
+ * FP32 scale per 128 x 128 block, ws [G, N/128, K/128] row-major ("Add
+ * FlyDSL grouped groupwise FP8 GEMM for ROCm", PR body: 128x128 weight
+ * blocks), with the same rule as the activations: s = amax / 448 as an FP32
+ * quotient (1.0 for an all-zero block), element code = nearest(FP32
+ * quotient w / s). */
+int oracle_quant_group_weight(int G, const float *w, int64_t N, int64_t K, uint8_t *codes, float *ws)
+{
+    if (N % 128 != 0 || K % 128 != 0) return -1;
+    const int64_t nb = N / 128, kb = K / 128;
+    #pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < (int64_t)G * nb * kb; ++blk) {
+        const int64_t g = blk / (nb * kb), bn = (blk / kb) % nb, bk = blk % kb;
+        const float *base = w + (g * N + bn * 128) * K + bk * 128;
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i)
+            for (int j = 0; j < 128; ++j)
+                if (fabsf(base[i * K + j]) > amax) amax = fabsf(base[i * K + j]);
+        volatile float s = amax / 448.0f;              /* FP32 quotient */
+        const float sc = amax > 0.0f ? s : 1.0f;
+        ws[blk] = sc;
+        uint8_t *out = codes + (g * N + bn * 128) * K + bk * 128;
+        for (int i = 0; i < 128; ++i)
+            for (int j = 0; j < 128; ++j) {
+                volatile float q = base[i * K + j] / sc;   /* FP32 quotient */
+                out[i * K + j] = (uint8_t)orc_nearest(ORC_E4M3, (double)q);
+            }
+    }
+    return 0;
+}

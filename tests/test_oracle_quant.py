@@ -153,3 +153,19 @@ def test_quant_group_act_rows_outside_groups_untouched():
     assert np.all(codes[5:] == 0xAB)
     assert np.all(xs[5 * 2:] == -1.0)
     assert np.all(xs[:5 * 2] > 0)
+
+
+def test_quant_group_weight_equals_input_generator_and_bracket():
+    w = synth.normal(80, (3, 256, 384), 0.02)
+    w[1, :128, 128:256] = 0.0                                     # an all-zero block
+    w[2, 128:, :128] *= np.float32(1e-20)                         # a tiny block
+    codes, ws = oracle.quant_group_weight(w)
+    c2, ws2 = synth.quant_group_weight(w)
+    assert np.array_equal(codes, c2)
+    assert np.array_equal(ws, ws2)
+    assert ws[1, 0, 1] == np.float32(1.0)
+    # every block's scale is the FP32 quotient amax / 448, and its largest
+    # element decodes to +-448 (or the nearest code to it)
+    blk = np.abs(w.reshape(3, 2, 128, 3, 128)).max(axis=(2, 4))
+    want = np.where(blk > 0, (blk / np.float32(448.0)).astype(np.float32), np.float32(1.0))
+    assert np.array_equal(ws, want)
