@@ -367,9 +367,10 @@ def mx_backward_bench(torch, synth, mxgemm, dev):
 
 
 def quant_bench(torch, synth, mxgemm, dev):
-    """The on-device quantizers at the workloads' activation shapes: MX E4M3
-    of the [16384, 4096] activation (E8M0 per 32) and groupwise E4M3 of the
-    grouped GEMM's [16384, 7168] activation (G = 8, per-group block scales).
+    """The on-device quantizers at the workloads' shapes: MX E4M3 of the
+    [16384, 4096] activation (E8M0 per 32), groupwise E4M3 of the grouped
+    GEMM's [16384, 7168] activation (G = 8, per-group block scales) and of its
+    [8, 2048, 7168] weights (128 x 128 blocks).
     HBM-bound: algorithmic bytes = 4 per value read + 1 per code + scales."""
     out = []
     x = torch.from_numpy(synth.normal(synth.seed_for(2, 1, 0), (16384, 4096))).to(dev)
@@ -389,10 +390,20 @@ def quant_bench(torch, synth, mxgemm, dev):
     nbytes = totM * K * 5 + totM * K // 128 * 4 + 8 * 8
     out.append({"name": "grouped_quantize_act e4m3 G=8", "rows": totM, "K": K, "us": us, "bytes": nbytes,
                 "gbs": nbytes / us / 1e3, "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
+    del x, codes, xs
+    G, N = 8, 2048
+    w = torch.from_numpy(synth.normal(synth.seed_for(4, 2, 2), (G, N, K), 0.02)).to(dev)
+    codes = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
+    us = time_calls(torch, lambda: mxgemm.grouped_quantize_weight(G, w, codes, xs, N, K))
+    nbytes = G * N * K * 5 + G * (N // 128) * (K // 128) * 4
+    out.append({"name": "grouped_quantize_weight e4m3 G=8", "rows": G * N, "K": K, "us": us, "bytes": nbytes,
+                "gbs": nbytes / us / 1e3, "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
+    del w
     for r in out:
         log("%s [%d, %d]: %.1f us, %.0f GB/s (%.1f%% of HBM)" % (r["name"], r["rows"], r["K"], r["us"], r["gbs"],
                                                                 r["pct_hbm"]))
-    del x, codes, xs
+    del codes, xs
     torch.cuda.empty_cache()
     return out
 

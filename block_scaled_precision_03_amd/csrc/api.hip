@@ -444,3 +444,19 @@ extern "C" int grouped_fp8_quantize_act(int G, const int64_t *m_sizes, const flo
                      (uint8_t *)codes, x_scale, totM, K);
   return launch_status();
 }
+
+extern "C" int grouped_fp8_quantize_weight(int G, const float *w, void *codes, float *w_scale, int64_t N, int64_t K,
+                                           hipStream_t stream) {
+  if (G < 1 || G > MXG_GROUPED_MAX_G) return MXG_ERR_UNSUPPORTED;
+  if (N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (N % 128 != 0 || K % 128 != 0) return MXG_ERR_UNSUPPORTED;
+  if (N >= MAX_DIM || K > MAX_ROW_BYTES) return MXG_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return MXG_OK;
+  if (!w || !codes || !w_scale) return MXG_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(codes, 4) || !aligned(w_scale, 4)) return MXG_ERR_MISALIGNED;
+  const int64_t blocks = (int64_t)G * (N / 128) * (K / 128);
+  if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(quant_group_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, (uint8_t *)codes,
+                     w_scale, N, K);
+  return launch_status();
+}

@@ -15,7 +15,11 @@
 // written in the per-group block layout the grouped GEMM reads: (row r of
 // group g, k block kb) at start_g * (K/128) + (r - start_g) + kb * M_g.
 //
-// Both are HBM-bound streams: 4 bytes read per element, 1 (FP8) or 1/2
+// The weights ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", PR body:
+// 128x128 weight blocks) follow the activations' rule per 128 x 128 block,
+// scales [G, N/128, K/128] row-major.
+//
+// All are HBM-bound streams: 4 bytes read per element, 1 (FP8) or 1/2
 // (FP4) written, plus the scales.
 #pragma once
 #include "common.hpp"
@@ -180,6 +184,47 @@ __global__ __launch_bounds__(256) void quant_group_act_kernel(const int64_t *__r
     }
     *(uint2 *)(codes + (int64_t)r * K + 128 * kb + 8 * sub) = make_uint2(lo4, hi4);
     if (sub == 0) xs[(int64_t)start * nkb + (r - start) + kb * mg] = s;
+  }
+}
+
+// Groupwise weights: one workgroup per 128 x 128 block of w [G, N, K] (K
+// contiguous).  Thread t reads float4 chunk t % 32 of rows 2i + (t / 32) % 2
+// of its wave's 32-row band (i = 0..15), so each load instruction covers two
+// whole 512-byte rows; the block maximum goes through the wave (shuffles) and
+// LDS (four waves).
+__global__ __launch_bounds__(256) void quant_group_weight_kernel(const float *__restrict__ w,
+                                                                 uint8_t *__restrict__ codes,
+                                                                 float *__restrict__ ws, int64_t N, int64_t K) {
+  __shared__ float wmax[4];
+  const int64_t nb = N / 128, kb = K / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t g = blk / (nb * kb), bn = (blk / kb) % nb, bk = blk % kb;
+  const int64_t origin = (g * N + bn * 128) * K + bk * 128;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = lane & 31, half = lane >> 5;
+  float4 v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t row = wave * 32 + 2 * i + half;
+    v[i] = *(const float4 *)(w + origin + row * K + 4 * chunk);
+    m = fmaxf(m, max4(fabsf(v[i].x), fabsf(v[i].y), fabsf(v[i].z), fabsf(v[i].w)));
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  m = max4(wmax[0], wmax[1], wmax[2], wmax[3]);
+  const float s = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+  if (threadIdx.x == 0) ws[blk] = s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t row = wave * 32 + 2 * i + half;
+    const uint32_t c = encode_nearest<F_E4M3>(__fdiv_rn(v[i].x, s)) |
+                       (encode_nearest<F_E4M3>(__fdiv_rn(v[i].y, s)) << 8) |
+                       (encode_nearest<F_E4M3>(__fdiv_rn(v[i].z, s)) << 16) |
+                       (encode_nearest<F_E4M3>(__fdiv_rn(v[i].w, s)) << 24);
+    *(uint32_t *)(codes + origin + row * K + 4 * chunk) = c;
   }
 }
 

@@ -26,7 +26,7 @@ EXPORTS = (
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
-    "mxgemm_quantize_mx", "grouped_fp8_quantize_act",
+    "mxgemm_quantize_mx", "grouped_fp8_quantize_act", "grouped_fp8_quantize_weight",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -63,6 +63,8 @@ _lib.grouped_fp8_preshuffle_b.restype = _i
 _lib.grouped_fp8_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
 _lib.mxgemm_quantize_mx.restype = _i
 _lib.mxgemm_quantize_mx.argtypes = [_i, _p, _p, _p, _i64, _i64, _p]
+_lib.grouped_fp8_quantize_weight.restype = _i
+_lib.grouped_fp8_quantize_weight.argtypes = [_i, _p, _p, _p, _i64, _i64, _p]
 _lib.grouped_fp8_quantize_act.restype = _i
 _lib.grouped_fp8_quantize_act.argtypes = [_i, _p, _p, _p, _p, _i64, _i64, _p]
 
@@ -174,3 +176,9 @@ def grouped_quantize_act(G, m_sizes, x, codes, x_scale, totM, K, stream=None):
     """FP32 activations -> E4M3 codes and per-group block-layout FP32 scales."""
     _check(_lib.grouped_fp8_quantize_act(G, _ptr(m_sizes), _ptr(x), _ptr(codes), _ptr(x_scale), totM, K,
                                          _stream(stream)), "grouped_fp8_quantize_act")
+
+
+def grouped_quantize_weight(G, w, codes, w_scale, N, K, stream=None):
+    """FP32 weights [G, N, K] -> E4M3 codes and FP32 128 x 128 block scales."""
+    _check(_lib.grouped_fp8_quantize_weight(G, _ptr(w), _ptr(codes), _ptr(w_scale), N, K, _stream(stream)),
+           "grouped_fp8_quantize_weight")

@@ -247,6 +247,25 @@ int grouped_fp8_quantize_act(int G, const int64_t *m_sizes, const float *x, void
                              float *x_scale, int64_t totM, int64_t K, hipStream_t stream);
 
 /*
+ * grouped_fp8_quantize_weight -- FP32 weights -> the WQ and w_scale inputs
+ * of grouped_fp8_gemm_run: E4M3 codes with one FP32 scale per 128 x 128
+ * block ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", PR body).
+ *
+ * w        device FP32 [G, N, K] row-major (K contiguous), 16-byte aligned.
+ * codes    device out: E4M3 [G, N, K] (plain layout; grouped_fp8_preshuffle_b
+ *          makes the preshuffled one), 4-byte aligned.
+ * w_scale  device out: FP32 [G, N/128, K/128] row-major, 4-byte aligned.
+ * Per block: s = amax / 448 as an FP32 quotient (1.0 for an all-zero
+ * block); element code = nearest E4M3 value of the FP32 quotient w / s,
+ * ties to the even code, saturating.  Inputs must be finite.
+ * Errors: MXG_ERR_UNSUPPORTED (G outside [1, MXG_GROUPED_MAX_G], N or K not
+ * a multiple of 128), MXG_ERR_INVALID_ARG, MXG_ERR_MISALIGNED.  N or K = 0:
+ * no-op.
+ */
+int grouped_fp8_quantize_weight(int G, const float *w, void *codes, float *w_scale,
+                                int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * mxgemm_mfma_ceiling -- a measurement aid, not part of the GEMM path: one
  * workgroup per compute unit, eight waves each running 32 independent chains
  * of the scaled 16x16x128 matrix-core instruction for `iters` iterations

@@ -113,6 +113,10 @@ def test_ops_reject_bad_args_before_device_use():
     assert lib.grouped_fp8_quantize_act(8, P, P, P, P, 128, 200, None) == -2    # K % 128
     assert lib.grouped_fp8_quantize_act(8, 0, P, P, P, 128, 128, None) == -1    # null m_sizes
     assert lib.grouped_fp8_quantize_act(8, P, P, P, P + 2, 128, 128, None) == -3  # misaligned scales
+    assert lib.grouped_fp8_quantize_weight(8, P, P, P, 200, 128, None) == -2     # N % 128
+    assert lib.grouped_fp8_quantize_weight(0, P, P, P, 128, 128, None) == -2     # G < 1
+    assert lib.grouped_fp8_quantize_weight(8, P + 4, P, P, 128, 128, None) == -3  # misaligned w
+    assert lib.grouped_fp8_quantize_weight(8, P, P, P, 0, 128, None) == 0        # N = 0: no-op
 
 
 def test_package_has_no_cpu_fallback():

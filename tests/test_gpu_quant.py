@@ -124,3 +124,23 @@ def test_group_act_full_size(totM, K):
     want_c, want_s = oracle.quant_group_act(m_sizes, x, codes_fill=0xAB, xs_fill=-1.0)
     assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
     assert np.array_equal(got_c, want_c)
+
+
+@pytest.mark.parametrize("G,N,K", [(1, 128, 128), (3, 256, 384), (8, 2048, 7168)])
+def test_group_weight_bit_exact(G, N, K):
+    """128 x 128 weight blocks (the last case is the grouped workload's
+    [8, 2048, 7168] weight), with an all-zero, a tiny and a saturating block."""
+    from block_scaled_precision_03_amd import mxgemm
+    w = synth.normal(60 + G + N, (G, N, K), 0.02)
+    w[0, :128, :128] = 0.0
+    if K >= 256:
+        w[0, :128, 128:256] *= np.float32(1e-20)
+    if N >= 256:
+        w[-1, 128:256, :128] = np.float32(448.0 * 0.5)
+    want_c, want_s = oracle.quant_group_weight(w)
+    codes = torch.full((G, N, K), 0xAB, dtype=torch.uint8, device=H.DEV)
+    ws = torch.full((G, N // 128, K // 128), -1.0, dtype=torch.float32, device=H.DEV)
+    mxgemm.grouped_quantize_weight(G, H.dev(w), codes, ws, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(ws.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), want_c)
