@@ -144,3 +144,57 @@ def test_group_weight_bit_exact(G, N, K):
     torch.cuda.synchronize()
     assert np.array_equal(ws.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
     assert np.array_equal(codes.cpu().numpy(), want_c)
+
+
+def test_device_quantize_then_mx_gemm():
+    """The whole MX path on the device: FP32 activations and weights ->
+    quantize_mx -> mxgemm_run (preshuffled B), against the oracle's GEMM of
+    the oracle's own quantization, and bit for bit against the device GEMM
+    run on the oracle's codes."""
+    from block_scaled_precision_03_amd import mxgemm
+    M, N, K = 528, 400, 1024
+    x = synth.normal(51, (M, K))
+    w = synth.normal(52, (N, K), 0.02)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=H.DEV)
+    sa = torch.empty((M, K // 32), dtype=torch.uint8, device=H.DEV)
+    qb = torch.empty((N, K), dtype=torch.uint8, device=H.DEV)
+    sb = torch.empty((N, K // 32), dtype=torch.uint8, device=H.DEV)
+    mxgemm.quantize_mx(E4, H.dev(x), qa, sa, M, K)
+    mxgemm.quantize_mx(E4, H.dev(w), qb, sb, N, K)
+    torch.cuda.synchronize()
+    ca, ea = oracle.quant_mx(oracle.E4M3, x)
+    cb, eb = oracle.quant_mx(oracle.E4M3, w)
+    opA = H.Operand(E4, qa.cpu().numpy(), sa.cpu().numpy(), False, M, K)
+    opB = H.Operand(E4, qb.cpu().numpy(), sb.cpu().numpy(), False, N, K)
+    D1 = H.run_dense(0, opA, opB, M, N, K, preshuffle_b=True)
+    D2 = H.run_dense(0, H.Operand(E4, ca, ea, False, M, K), H.Operand(E4, cb, eb, False, N, K), M, N, K,
+                     preshuffle_b=True)
+    assert np.array_equal(H.bits(D1), H.bits(D2))
+    ref = oracle.gemm((oracle.E4M3, oracle.SCALE_MX, False, ca, ea), (oracle.E4M3, oracle.SCALE_MX, False, cb, eb),
+                      M, N, K)
+    H.assert_close(H.bf16_to_f64(D1), ref, "device quantize + mx gemm")
+
+
+def test_device_quantize_then_grouped_gemm():
+    """The whole grouped path on the device: FP32 activations and weights ->
+    grouped_fp8_quantize_act / _weight -> grouped_fp8_gemm_run, against the
+    oracle's grouped GEMM of the oracle's quantization."""
+    from block_scaled_precision_03_amd import mxgemm
+    G, totM, N, K = 8, 1024, 256, 384
+    m_sizes = synth.m_sizes_for(totM, G, 53)
+    x = synth.normal(54, (totM, K))
+    w = synth.normal(55, (G, N, K), 0.02)
+    ms = H.dev(m_sizes)
+    xq = torch.empty((totM, K), dtype=torch.uint8, device=H.DEV)
+    xs = torch.empty((totM * K // 128,), dtype=torch.float32, device=H.DEV)
+    wq = torch.empty((G, N, K), dtype=torch.uint8, device=H.DEV)
+    ws = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=H.DEV)
+    mxgemm.grouped_quantize_act(G, ms, H.dev(x), xq, xs, totM, K)
+    mxgemm.grouped_quantize_weight(G, H.dev(w), wq, ws, N, K)
+    D = torch.full((totM, N), float("nan"), dtype=torch.bfloat16, device=H.DEV)
+    mxgemm.grouped_run(G, ms, xq, xs, wq, ws, D, totM, N, K)
+    torch.cuda.synchronize()
+    cx, sx = oracle.quant_group_act(m_sizes, x)
+    cw, sw = oracle.quant_group_weight(w)
+    ref = oracle.grouped_gemm(m_sizes, cx, sx, cw, sw, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D), ref, "device quantize + grouped gemm")
