@@ -152,12 +152,14 @@ __global__ __launch_bounds__(256) void quant_group_act_kernel(const int64_t *__r
   }
   __syncthreads();
   const int covered = pre[G];
-  const int64_t nkb = K / 128;
-  const int64_t nblk = (int64_t)covered * nkb;
+  // block counts stay below 2^29 (the entry point bounds totM * K/128), so
+  // the row of a block comes from a 32-bit division
+  const uint32_t nkb = (uint32_t)(K / 128);
+  const uint32_t nblk = (uint32_t)covered * nkb;
   const int sub = threadIdx.x & 15;
-  for (int64_t b = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); b < nblk; b += (int64_t)gridDim.x * 16) {
+  for (uint32_t b = blockIdx.x * 16u + (threadIdx.x >> 4); b < nblk; b += gridDim.x * 16u) {
     const int r = (int)(b / nkb);
-    const int64_t kb = b - (int64_t)r * nkb;
+    const int64_t kb = (int64_t)(b - (uint32_t)r * nkb);
     // group of row r: the last g with pre[g] <= r (pre[g+1] > r then)
     int lo = 0, hi = G;                          // pre[lo] <= r < pre[hi]
     while (hi - lo > 1) {
