@@ -56,6 +56,25 @@ __device__ inline uint32_t encode_nearest(float y) {
   return c | (neg << (FMT == F_E2M1 ? 3 : 7));
 }
 
+// Four E4M3 (E5M2) codes of a, b, c, d (finite) by gfx950's conversion
+// instruction (round to nearest even, OCP formats), after saturating to
+// +-448 (+-57344) so that no value overflows: the same decision as
+// encode_nearest, in one instruction per pair.  encode_nearest stays the
+// definition the tests compare both against (and the E2M1 encoder).
+__device__ inline uint32_t encode4_e4m3_hw(float a, float b, float c, float d) {
+  auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+
+__device__ inline uint32_t encode4_e5m2_hw(float a, float b, float c, float d) {
+  auto sat = [](float v) { return fminf(fmaxf(v, -57344.0f), 57344.0f); };
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+
 // X = floor(log2(amax / fmt_max)), exactly: with amax = f 2^e (f in
 // [0.5, 1)) and fmt_max = g 2^h (g in [0.5, 1)), the ratio is (f/g) 2^(e-h)
 // with f/g in (0.5, 2), so X = e - h, less one when f < g.
@@ -95,14 +114,10 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__
 #pragma unroll
     for (int j = 0; j < 8; ++j) w |= encode_nearest<FMT>(y[j]) << (4 * j);
     ((uint32_t *)codes)[t] = w;
+  } else if constexpr (FMT == F_E4M3) {
+    ((uint2 *)codes)[t] = make_uint2(encode4_e4m3_hw(y[0], y[1], y[2], y[3]), encode4_e4m3_hw(y[4], y[5], y[6], y[7]));
   } else {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= encode_nearest<FMT>(y[j]) << (8 * j);
-      hi |= encode_nearest<FMT>(y[4 + j]) << (8 * j);
-    }
-    ((uint2 *)codes)[t] = make_uint2(lo, hi);
+    ((uint2 *)codes)[t] = make_uint2(encode4_e5m2_hw(y[0], y[1], y[2], y[3]), encode4_e5m2_hw(y[4], y[5], y[6], y[7]));
   }
   if ((t & 3) == 0) scales[t >> 2] = (uint8_t)(X + 127);
 }
@@ -178,12 +193,8 @@ __global__ __launch_bounds__(256) void quant_group_act_kernel(const int64_t *__r
     const float s = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
     const float q[8] = {__fdiv_rn(u.x, s), __fdiv_rn(u.y, s), __fdiv_rn(u.z, s), __fdiv_rn(u.w, s),
                         __fdiv_rn(v.x, s), __fdiv_rn(v.y, s), __fdiv_rn(v.z, s), __fdiv_rn(v.w, s)};
-    uint32_t lo4 = 0, hi4 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo4 |= encode_nearest<F_E4M3>(q[j]) << (8 * j);
-      hi4 |= encode_nearest<F_E4M3>(q[4 + j]) << (8 * j);
-    }
+    const uint32_t lo4 = encode4_e4m3_hw(q[0], q[1], q[2], q[3]);
+    const uint32_t hi4 = encode4_e4m3_hw(q[4], q[5], q[6], q[7]);
     *(uint2 *)(codes + (int64_t)r * K + 128 * kb + 8 * sub) = make_uint2(lo4, hi4);
     if (sub == 0) xs[(int64_t)start * nkb + (r - start) + kb * mg] = s;
   }
@@ -222,10 +233,8 @@ __global__ __launch_bounds__(256) void quant_group_weight_kernel(const float *__
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t row = wave * 32 + 2 * i + half;
-    const uint32_t c = encode_nearest<F_E4M3>(__fdiv_rn(v[i].x, s)) |
-                       (encode_nearest<F_E4M3>(__fdiv_rn(v[i].y, s)) << 8) |
-                       (encode_nearest<F_E4M3>(__fdiv_rn(v[i].z, s)) << 16) |
-                       (encode_nearest<F_E4M3>(__fdiv_rn(v[i].w, s)) << 24);
+    const uint32_t c = encode4_e4m3_hw(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s), __fdiv_rn(v[i].z, s),
+                                       __fdiv_rn(v[i].w, s));
     *(uint32_t *)(codes + origin + row * K + 4 * chunk) = c;
   }
 }
