@@ -488,6 +488,53 @@ def cpu_baseline(synth, target_s=12.0):
             "seconds": dt}
 
 
+_SINGLE_THREAD = r'''
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import oracle
+from block_scaled_precision_03_amd import synth
+x = synth.normal(synth.seed_for(1, 1), (256, 256))
+w = synth.normal(synth.seed_for(1, 2), (256, 256))
+qa, sa = synth.quant_mx(x, "e4m3")
+qb, sb = synth.quant_mx(w, "e4m3")
+t0 = time.perf_counter()
+oracle.gemm((oracle.E4M3, oracle.SCALE_MX, 0, qa, sa), (oracle.E4M3, oracle.SCALE_MX, 0, qb, sb), 256, 256, 256)
+t1 = time.perf_counter() - t0
+G, totM, N, K = 8, 128, 2048, 7168
+ms = synth.m_sizes_for(totM, G, synth.seed_for(4, 4, 0))
+xq, xs = synth.quant_group_act(synth.normal(synth.seed_for(4, 1, 0), (totM, K)), ms)
+wq, ws = synth.quant_group_weight(synth.normal(synth.seed_for(4, 2, 0), (G, N, K), 0.02))
+t0 = time.perf_counter()
+oracle.grouped_gemm(ms, xq, xs, wq, ws, totM, N, K)
+t4 = time.perf_counter() - t0
+print(json.dumps({"mxfp8_256_cube_s": t1, "grouped_totM128_2048x7168_s": t4}))
+'''
+
+
+def cpu_single_thread_start():
+    """Starts the oracle on one thread (OMP_NUM_THREADS=1) in a child process
+    that never touches the GPU: the MXFP8 256^3 GEMM and the grouped G=8,
+    totM=128, N=2048, K=7168 GEMM, contraction time only.  It runs beside the
+    GPU legs (one host core) and is collected before the all-core sample."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    return subprocess.Popen([sys.executable, "-c", _SINGLE_THREAD, ROOT], env=env,
+                            stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def cpu_single_thread_collect(proc):
+    import subprocess
+    try:
+        out, err = proc.communicate(timeout=300)
+        if proc.returncode != 0:
+            return {"error": err.strip()[-200:]}
+        return json.loads(out.strip().splitlines()[-1])
+    except (subprocess.SubprocessError, ValueError, IndexError) as exc:
+        proc.kill()
+        proc.communicate()
+        return {"error": str(exc)[:200]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -559,6 +606,9 @@ def main():
     }
     del outs, calls, xs, ws
     torch.cuda.empty_cache()
+    single = None
+    if not args.only_step and not args.no_cpu:
+        single = cpu_single_thread_start()
     if not args.only_step and not args.no_grouped:
         log("grouped G=8 ...")
         result["grouped"] = grouped_bench(torch, synth, mxgemm, dev)
@@ -575,8 +625,11 @@ def main():
         result["roofline"]["frac_of_mfma_ceiling"] = (
             result["roofline"]["achieved"] / result["mfma_ceiling"]["fp8"]["tflops"])
     if not args.only_step and not args.no_cpu:
+        log("CPU oracle, one thread (C1 256^3, grouped totM=128) ...")
+        single = cpu_single_thread_collect(single)
         log("CPU oracle sample ...")
         result["cpu_baseline"] = cpu_baseline(synth)
+        result["cpu_baseline"]["single_thread"] = single
         log("cpu baseline: %.4g TFLOP/s on %d threads" % (result["cpu_baseline"]["value"],
                                                           result["cpu_baseline"]["cores"]))
     else:
