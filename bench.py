@@ -456,9 +456,26 @@ def mxfp4_bench(torch, synth, mxgemm, dev):
     return {"M": M, "N": N, "K": K, "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP4_TFLOPS}
 
 
-def cpu_baseline(synth, target_s=12.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def bf16_bits_to_f64(u16):
+    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def cpu_baseline(synth, gpu_bits=None, target_s=12.0):
     """The FP64 oracle, as it stands, on rows [0, R) of the M=16384,
-    N=4096, K=4096 MXFP8 GEMM (dequantize + plain FP64 dot products)."""
+    N=4096, K=4096 MXFP8 GEMM (dequantize + plain FP64 dot products).
+    gpu_bits: the BF16 bits of the timed step's result for that GEMM (same
+    seeded inputs); its rows [0, R) are checked against the oracle's."""
     import oracle
     N = K = 4096
     x = synth.normal(synth.seed_for(2, 1, 0), (16384, K))
@@ -468,24 +485,29 @@ def cpu_baseline(synth, target_s=12.0):
     def run(rows):
         qa, sa = synth.quant_mx(x[:rows], "e4m3")
         t0 = time.perf_counter()
-        oracle.gemm((oracle.E4M3, oracle.SCALE_MX, 0, qa, sa), opB, rows, N, K)
-        return time.perf_counter() - t0
+        D = oracle.gemm((oracle.E4M3, oracle.SCALE_MX, 0, qa, sa), opB, rows, N, K)
+        return time.perf_counter() - t0, D
     # size the sample from a probe, and once more from the first sample if
     # the probe (thread start-up included) misjudged it by more than 2x
     probe_rows = 128
-    tp = run(probe_rows)
+    tp, _ = run(probe_rows)
     rows = int(max(probe_rows, min(16384, probe_rows * target_s / max(tp, 1e-3))))
     rows = max(16, rows // 16 * 16)
-    dt = run(rows)
+    dt, D = run(rows)
     if dt < 0.5 * target_s and rows < 16384:
         rows = max(16, int(min(16384, rows * target_s / max(dt, 1e-3))) // 16 * 16)
-        dt = run(rows)
+        dt, D = run(rows)
     flops = 2.0 * rows * N * K
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "rows 0..%d of the M=16384 N=4096 K=4096 MXFP8 NT GEMM (FP64 dequant + "
-                      "dot products), %.1f s" % (rows, dt),
-            "seconds": dt}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": "rows 0..%d of the M=16384 N=4096 K=4096 MXFP8 NT GEMM (FP64 dequant + "
+                     "dot products), %.1f s" % (rows, dt),
+           "seconds": dt, "cpu_model": cpu_model()}
+    if gpu_bits is not None:
+        ok, worst = oracle.within_tolerance(bf16_bits_to_f64(gpu_bits[:rows]), D)
+        res["parity"] = {"rows": rows, "worst_ratio": worst, "pass": ok,
+                         "bound": "|d-ref| <= 2^-7|ref| + 1e-3 max|ref| (max over the sampled rows)"}
+    return res
 
 
 _SINGLE_THREAD = r'''
@@ -604,6 +626,11 @@ def main():
                      "kernel_ms_per_step": kernel_ms},
         "per_gemm": per_gemm,
     }
+    # the timed step's result of the M=16384 N=K=4096 GEMM, for the check in
+    # the CPU leg (the oracle runs on the same seeded inputs)
+    check_bits = None
+    if not args.only_step and not args.no_cpu:
+        check_bits = outs[(16384, 4096, 4096)].view(torch.int16).cpu().numpy().view(np.uint16)
     del outs, calls, xs, ws
     torch.cuda.empty_cache()
     single = None
@@ -628,10 +655,15 @@ def main():
         log("CPU oracle, one thread (C1 256^3, grouped totM=128) ...")
         single = cpu_single_thread_collect(single)
         log("CPU oracle sample ...")
-        result["cpu_baseline"] = cpu_baseline(synth)
+        result["cpu_baseline"] = cpu_baseline(synth, check_bits)
+        del check_bits
         result["cpu_baseline"]["single_thread"] = single
         log("cpu baseline: %.4g TFLOP/s on %d threads" % (result["cpu_baseline"]["value"],
                                                           result["cpu_baseline"]["cores"]))
+        par = result["cpu_baseline"].get("parity")
+        if par is not None:
+            log("step result vs oracle, rows 0..%d: worst ratio %.3g, %s"
+                % (par["rows"], par["worst_ratio"], "pass" if par["pass"] else "FAIL"))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
