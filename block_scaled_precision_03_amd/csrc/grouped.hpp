@@ -157,10 +157,11 @@ namespace mxg {
 //   major and M-tile minor, so that consecutive tiles share one weight tile.
 //   Each workgroup finds a tile's group by binary search in a table of the
 //   groups' first rows and first tiles that wave 0 builds in LDS once.
-// * Persistent grid of P workgroups, two per compute unit: workgroup j walks
-//   tiles j, j + P, j + 2P, ...; workgroups are renumbered so that
-//   consecutive j run on one XCD (one L2), and tiles that read the same
-//   weights at the same time share it.
+// * Persistent grid of P workgroups, two per compute unit: each walks one
+//   tile of every round of P consecutive tiles; within a round each XCD (one
+//   L2) takes a contiguous band of tiles, the eight bands as even as the
+//   round allows, so tiles that read the same weights at the same time
+//   share an L2 and no XCD idles while another holds two tiles per CU.
 // * A two-slot ring of stages of KS 128-K steps (per step: A rows, weight
 //   rows, the tile's activation scales and weight block scale) is filled by
 //   buffer-load-to-LDS DMA issued from inline assembly with explicit waits.
@@ -282,11 +283,22 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   if (w == 0) build_group_table<BM>(p, gt, lane);
   __syncthreads();
   const int P = (int)gridDim.x;
-  int j = (int)blockIdx.x;
-  if ((P & 7) == 0) j = (j & 7) * (P >> 3) + (j >> 3);
   const int64_t T = (int64_t)uni32(gt.mtile[p.G]) * p.tiles_n;   // real tiles
-  if (j >= T) return;
-  const int64_t ntile = (T - 1 - j) / P + 1;       // tiles of this workgroup
+  // Workgroup b runs on XCD x = b % 8 (workgroups are dealt to the eight
+  // XCDs in turn) as that XCD's r-th, r = b / 8.  Each round of P
+  // consecutive tiles (the last round holds T mod P) is cut into eight
+  // contiguous bands as even as the round allows, band x for XCD x, and the
+  // r-th workgroup of XCD x takes tile r of its band.  Every XCD then has
+  // the same share of the work, also when there are fewer tiles than
+  // workgroups, and tiles with the same weights share one L2.
+  const int x = (int)(blockIdx.x & 7), r = (int)(blockIdx.x >> 3);
+  const int64_t full = T / P, last = T - full * P;
+  auto band_start = [&](int64_t size) -> int64_t { return x * (size >> 3) + (x < (size & 7) ? x : (size & 7)); };
+  auto band_count = [&](int64_t size) -> int64_t { return (size >> 3) + (x < (size & 7) ? 1 : 0); };
+  const int64_t ntile = full + (r < band_count(last) ? 1 : 0);   // tiles of this workgroup
+  if (ntile == 0) return;
+  const int64_t off_full = band_start(P) + r, off_last = band_start(last) + r;
+  auto tile_of = [&](int64_t i) -> int64_t { return i * P + (i < full ? off_full : off_last); };
   const int64_t K = p.K, N = p.N;
   const int nst = (int)(K / 128);                  // K steps per tile
   const int nsg = (nst + KS - 1) / KS;             // stages per tile
@@ -308,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     int vrows;
   };
   auto make_src = [&](int64_t i) {
-    const StreamTile t = stream_tile<BM>(p, gt, j + i * P);
+    const StreamTile t = stream_tile<BM>(p, gt, tile_of(i));
     Src s;
     const int64_t abase = t.row0 * K;
     s.ra = rsrc4(p.XQ + abase, clamp_records(p.totM * K - abase));
@@ -429,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     if (++csg == nsg) {
       // Last K step of tile ci: lane (i16, q) holds rows 16a + i16 and
       // columns 16b + 4q .. +3 of the wave's 32 x 32 block.
-      const StreamTile t = stream_tile<BM>(p, gt, j + ci * P);
+      const StreamTile t = stream_tile<BM>(p, gt, tile_of(ci));
       const int64_t row_lim = t.start + t.mg;
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
