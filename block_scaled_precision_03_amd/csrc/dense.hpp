@@ -557,23 +557,45 @@ struct DenseLoop {
         return rdt(lb, L.bt ^ ((uint32_t)b << 4));
       } else return rd8(lb, L.b[0], L.b[1], b * 2048);
     };
+    auto b_scale = [&](int s, int b) -> int {
+      if constexpr (MX) {
+        const int j = (st * KS + s) & 3;        // K step within the scale group
+        if constexpr (PSB) {
+          const uint32_t word = lds_u32(ls + L.sb + b * 256);
+          return (int)(word >> (8 * j));
+        } else {
+          const uint32_t word = lds_u32(ls + L.sb + b * 256 + j * 4);
+          return (int)(word >> (8 * c.q));
+        }
+      }
+      return E8M0_ONE_X4;
+    };
+    // A stage of two K steps (FP4) reads both steps' B fragments and scales
+    // up front, so that the second step's reads overlap the first step's
+    // matrix work instead of stalling between the two.
+    v8i bpre[KS][FN];
+    int spre[KS][FN];
+    if constexpr (KS > 1) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          bpre[s][b] = read_b(s, b);
+          spre[s][b] = b_scale(s, b);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       v8i bf[FN];
       int sb[FN];
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
-        bf[b] = read_b(s, b);
-        sb[b] = E8M0_ONE_X4;
-        if constexpr (MX) {
-          const int j = (st * KS + s) & 3;      // K step within the scale group
-          if constexpr (PSB) {
-            const uint32_t word = lds_u32(ls + L.sb + b * 256);
-            sb[b] = (int)(word >> (8 * j));
-          } else {
-            const uint32_t word = lds_u32(ls + L.sb + b * 256 + j * 4);
-            sb[b] = (int)(word >> (8 * c.q));
-          }
+        if constexpr (KS > 1) {
+          bf[b] = bpre[s][b];
+          sb[b] = spre[s][b];
+        } else {
+          bf[b] = read_b(s, b);
+          sb[b] = b_scale(s, b);
         }
       }
       // A scale words: with K-contiguous operands all of the step's up front
