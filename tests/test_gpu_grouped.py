@@ -183,3 +183,27 @@ def test_grouped_stream128_kernel(preshuffled):
     inn = np.concatenate([inn, np.tile(np.arange(N), len(edge))])
     ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
     H.assert_close(d[im, inn], ref, "grouped 128-row tiles")
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_many_groups_several_rounds(preshuffled):
+    """200 small groups (some empty): the persistent 64 x 64 kernel walks more
+    real tiles than it has workgroups (on 256 compute units three whole
+    rounds of 512 and a last round of 314 tiles, which do not split evenly
+    over the eight XCD bands).
+    Every row written, all entries against the oracle."""
+    from block_scaled_precision_03_amd import mxgemm
+    G, N, K = 200, 640, 256
+    rng = np.random.default_rng(100)
+    split = rng.integers(0, 41, G)
+    split[::17] = 0
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(960, split, N, K)
+    assert mxgemm.grouped_variant(G, totM, N, K) == mxgemm.GROUPED_STREAM64
+    real_tiles = int(sum((m + 63) // 64 for m in split)) * (N // 64)
+    P = min(((totM + 63) // 64 + G - 1) * (N // 64),
+            2 * torch.cuda.get_device_properties(0).multi_processor_count)
+    assert real_tiles // P >= 2 and (real_tiles % P) % 8 != 0
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped, 200 groups")
