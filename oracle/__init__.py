@@ -53,6 +53,8 @@ def lib():
         L.oracle_quant_group_weight.argtypes = [i, p, i64, i64, p, p]
         L.oracle_quant_group_act.restype = i
         L.oracle_quant_group_act.argtypes = [i, p, p, i64, i64, p, p]
+        L.oracle_quant_tensor.restype = i
+        L.oracle_quant_tensor.argtypes = [i, p, i64, p, p]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_bf16_rne.argtypes = [d]
         L.oracle_bf16_rne_array.restype = None
@@ -242,3 +244,15 @@ def quant_group_weight(w):
     if lib().oracle_quant_group_weight(G, _ptr(w), N, K, _ptr(codes), _ptr(ws)) != 0:
         raise ValueError("oracle_quant_group_weight: N or K not a multiple of 128")
     return codes, ws
+
+
+def quant_tensor(fmt, x):
+    """Tensor-wise E4M3 / E5M2: FP32 array -> (codes of the same shape,
+    FP32 dequant scale s = amax / fmt_max, 1.0 for an all-zero tensor);
+    codes = nearest(FP32 quotient x / s)."""
+    x = _c(x, np.float32)
+    codes = np.zeros(x.shape, np.uint8)
+    s = np.zeros(1, np.float32)
+    if lib().oracle_quant_tensor(fmt, _ptr(x), x.size, _ptr(codes), _ptr(s)) != 0:
+        raise ValueError("oracle_quant_tensor: format must be E4M3 or E5M2")
+    return codes, np.float32(s[0])

@@ -463,6 +463,30 @@ int oracle_quant_group_act(int G, const int64_t *m_sizes, const float *x, int64_
     return 0;
 }
 
+/* Tensor-wise FP8 (E4M3 or E5M2): one FP32 dequant scale for the whole
+ * tensor ("Experimental FlyDSL GEMM backend for TE PyTorch", Supported Data
+ * Types: tensor-wise FP8 with delayed scaling), taken from the current
+ * tensor: s = amax / fmt_max as an FP32 quotient (1.0 for an all-zero
+ * tensor), element code = nearest(FP32 quotient x / s), the same rule as the
+ * groupwise quantizers with the whole tensor as one block.  x: n FP32
+ * values; codes: n bytes. */
+int oracle_quant_tensor(int fmt, const float *x, int64_t n, uint8_t *codes, float *s_out)
+{
+    if (fmt != ORC_E4M3 && fmt != ORC_E5M2) return -1;
+    const float fmax = (float)orc_fmt_max(fmt);
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    volatile float s = amax / fmax;                     /* FP32 quotient */
+    const float sc = amax > 0.0f ? s : 1.0f;
+    *s_out = sc;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        volatile float q = x[i] / sc;                   /* FP32 quotient */
+        codes[i] = (uint8_t)orc_nearest(fmt, (double)q);
+    }
+    return 0;
+}
+
 /* Groupwise E4M3 weights: w FP32 [G, N, K], N % 128 == 0, K % 128 == 0; one
  * FP32 scale per 128 x 128 block, ws [G, N/128, K/128] row-major ("Add
  * FlyDSL grouped groupwise FP8 GEMM for ROCm", PR body: 128x128 weight

@@ -169,3 +169,35 @@ def test_quant_group_weight_equals_input_generator_and_bracket():
     blk = np.abs(w.reshape(3, 2, 128, 3, 128)).max(axis=(2, 4))
     want = np.where(blk > 0, (blk / np.float32(448.0)).astype(np.float32), np.float32(1.0))
     assert np.array_equal(ws, want)
+
+
+@pytest.mark.parametrize("elem,fmt", [("e4m3", oracle.E4M3), ("e5m2", oracle.E5M2)])
+def test_quant_tensor_equals_input_generator_and_torch_cast(elem, fmt):
+    """Tensor-wise scale s = amax / fmt_max (FP32 quotient); codes against
+    the input generator (independent code) and against torch's own float8
+    cast of the same FP32 quotient (clipped to +-fmt_max, since torch's cast
+    does not saturate)."""
+    x = synth.normal(81, (96, 384))
+    x[5] = 0.0
+    x[7, :50] *= np.float32(1e-12)
+    codes, s = oracle.quant_tensor(fmt, x)
+    c2, s2 = synth.quant_tensor(x, elem)
+    assert s == s2 and np.array_equal(codes, c2)
+    assert s == np.float32(np.float32(np.abs(x).max()) / np.float32(FMAX[fmt]))
+    dt = torch.float8_e4m3fn if fmt == oracle.E4M3 else torch.float8_e5m2
+    q = torch.from_numpy(x) / torch.tensor(s, dtype=torch.float32)
+    want = q.clamp(-FMAX[fmt], FMAX[fmt]).to(dt).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want)
+    # the largest element lands on +-fmt_max
+    i = np.unravel_index(np.abs(x).argmax(), x.shape)
+    assert abs(float(oracle.decode(fmt, np.array([codes[i]]))[0])) == FMAX[fmt]
+
+
+def test_quant_tensor_all_zero_and_single_value():
+    codes, s = oracle.quant_tensor(oracle.E4M3, np.zeros((4, 32), np.float32))
+    assert s == np.float32(1.0) and not codes.any()
+    x = np.zeros(64, np.float32)
+    x[9] = np.float32(-3.5)
+    codes, s = oracle.quant_tensor(oracle.E5M2, x)
+    assert s == np.float32(np.float32(3.5) / np.float32(57344.0))
+    assert codes[9] == (0x7B | 0x80) and codes.sum() == codes[9]
