@@ -367,8 +367,8 @@ def mx_backward_bench(torch, synth, mxgemm, dev):
 
 
 def quant_bench(torch, synth, mxgemm, dev):
-    """The on-device quantizers at the workloads' shapes: MX E4M3 of the
-    [16384, 4096] activation (E8M0 per 32), groupwise E4M3 of the grouped
+    """The on-device quantizers at the workloads' shapes: MX E4M3 and
+    tensor-wise E4M3 of the [16384, 4096] activation, groupwise E4M3 of the grouped
     GEMM's [16384, 7168] activation (G = 8, per-group block scales) and of its
     [8, 2048, 7168] weights (128 x 128 blocks).
     HBM-bound: algorithmic bytes = 4 per value read + 1 per code + scales."""
@@ -380,7 +380,14 @@ def quant_bench(torch, synth, mxgemm, dev):
     nbytes = 16384 * 4096 * 5 + 16384 * 128
     out.append({"name": "quantize_mx e4m3", "rows": 16384, "K": 4096, "us": us, "bytes": nbytes,
                 "gbs": nbytes / us / 1e3, "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
-    del x, codes, scales
+    # tensor-wise E4M3 of the same activation: the data is read twice (amax,
+    # then encode), but the algorithmic bytes count it once
+    tscale = torch.empty((1,), dtype=torch.float32, device=dev)
+    us = time_calls(torch, lambda: mxgemm.quantize_tensor(mxgemm.FP8_E4M3_TENSOR, x, codes, tscale, 16384 * 4096))
+    nbytes = 16384 * 4096 * 5 + 4
+    out.append({"name": "quantize_tensor e4m3", "rows": 16384, "K": 4096, "us": us, "bytes": nbytes,
+                "gbs": nbytes / us / 1e3, "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
+    del x, codes, scales, tscale
     totM, K = 16384, 7168
     ms = torch.from_numpy(synth.m_sizes_for(totM, 8, synth.seed_for(4, 4, 2))).to(dev)
     x = torch.from_numpy(synth.normal(synth.seed_for(4, 1, 2), (totM, K))).to(dev)

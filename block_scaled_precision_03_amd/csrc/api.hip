@@ -426,6 +426,34 @@ extern "C" int mxgemm_quantize_mx(int fmt, const float *x, void *codes, void *sc
   return launch_status();
 }
 
+extern "C" int mxgemm_quantize_tensor(int fmt, const float *x, void *codes, float *scale, int64_t n,
+                                      hipStream_t stream) {
+  const FmtInfo f = fmt_info(fmt);
+  if (!f.ok || f.mx || n < 0 || !scale) return MXG_ERR_INVALID_ARG;
+  if (n % 8 != 0) return MXG_ERR_UNSUPPORTED;
+  if (n > 0 && (!x || !codes)) return MXG_ERR_INVALID_ARG;
+  if ((n > 0 && (!aligned(x, 16) || !aligned(codes, 16))) || !aligned(scale, 4)) return MXG_ERR_MISALIGNED;
+  const int64_t n8 = n / 8;
+  const int64_t blocks = cdiv(n8, 256);
+  if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  uint32_t *word = (uint32_t *)scale;
+  uint8_t *c = (uint8_t *)codes;
+  hipLaunchKernelGGL(tensor_amax_clear_kernel, dim3(1), dim3(64), 0, stream, word);
+  if (n8 > 0) {
+    const unsigned amax_blocks = (unsigned)std::min<int64_t>(blocks, (int64_t)8 * cu_count());
+    hipLaunchKernelGGL(tensor_amax_kernel, dim3(amax_blocks), dim3(256), 0, stream, x, n8, word);
+    if (f.elem == F_E4M3)
+      hipLaunchKernelGGL((tensor_quant_kernel<F_E4M3>), dim3((unsigned)blocks), dim3(256), 0, stream, x, c,
+                         (const uint32_t *)word, n8);
+    else
+      hipLaunchKernelGGL((tensor_quant_kernel<F_E5M2>), dim3((unsigned)blocks), dim3(256), 0, stream, x, c,
+                         (const uint32_t *)word, n8);
+  }
+  if (f.elem == F_E4M3) hipLaunchKernelGGL((tensor_scale_kernel<F_E4M3>), dim3(1), dim3(64), 0, stream, word);
+  else hipLaunchKernelGGL((tensor_scale_kernel<F_E5M2>), dim3(1), dim3(64), 0, stream, word);
+  return launch_status();
+}
+
 static_assert(QG_MAX == MXG_GROUPED_MAX_G, "group table of the activation quantizer");
 
 extern "C" int grouped_fp8_quantize_act(int G, const int64_t *m_sizes, const float *x, void *codes,

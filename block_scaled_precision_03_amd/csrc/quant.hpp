@@ -19,8 +19,15 @@
 // 128x128 weight blocks) follow the activations' rule per 128 x 128 block,
 // scales [G, N/128, K/128] row-major.
 //
+// Tensor-wise ("Experimental FlyDSL GEMM backend for TE PyTorch", Supported
+// Data Types: tensor-wise FP8): one FP32 dequant scale for the whole tensor
+// from its own amax, s = amax / fmt_max as an FP32 quotient (1.0 for an
+// all-zero tensor), elements the FP32 quotient x / s rounded to the nearest
+// E4M3 or E5M2 code: the groupwise rule with the tensor as one block.
+//
 // All are HBM-bound streams: 4 bytes read per element, 1 (FP8) or 1/2
-// (FP4) written, plus the scales.
+// (FP4) written, plus the scales (the tensor-wise quantizer reads the data
+// twice: once for the amax, once to encode).
 #pragma once
 #include "common.hpp"
 
@@ -237,6 +244,65 @@ __global__ __launch_bounds__(256) void quant_group_weight_kernel(const float *__
                                        __fdiv_rn(v[i].w, s));
     *(uint32_t *)(codes + origin + row * K + 4 * chunk) = c;
   }
+}
+
+// Tensor-wise quantizer, four launches on one stream and no scratch: the
+// caller's scale word holds the amax (as FP32 bits, which order like
+// unsigned integers for non-negative values) until the last launch turns it
+// into the scale.
+__global__ void tensor_amax_clear_kernel(uint32_t *amax_bits) {
+  if (threadIdx.x == 0) amax_bits[threadIdx.x] = 0u;
+}
+
+// Grid-stride over groups of 8 values; block maximum by wave shuffles and
+// LDS, then one atomic maximum per block.
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const float *__restrict__ x, int64_t n8,
+                                                          uint32_t *amax_bits) {
+  __shared__ float wmax[4];
+  float m = 0.0f;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n8; t += (int64_t)gridDim.x * 256) {
+    const float4 u = ((const float4 *)x)[2 * t];
+    const float4 v = ((const float4 *)x)[2 * t + 1];
+    m = fmaxf(m, fmaxf(max4(fabsf(u.x), fabsf(u.y), fabsf(u.z), fabsf(u.w)),
+                       max4(fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(max4(wmax[0], wmax[1], wmax[2], wmax[3])));
+}
+
+template <int FMT>
+__device__ inline float tensor_scale(uint32_t amax_bits) {
+  constexpr float FMAX = FMT == F_E4M3 ? 448.0f : 57344.0f;
+  const float amax = __uint_as_float(amax_bits);
+  return amax > 0.0f ? __fdiv_rn(amax, FMAX) : 1.0f;
+}
+
+// One thread per 8 consecutive values.
+template <int FMT>
+__global__ __launch_bounds__(256) void tensor_quant_kernel(const float *__restrict__ x, uint8_t *__restrict__ codes,
+                                                           const uint32_t *__restrict__ amax_bits, int64_t n8) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;
+  const float s = tensor_scale<FMT>(*amax_bits);
+  const float4 u = ((const float4 *)x)[2 * t];
+  const float4 v = ((const float4 *)x)[2 * t + 1];
+  const float y[8] = {__fdiv_rn(u.x, s), __fdiv_rn(u.y, s), __fdiv_rn(u.z, s), __fdiv_rn(u.w, s),
+                      __fdiv_rn(v.x, s), __fdiv_rn(v.y, s), __fdiv_rn(v.z, s), __fdiv_rn(v.w, s)};
+  if constexpr (FMT == F_E4M3)
+    ((uint2 *)codes)[t] = make_uint2(encode4_e4m3_hw(y[0], y[1], y[2], y[3]), encode4_e4m3_hw(y[4], y[5], y[6], y[7]));
+  else
+    ((uint2 *)codes)[t] = make_uint2(encode4_e5m2_hw(y[0], y[1], y[2], y[3]), encode4_e5m2_hw(y[4], y[5], y[6], y[7]));
+}
+
+// The amax in the scale word becomes the scale (after every encoder thread
+// has read the amax: the launch follows the encoder on the stream).
+template <int FMT>
+__global__ void tensor_scale_kernel(uint32_t *scale_word) {
+  if (threadIdx.x == 0) scale_word[threadIdx.x] = __float_as_uint(tensor_scale<FMT>(scale_word[threadIdx.x]));
 }
 
 }  // namespace mxg

@@ -26,7 +26,7 @@ EXPORTS = (
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
-    "mxgemm_quantize_mx", "grouped_fp8_quantize_act", "grouped_fp8_quantize_weight",
+    "mxgemm_quantize_mx", "mxgemm_quantize_tensor", "grouped_fp8_quantize_act", "grouped_fp8_quantize_weight",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -63,6 +63,8 @@ _lib.grouped_fp8_preshuffle_b.restype = _i
 _lib.grouped_fp8_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
 _lib.mxgemm_quantize_mx.restype = _i
 _lib.mxgemm_quantize_mx.argtypes = [_i, _p, _p, _p, _i64, _i64, _p]
+_lib.mxgemm_quantize_tensor.restype = _i
+_lib.mxgemm_quantize_tensor.argtypes = [_i, _p, _p, _p, _i64, _p]
 _lib.grouped_fp8_quantize_weight.restype = _i
 _lib.grouped_fp8_quantize_weight.argtypes = [_i, _p, _p, _p, _i64, _i64, _p]
 _lib.grouped_fp8_quantize_act.restype = _i
@@ -170,6 +172,13 @@ def quantize_mx(fmt, x, codes, scales, rows, K, stream=None):
     """FP32 [rows, K] -> MX codes and E8M0 scales (see include/mxgemm.h)."""
     _check(_lib.mxgemm_quantize_mx(fmt, _ptr(x), _ptr(codes), _ptr(scales), rows, K, _stream(stream)),
            "mxgemm_quantize_mx")
+
+
+def quantize_tensor(fmt, x, codes, scale, n, stream=None):
+    """FP32 values -> tensor-wise FP8 codes and one FP32 dequant scale (see
+    include/mxgemm.h)."""
+    _check(_lib.mxgemm_quantize_tensor(fmt, _ptr(x), _ptr(codes), _ptr(scale), n, _stream(stream)),
+           "mxgemm_quantize_tensor")
 
 
 def grouped_quantize_act(G, m_sizes, x, codes, x_scale, totM, K, stream=None):

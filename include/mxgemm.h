@@ -223,6 +223,30 @@ int mxgemm_quantize_mx(int fmt, const float *x, void *codes, void *scales,
                        int64_t rows, int64_t K, hipStream_t stream);
 
 /*
+ * mxgemm_quantize_tensor -- FP32 data -> tensor-wise FP8 operand (codes +
+ * one FP32 dequant scale), the step that produces mxgemm_run's tensor-wise
+ * inputs ("Experimental FlyDSL GEMM backend for TE PyTorch", Supported Data
+ * Types: tensor-wise FP8, scales from the tensor's amax).
+ *
+ * fmt     MXG_FP8_E4M3_TENSOR or MXG_FP8_E5M2_TENSOR.
+ * x       device FP32, n values (any shape, flattened), 16-byte aligned.
+ * codes   device out: n bytes, 16-byte aligned.
+ * scale   device out: one FP32, 4-byte aligned: s = amax(|x|) / fmt_max
+ *         (448 or 57344) as an FP32 quotient, 1.0 when every value is zero
+ *         (and for n = 0); pass it as mxgemm_run's sA or sB.
+ * Element code = nearest representable value of the FP32 quotient x / s,
+ * ties to the even code, saturating at +-fmt_max.  Inputs must be finite.
+ * Four launches on `stream` (clear, amax, encode, scale); until the last
+ * one completes the scale word holds the amax bits, so calls that share a
+ * scale pointer must not overlap.  Nothing is allocated.
+ * Errors (before anything is enqueued): MXG_ERR_INVALID_ARG (not a
+ * tensor-wise fmt, n < 0, null pointer), MXG_ERR_UNSUPPORTED (n % 8 != 0,
+ * sizes past the 32-bit grid), MXG_ERR_MISALIGNED.
+ */
+int mxgemm_quantize_tensor(int fmt, const float *x, void *codes, float *scale, int64_t n,
+                           hipStream_t stream);
+
+/*
  * grouped_fp8_quantize_act -- FP32 activations -> the XQ and x_scale inputs
  * of grouped_fp8_gemm_run: E4M3 codes with one FP32 scale per row and
  * 128-value K block ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", PR

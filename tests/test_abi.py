@@ -109,6 +109,12 @@ def test_ops_reject_bad_args_before_device_use():
     assert lib.mxgemm_quantize_mx(0, P, P, P, 4, 48, None) == -2         # K % 32
     assert lib.mxgemm_quantize_mx(0, P + 4, P, P, 4, 32, None) == -3     # misaligned x
     assert lib.mxgemm_quantize_mx(0, P, P, P, 0, 32, None) == 0          # rows = 0: no-op
+    assert lib.mxgemm_quantize_tensor(0, P, P, P, 64, None) == -1       # MX fmt
+    assert lib.mxgemm_quantize_tensor(16, P, P, P, -8, None) == -1      # n < 0
+    assert lib.mxgemm_quantize_tensor(16, P, P, 0, 64, None) == -1      # null scale
+    assert lib.mxgemm_quantize_tensor(17, P, P, P, 60, None) == -2      # n % 8
+    assert lib.mxgemm_quantize_tensor(16, P + 4, P, P, 64, None) == -3  # misaligned x
+    assert lib.mxgemm_quantize_tensor(16, P, P, P + 2, 64, None) == -3  # misaligned scale
     assert lib.grouped_fp8_quantize_act(0, P, P, P, P, 128, 128, None) == -2    # G < 1
     assert lib.grouped_fp8_quantize_act(8, P, P, P, P, 128, 200, None) == -2    # K % 128
     assert lib.grouped_fp8_quantize_act(8, 0, P, P, P, 128, 128, None) == -1    # null m_sizes

@@ -6,7 +6,9 @@ Covered: every MX format, shapes from one block to full activation sizes,
 all-zero and tiny blocks, exact midpoints between neighbouring codes (ties
 to the even code), negative values rounding to zero, saturation; groupwise
 activations with uneven and empty groups, G = 1 and G = 1024, rows in no
-group left untouched, and the full grouped workload shapes."""
+group left untouched, and the full grouped workload shapes; tensor-wise
+E4M3 and E5M2 from 8 values to a full 8192 x 4096 tensor, ties, all-zero
+and empty tensors, and the tensor-wise GEMM fed by it."""
 import numpy as np
 import pytest
 import torch
@@ -198,3 +200,69 @@ def test_device_quantize_then_grouped_gemm():
     cw, sw = oracle.quant_group_weight(w)
     ref = oracle.grouped_gemm(m_sizes, cx, sx, cw, sw, totM, N, K)
     H.assert_close(H.bf16_to_f64(D), ref, "device quantize + grouped gemm")
+
+
+T4, T5 = 16, 17                      # tensor-wise E4M3 / E5M2 formats of the library
+TORC = {T4: oracle.E4M3, T5: oracle.E5M2}
+TMAX = {T4: 448.0, T5: 57344.0}
+
+
+def _quantize_tensor(fmt, x):
+    from block_scaled_precision_03_amd import mxgemm
+    n = x.size
+    codes = torch.full((max(n, 16),), 0xAB, dtype=torch.uint8, device=H.DEV)
+    scale = torch.full((4,), float("nan"), dtype=torch.float32, device=H.DEV)
+    mxgemm.quantize_tensor(fmt, H.dev(x.reshape(-1)) if n else codes, codes, scale, n)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy()[:n].reshape(x.shape), np.float32(scale[0].item()), codes.cpu().numpy()[n:]
+
+
+@pytest.mark.parametrize("fmt", [T4, T5])
+@pytest.mark.parametrize("shape", [(8,), (37, 96), (1000, 1024), (8192, 4096)])
+def test_quantize_tensor_bit_exact(fmt, shape):
+    x = synth.normal(930 + fmt + len(shape), shape)
+    flat = x.reshape(-1)
+    if flat.size >= 4096:
+        # one element at fmt_max makes s = 1, so exact midpoints between
+        # neighbouring codes can be planted directly (ties to the even code)
+        top = {T4: 0x7E, T5: 0x7B}[fmt]
+        vals = oracle.decode(TORC[fmt], np.arange(top + 1, dtype=np.uint8)).astype(np.float64)
+        mids = ((vals[:-1] + vals[1:]) / 2.0).astype(np.float32)
+        flat[:] = np.clip(flat, -TMAX[fmt] / 2, TMAX[fmt] / 2)
+        flat[0] = TMAX[fmt]
+        flat[1:1 + mids.size] = mids
+        flat[1 + mids.size:1 + 2 * mids.size] = -mids
+        flat[1 + 2 * mids.size:1 + 2 * mids.size + 64] = np.float32(-1e-30)   # round to -0
+    want_c, want_s = oracle.quant_tensor(TORC[fmt], x)
+    got_c, got_s, tail = _quantize_tensor(fmt, x)
+    assert got_s == want_s
+    assert np.array_equal(got_c, want_c)
+    assert np.all(tail == 0xAB)
+
+
+def test_quantize_tensor_zero_and_empty():
+    got_c, got_s, _ = _quantize_tensor(T4, np.zeros((16, 64), np.float32))
+    assert got_s == np.float32(1.0) and not got_c.any()
+    _, got_s, tail = _quantize_tensor(T5, np.zeros((0,), np.float32))
+    assert got_s == np.float32(1.0) and np.all(tail == 0xAB)
+
+
+def test_device_quantize_tensor_then_gemm():
+    """Tensor-wise path on the device: FP32 X (E4M3) and W (E5M2) ->
+    quantize_tensor -> mxgemm_run NT, bit for bit against the device GEMM on
+    the oracle's codes and scales, and within the bound against the
+    oracle's GEMM."""
+    M, N, K = 300, 272, 640
+    x = synth.normal(61, (M, K))
+    w = synth.normal(62, (N, K), 0.02)
+    qa, sa, _ = _quantize_tensor(T4, x)
+    qb, sb, _ = _quantize_tensor(T5, w)
+    ca, ea = oracle.quant_tensor(oracle.E4M3, x)
+    cb, eb = oracle.quant_tensor(oracle.E5M2, w)
+    assert sa == ea and sb == eb and np.array_equal(qa, ca) and np.array_equal(qb, cb)
+    D1 = H.run_dense(0, H.Operand(T4, qa, sa, False, M, K), H.Operand(T5, qb, sb, False, N, K), M, N, K)
+    D2 = H.run_dense(0, H.Operand(T4, ca, ea, False, M, K), H.Operand(T5, cb, eb, False, N, K), M, N, K)
+    assert np.array_equal(H.bits(D1), H.bits(D2))
+    ref = oracle.gemm((oracle.E4M3, oracle.SCALE_TENSOR, False, ca, ea), (oracle.E5M2, oracle.SCALE_TENSOR, False, cb, eb),
+                      M, N, K)
+    H.assert_close(H.bf16_to_f64(D1), ref, "device tensor-wise quantize + gemm")
