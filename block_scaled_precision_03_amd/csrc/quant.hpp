@@ -254,18 +254,28 @@ __global__ void tensor_amax_clear_kernel(uint32_t *amax_bits) {
   if (threadIdx.x == 0) amax_bits[threadIdx.x] = 0u;
 }
 
-// Grid-stride over groups of 8 values; block maximum by wave shuffles and
-// LDS, then one atomic maximum per block.
+// Grid-stride over groups of 8 values, four groups (eight 16-byte loads)
+// in flight per thread; block maximum by wave shuffles and LDS, then one
+// atomic maximum per block.
 __global__ __launch_bounds__(256) void tensor_amax_kernel(const float *__restrict__ x, int64_t n8,
                                                           uint32_t *amax_bits) {
   __shared__ float wmax[4];
+  const float4 *x4 = (const float4 *)x;
+  auto absmax = [](const float4 &u) { return max4(fabsf(u.x), fabsf(u.y), fabsf(u.z), fabsf(u.w)); };
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float m = 0.0f;
-  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n8; t += (int64_t)gridDim.x * 256) {
-    const float4 u = ((const float4 *)x)[2 * t];
-    const float4 v = ((const float4 *)x)[2 * t + 1];
-    m = fmaxf(m, fmaxf(max4(fabsf(u.x), fabsf(u.y), fabsf(u.z), fabsf(u.w)),
-                       max4(fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w))));
+  for (; t + 3 * stride < n8; t += 4 * stride) {
+    float4 u[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[2 * j] = x4[2 * (t + j * stride)];
+      u[2 * j + 1] = x4[2 * (t + j * stride) + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, absmax(u[j]));
   }
+  for (; t < n8; t += stride) m = fmaxf(m, fmaxf(absmax(x4[2 * t]), absmax(x4[2 * t + 1])));
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
