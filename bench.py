@@ -301,6 +301,22 @@ def time_calls(torch, call, reps=20, warmup=3):
     return a.elapsed_time(b) * 1000.0 / reps
 
 
+def small_bench(torch, synth, mxgemm, dev):
+    """MXFP8 NT 256 x 256 x 256 (one output tile, one workgroup): launch- and
+    latency-bound, so µs per call of back-to-back launches, not a fraction
+    of peak."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    M = N = K = 256
+    qa, sa = synth.quant_mx(synth.normal(synth.seed_for(1, 1), (M, K)), "e4m3")
+    qb, sb = synth.quant_mx(synth.normal(synth.seed_for(1, 2), (N, K)), "e4m3")
+    A, SA, B, SB = t(qa), t(sa), t(qb), t(sb)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = time_calls(torch, lambda: mxgemm.run(mxgemm.MXFP8_E4M3, mxgemm.MXFP8_E4M3, mxgemm.NT, A, SA, B, SB,
+                                              D, M, N, K), reps=200, warmup=20)
+    log("mxfp8 256^3: %.2f us per call (back-to-back launches)" % us)
+    return {"M": M, "N": N, "K": K, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}
+
+
 def tensorwise_bench(torch, synth, mxgemm, dev):
     """Tensor-wise FP8 (FP32 per-tensor scales) GEMMs of a 4096 -> 11008
     linear layer at 8192 tokens in its three layouts, each with both format
@@ -647,6 +663,7 @@ def main():
         log("grouped G=8 ...")
         result["grouped"] = grouped_bench(torch, synth, mxgemm, dev)
     if not args.only_step and not args.no_extra:
+        result["mxfp8_256"] = small_bench(torch, synth, mxgemm, dev)
         log("tensor-wise FP8 ...")
         result["tensorwise_fp8"] = tensorwise_bench(torch, synth, mxgemm, dev)
         log("MXFP8 backward layouts ...")
