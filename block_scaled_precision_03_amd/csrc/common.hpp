@@ -72,6 +72,18 @@ __device__ inline u32x4 sreg(const u32x4 &r) {
   return (u32x4){sreg(r.x), sreg(r.y), sreg(r.z), sreg(r.w)};
 }
 
+// Wait states inside the assembly blocks below.  A VALU instruction that
+// writes an SGPR (v_readfirstlane, or v_readlane when the compiler reloads a
+// spilled SGPR) needs five wait states before a vector-memory instruction
+// reads that SGPR as its resource or scalar offset (the gfx9 family's
+// manually inserted wait states).  The compiler counts them for the
+// vector-memory instructions it emits, but never for those inside inline
+// assembly, and it may put such a write directly before the block: a store
+// of the dense epilogue then used a stale scalar row offset whenever its
+// SGPR had just been reloaded from a spill, writing rows of D to the wrong
+// place in the transposed tensor-wise kernels of one build.  So every block
+// issues at least five wait states before its memory instruction.
+//
 // lds: LDS byte address of lane 0's destination, uniform; IMM is added to
 // it inside the instruction sequence so that call sites that differ only by
 // a constant share one base register.  The buffer range check covers the
@@ -81,10 +93,10 @@ template <int BYTES, int IMM = 0>
 __device__ inline void dma_asm(uint32_t lds, const u32x4 &r, uint32_t voff, uint32_t soff) {
   static_assert(BYTES == 4 || BYTES == 16, "DMA width");
   if constexpr (BYTES == 16)
-    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 3\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  ::"s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(soff)), "i"(IMM) : "memory", "m0", "scc");
   else
-    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 3\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  ::"s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(soff)), "i"(IMM) : "memory", "m0", "scc");
 }
 
@@ -98,21 +110,23 @@ __device__ inline void dma_asm_v(uint32_t lds, const u32x4 &r, uint32_t voff, ui
   static_assert(BYTES == 4 || BYTES == 16, "DMA width");
   uint32_t t;
   if constexpr (BYTES == 16)
-    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %4, %2\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
+    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %4, %2\n\ts_nop 2\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
                  : "=&v"(t) : "s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(add)), "i"(IMM) : "memory", "m0", "scc");
   else
-    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %4, %2\n\tbuffer_load_dword %0, %3, 0 offen lds"
+    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %4, %2\n\ts_nop 2\n\tbuffer_load_dword %0, %3, 0 offen lds"
                  : "=&v"(t) : "s"(sreg(lds)), "v"(voff), "s"(sreg(r)), "s"(sreg(add)), "i"(IMM) : "memory", "m0", "scc");
 }
 
-// A 16-byte buffer store (D[voff + soff] = v) and three wait states in one
-// assembly block.  The store reads its data VGPRs after it issues; a VALU
-// write of those VGPRs in the next two cycles corrupts what is stored.  The
-// compiler's hazard checks assume no such hazard when soffset is an SGPR,
-// which does not hold on gfx950 (seen as a wrong last dword in lanes 12-15
-// of each row of 16 lanes), so the wait is part of the store itself.
+// A 16-byte buffer store (D[voff + soff] = v) with wait states on both
+// sides in one assembly block.  Before it: five, for an SGPR operand just
+// written by a VALU instruction (see above).  After it: three, because the
+// store reads its data VGPRs after it issues and a VALU write of those VGPRs
+// in the next two cycles corrupts what is stored; the compiler's hazard
+// checks assume no such hazard when soffset is an SGPR, which does not hold
+// on gfx950 (seen as a wrong last dword in lanes 12-15 of each row of 16
+// lanes).
 __device__ inline void store16_asm(const v4i &v, const u32x4 &r, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 2"
+  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 2"
                ::"v"(v), "v"(voff), "s"(sreg(r)), "s"(sreg(soff)) : "memory");
 }
 
@@ -147,16 +161,13 @@ __device__ inline v4f mfma_scaled(const v8i &x, const v8i &y, const v4f &c, int 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, sx, 0, sy);
 }
 
-// FP32 -> BF16 bits, round to nearest even; NaN -> quiet NaN.
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// Two FP32 values -> packed BF16 (lo in bits 0-15), rounded to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950 (the compiler's lowering of the
+// vector conversion).  A NaN stays a NaN (its payload is not specified).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 __device__ inline uint32_t lds_load_u32(const void *p) { return *(const lds_u32_t *)p; }

@@ -489,8 +489,12 @@ struct DenseLoop {
     e.voff = (uint32_t)(2 * ((c.wm * (FM * 16) + i) * p.N + c.wn * (FN * 16) + 16 * (q & 1) + 8 * (q >> 1)));
   }
 
-  __device__ static inline void store_rows(const Ctx &c, const Epi &e, int a, const v4f (&row)[FN]) {
+  __device__ static inline void store_rows(const Ctx &c, const Epi &e, int a, const v4f (&row_in)[FN]) {
     const float al = e.alpha;
+    // alpha is 1 for MX operands: no multiply
+    v4f row[FN];
+#pragma unroll
+    for (int b = 0; b < FN; ++b) row[b] = MX ? row_in[b] : row_in[b] * al;
     if (e.full) {
       // computed here, not hoisted into a register per row tile
       uint32_t rs = e.rowstride;
@@ -501,8 +505,8 @@ struct DenseLoop {
 #pragma unroll
       for (int pr = 0; pr < FN / 2; ++pr) {
         const v4f x = row[2 * pr], y = row[2 * pr + 1];
-        const uint32_t xlo = pack_bf16x2(x.x * al, x.y * al), xhi = pack_bf16x2(x.z * al, x.w * al);
-        const uint32_t ylo = pack_bf16x2(y.x * al, y.y * al), yhi = pack_bf16x2(y.z * al, y.w * al);
+        const uint32_t xlo = pack_bf16x2(x.x, x.y), xhi = pack_bf16x2(x.z, x.w);
+        const uint32_t ylo = pack_bf16x2(y.x, y.y), yhi = pack_bf16x2(y.z, y.w);
         // q even keeps its tile-2p chunk and takes the partner's; q odd the
         // same with tile 2p+1
         const uint32_t rlo = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)(odd ? xlo : ylo));
@@ -521,7 +525,7 @@ struct DenseLoop {
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
           const v4f v = row[b];
-          const uint32_t u[2] = {pack_bf16x2(v.x * al, v.y * al), pack_bf16x2(v.z * al, v.w * al)};
+          const uint32_t u[2] = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
           const int64_t col = (int64_t)e.n0 + c.wn * (FN * 16) + b * 16 + 4 * q;
 #pragma unroll
           for (int k = 0; k < 4; ++k)
