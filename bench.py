@@ -688,9 +688,17 @@ def main():
         if par is not None:
             log("step result vs oracle, rows 0..%d: worst ratio %.3g, %s"
                 % (par["rows"], par["worst_ratio"], "pass" if par["pass"] else "FAIL"))
+            if not par["pass"]:
+                # a wrong result has no throughput: the line says so and the
+                # process fails
+                result["parity_failed"] = True
+                result["value_if_valid"] = result["value"]
+                result["value"] = None
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    if result.get("parity_failed"):
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -1,6 +1,6 @@
 // C ABI of the gfx950 block-scaled GEMM library: argument validation, tile
 // and grid selection from static shapes, and kernel launch.  The host never
-// reads device memory; every call enqueues exactly one kernel on the caller's
+// reads device memory; every call enqueues one kernel on the caller's
 // stream or returns an error before enqueueing anything.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,6 +42,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 constexpr int64_t MAX_ROW_BYTES = 1ll << 22;   // bytes of K per row (256 rows < 2^30)
 constexpr int64_t MAX_DIM = 1ll << 31;
 constexpr int64_t MAX_T_BYTES = 0x7FFFFFF0ll;   // a transposed operand, whole
+constexpr int64_t MAX_PSB_BYTES = (1ll << 32) - (1ll << 16);   // a preshuffled B, whole
 
 int launch_status() {
   const hipError_t e = hipGetLastError();
@@ -123,6 +124,10 @@ extern "C" int mxgemm_validate(int fmtA, int fmtB, int layout, const void *A, co
   if ((layout == MXG_TN || layout == MXG_NN) && (N % 16 != 0 || N * K >= MAX_T_BYTES))
     return MXG_ERR_UNSUPPORTED;
   if (fa.mx && (M * (K / 32) >= (1ll << 31) || cdiv(N, 64) * 64 * (K / 32) >= (1ll << 31)))
+    return MXG_ERR_UNSUPPORTED;
+  // A preshuffled B is addressed from its start with one 32-bit offset per
+  // DMA (column group, K step and lane); it must stay below 2^32.
+  if (psb && mxgemm_preshuffle_b_bytes(fmtB & ~MXG_PRESHUFFLED, N, K) > MAX_PSB_BYTES)
     return MXG_ERR_UNSUPPORTED;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, fa.mx ? 16 : 4) || !aligned(sB, fb.mx ? 16 : 4))
     return MXG_ERR_MISALIGNED;

@@ -481,7 +481,11 @@ struct DenseLoop {
     e.n0 = (int)n0;
     e.alpha = alpha;
     e.on = on;
-    e.full = m0 + DBM <= p.M && n0 + DBN <= p.N && (p.N & 7) == 0 && p.N < (1 << 23);
+    // Full tiles store through the range-checked vector offset (at most
+    // 2 (255 N + 255) bytes from the tile's origin), which must stay below
+    // the resource's clamped size of 2^31 - 16 bytes; wider D takes the
+    // element-wise path.
+    e.full = m0 + DBM <= p.M && n0 + DBN <= p.N && (p.N & 7) == 0 && p.N <= (1 << 22);
     const int64_t org = m0 * p.N + n0;
     e.rd = rsrc4(p.D + org, clamp_records(2 * (p.M * p.N - org)));
     e.rowstride = (uint32_t)(32 * p.N);

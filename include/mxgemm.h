@@ -26,7 +26,9 @@
  *  - All data pointers are DEVICE pointers owned by the caller.  The library
  *    never allocates, frees or retains caller memory and uses no workspace.
  *  - Calls are stream-ordered and asynchronous: exactly one kernel is
- *    enqueued on `stream` (0 = the null stream) per successful call.
+ *    enqueued on `stream` (0 = the null stream) per successful call, with
+ *    one exception, mxgemm_quantize_tensor, which enqueues four (its scale
+ *    output serves as the amax word between them; see there).
  *  - All argument checks are synchronous and happen before anything is
  *    enqueued; on error nothing is enqueued and outputs are untouched.
  *  - No C++ exception crosses this ABI.  Returns MXG_OK (0) or a negative
@@ -79,12 +81,21 @@ enum { MXG_NT = 0, MXG_NN = 1, MXG_TN = 2 };
 #define MXG_GROUPED_MAX_G 1024
 
 /*
- * mxgemm_init -- load the library's code objects on the current device.
- * Call once per device before capturing calls into a HIP graph.  Idempotent.
+ * mxgemm_init -- load the library's code objects on the current device and
+ * query its compute-unit count once, so that later calls read no device
+ * state and can be captured into a HIP graph ("Add FlyDSL grouped groupwise
+ * FP8 GEMM for ROCm", Tile selection: a captured call must not depend on
+ * anything a capture cannot replay).  Call once per device before capture.
+ * Idempotent.  Returns MXG_OK, or MXG_ERR_HIP if no device is usable.
  */
 int mxgemm_init(void);
 
-/* Static description of a status code; never freed. */
+/* Static description of a status code ("ok", "invalid argument", ...);
+ * never freed, never NULL ("unknown status" for a code not listed above).
+ * The pages' wrappers report unsupported configurations rather than
+ * failing silently ("Experimental FlyDSL GEMM backend for TE PyTorch",
+ * Summary: unsupported configs fall back); this library has no fallback and
+ * names the reason instead. */
 const char *mxgemm_status_string(int status);
 
 /*
@@ -105,7 +116,8 @@ const char *mxgemm_status_string(int status);
  * Divisibility: MX needs K % 128 == 0 (E2M1: K % 256 == 0); NN/TN need the
  *             contiguous dimension of each transposed operand (M for A 'T',
  *             N for B 'N') to be a multiple of 16, and each transposed
- *             operand to hold fewer than 2^31 - 16 bytes.  Otherwise
+ *             operand to hold fewer than 2^31 - 16 bytes, and a
+ *             preshuffled B to hold fewer than 2^32 - 2^16 bytes.  Otherwise
  *             MXG_ERR_UNSUPPORTED.  A, B, sA, sB and D must be 16-byte
  *             aligned (MXG_ERR_MISALIGNED).
  * Edge rows/columns (M, N not multiples of the tile) are masked.
@@ -122,7 +134,14 @@ int mxgemm_validate(int fmtA, int fmtB, int layout,
 
 /*
  * grouped_fp8_gemm_run -- grouped groupwise FP8 GEMM (one GEMM per group of
- * rows, e.g. per expert).
+ * rows, e.g. per expert): "Add FlyDSL grouped groupwise FP8 GEMM for ROCm"
+ * (PR body: E4M3 X and W with FP32 1x128 activation and 128x128 weight
+ * scales, plain or preshuffled [G,N,K] weights, BF16 out; commit message
+ * fixing the scale_a addressing: the per-group block layout of x_scale;
+ * Tile selection: the grid comes from static shapes only and m_sizes is
+ * resolved in the kernel; Architecture support: the scaled matrix-core
+ * instruction with a neutral E8M0 scale and the FP32 scales applied in
+ * software per 128-K block).
  *
  * G           number of groups, 1 <= G <= MXG_GROUPED_MAX_G.
  * m_sizes     device int64[G]: rows per group, in order.  Group g owns rows
@@ -186,7 +205,13 @@ int mxgemm_preshuffle_b(int fmtB, int layout, const void *B, void *B_out,
  * mxgemm_preshuffle_scales: E8M0 scales [rows, K/32] -> s_out of
  * mxgemm_preshuffle_scales_bytes(rows, K) bytes, in per-lane order (one
  * 32-bit word per lane covers four consecutive 128-K steps).  Padding is
- * filled with 127 (scale 1).
+ * filled with 127 (scale 1).  "[gfx1250] Add MXFP4 GEMM support to FlyDSL
+ * backend" (Description: callers pass plain scales and the library reorders
+ * them once so that the K loop reads them in iteration order).
+ * s: device uint8 [rows, K/32], 4-byte aligned; s_out: device, 16-byte
+ * aligned, caller-allocated.  Errors: MXG_ERR_INVALID_ARG (negative size,
+ * null pointer), MXG_ERR_UNSUPPORTED (K % 32 != 0), MXG_ERR_MISALIGNED.
+ * rows or K = 0: no-op.
  */
 int64_t mxgemm_preshuffle_scales_bytes(int64_t rows, int64_t K);
 int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K,

@@ -66,6 +66,14 @@ P = 1 << 20       # a fake, 16-byte aligned address (never dereferenced)
     ((16, 17, 1, P, P, P, P, P, 256, 208, 256), 0),
     ((16, 16, 0, P, P + 4, P, P + 4, P, 256, 256, 256), 0),  # tensor scales 4-aligned
     ((0, 0x100, 1, P, P, P, P, P, 256, 256, 256), -2),      # preshuffled B only NT
+    # a preshuffled B of 2^32 bytes or more does not fit the kernel's 32-bit
+    # offsets: 262144 x 16384 E4M3 is exactly 2^32 bytes, 131072 x 16384 half
+    ((0, 0x100, 0, P, P, P, P, P, 256, 262144, 16384), -2),
+    ((16, 0x110, 0, P, P, P, P, P, 256, 262144, 16384), -2),
+    ((0, 0x100, 0, P, P, P, P, P, 256, 131072, 16384), 0),
+    ((4, 0x104, 0, P, P, P, P, P, 256, 262144, 16384), 0),   # FP4: half the bytes
+    ((4, 0x104, 0, P, P, P, P, P, 256, 262144, 32768), -2),
+    ((0, 0, 0, P, P, P, P, P, 256, 262144, 16384), 0),        # plain B is rebased per tile
 ])
 def test_validate(args, expect):
     m = _mx()

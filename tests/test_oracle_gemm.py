@@ -77,8 +77,8 @@ for fa, fb in [(oracle.E4M3, oracle.E4M3), (oracle.E4M3, oracle.E5M2), (oracle.E
         if fa == oracle.E2M1 and sk == oracle.SCALE_TENSOR:
             continue
         for ta, tb in [(0, 0), (0, 1), (1, 1)]:     # NT, NN, TN in row-major naming
-            if fa == oracle.E2M1 and (ta or tb):
-                continue    # packed E2M1 is stored K-contiguous only
+            # a transposed E2M1 operand [K, rows] packs two rows per byte
+            # along its contiguous dimension (row 2j in the low nibble)
             CASES.append((fa, fb, sk, ta, tb))
 
 
@@ -86,7 +86,7 @@ for fa, fb in [(oracle.E4M3, oracle.E4M3), (oracle.E4M3, oracle.E5M2), (oracle.E
 @pytest.mark.parametrize("K", [32, 128, 256])
 def test_exact_rational_brute_force(fa, fb, sk, ta, tb, K):
     rng = np.random.default_rng(hash((fa, fb, sk, ta, tb, K)) % (2 ** 32))
-    M, N = 3, 4
+    M, N = (4, 6) if fa == oracle.E2M1 and ta else (3, 4)
     opA, a = _make_operand(rng, fa, sk, M, K, ta)
     opB, b = _make_operand(rng, fb, sk, N, K, tb)
     D = oracle.gemm(opA, opB, M, N, K)
@@ -117,6 +117,8 @@ def test_exact_when_representable(fmt):
 def test_matches_numpy_matmul(fa, fb, sk, ta, tb):
     rng = np.random.default_rng(11)
     M, N, K = 37, 29, 192
+    if fa == oracle.E2M1:
+        M, N = M + ta, N + tb          # even row counts when packed along rows
     opA, a = _make_operand(rng, fa, sk, M, K, ta)
     opB, b = _make_operand(rng, fb, sk, N, K, tb)
     D = oracle.gemm(opA, opB, M, N, K)
@@ -222,6 +224,33 @@ def test_layouts_equivalent():
     nn = oracle.gemm((0, 1, 0, A, sA), (0, 1, 1, B.T.copy(), sB), M, N, K)
     tn = oracle.gemm((0, 1, 1, A.T.copy(), sA), (0, 1, 1, B.T.copy(), sB), M, N, K)
     assert np.array_equal(nt, nn) and np.array_equal(nt, tn)
+
+
+def test_fp4_transposed_nibble_order():
+    """A transposed E2M1 operand [K, rows] packs rows 2j (low nibble) and
+    2j + 1 (high nibble) of one k in a byte: A^T[0, 0] = 0x72 puts 1.0 in
+    row 0 and 6.0 in row 1 at k = 0; B = 1.0 at k = 0 gives D = [1, 6]^T.
+    With A^T[1, 0] = 0x40 (code 4 = 2.0 in row 1 at k = 1) and B = 1.0 at
+    k = 1 as well, row 1 becomes 6 + 2 = 8."""
+    K = 32
+    s1 = np.full((2, K // 32), 127, np.uint8)
+    sb = np.full((1, K // 32), 127, np.uint8)
+    At = np.zeros((K, 1), np.uint8)
+    At[0, 0] = 0x72
+    B = np.zeros((1, K // 2), np.uint8)
+    B[0, 0] = 0x02
+    D = oracle.gemm((oracle.E2M1, 0, 1, At, s1), (oracle.E2M1, 0, 0, B, sb), 2, 1, K)
+    assert D.tolist() == [[1.0], [6.0]]
+    At[1, 0] = 0x40
+    B[0, 0] = 0x22
+    D = oracle.gemm((oracle.E2M1, 0, 1, At, s1), (oracle.E2M1, 0, 0, B, sb), 2, 1, K)
+    assert D.tolist() == [[1.0], [8.0]]
+    # the same operand stored K-contiguous, packed along k, gives the same D
+    A = np.zeros((2, K // 2), np.uint8)
+    A[0, 0] = 0x02                                  # row 0: 1.0 at k = 0
+    A[1, 0] = 0x47                                  # row 1: 6.0 at k = 0, 2.0 at k = 1
+    D2 = oracle.gemm((oracle.E2M1, 0, 0, A, s1), (oracle.E2M1, 0, 0, B, sb), 2, 1, K)
+    assert np.array_equal(D, D2)
 
 
 def test_fp4_nibble_order():
