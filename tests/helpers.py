@@ -130,3 +130,24 @@ def sample_indices(rng, M, N, count):
         im.append(m)
         inn.append(N - 1)
     return np.array(im, np.int64), np.array(inn, np.int64)
+
+
+def int_operand(rng, fmt, rows, K, transposed=False, mx=True):
+    """Codes of small integers {-2..2} and power-of-two scales 1, 2 or 4
+    (tensor-wise: s = 2).  With such inputs every partial sum of a GEMM is an
+    integer far below 2^24, exact in FP32 in any order, so a kernel's BF16
+    output must equal the oracle's exact result rounded once, bit for bit.
+    A transposed E2M1 operand [K, rows] is packed two rows per byte."""
+    table = {0: [0xC0, 0xB8, 0x00, 0x38, 0x40], 1: [0xC0, 0xBC, 0x00, 0x3C, 0x40],
+             4: [0xC, 0xA, 0x0, 0x2, 0x4]}
+    base = 0 if fmt in (0, 16) else (1 if fmt in (1, 17) else 4)
+    codes = np.array(table[base], np.uint8)[rng.integers(0, 5, (rows, K))]
+    if transposed:
+        codes = np.ascontiguousarray(codes.T)
+    if base == 4:
+        codes = synth.pack_e2m1(codes)
+    if mx:
+        s = rng.integers(127, 130, (rows, K // 32)).astype(np.uint8)
+    else:
+        s = np.float32(2.0)
+    return Operand(fmt, codes, s, transposed, rows, K)

@@ -96,21 +96,7 @@ def test_exhaustive_code_pairs_bit_exact(fa, fb):
     assert np.array_equal(H.bits(D), oracle.bf16_rne(ref))
 
 
-def _int_operand(rng, fmt, rows, K, transposed=False, mx=True):
-    """Codes of small integers {-2..2} and power-of-two scales 1, 2 or 4."""
-    table = {E4: [0xC0, 0xB8, 0x00, 0x38, 0x40], E5: [0xC0, 0xBC, 0x00, 0x3C, 0x40],
-             F4: [0xC, 0xA, 0x0, 0x2, 0x4]}
-    base = E4 if fmt in (E4, T4) else (E5 if fmt in (E5, T5) else F4)
-    codes = np.array(table[base], np.uint8)[rng.integers(0, 5, (rows, K))]
-    if base == F4:
-        codes = synth.pack_e2m1(codes)
-    if mx:
-        s = rng.integers(127, 130, (rows, K // 32)).astype(np.uint8)
-    else:
-        s = np.float32(2.0)
-    if transposed:
-        codes = np.ascontiguousarray(codes.T)
-    return H.Operand(fmt, codes, s, transposed, rows, K)
+_int_operand = H.int_operand
 
 
 @pytest.mark.parametrize("fa,fb,M,N,K", [(E4, E4, 520, 300, 1024), (E5, E4, 256, 512, 2048),
