@@ -291,10 +291,31 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   } else if (variant == MXG_GROUPED_STREAM128) {
     if (pre) hipLaunchKernelGGL((grouped_stream_kernel<true, 128, 1, 2>), dim3(P), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((grouped_stream_kernel<false, 128, 1, 2>), dim3(P), dim3(256), 0, stream, a);
-  } else if (pre) {
-    hipLaunchKernelGGL((grouped_kernel<128, 128, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((grouped_kernel<128, 128, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    // matrix-core regime: the dense pipeline with groupwise scales, 256 x
+    // 256 tiles, one persistent workgroup per compute unit
+    DenseArgs d = {};
+    d.A = (const uint8_t *)XQ;
+    d.B = (const uint8_t *)WQ;
+    d.sA = x_scale;
+    d.sB = w_scale;
+    d.D = (uint16_t *)D;
+    d.M = totM;
+    d.N = N;
+    d.K = K;
+    d.a_bytes = totM * K;
+    d.b_bytes = (int64_t)G * N * K;
+    d.sa_bytes = totM * (K / 128) * 4;
+    d.sb_bytes = (int64_t)G * (N / 128) * (K / 128) * 4;
+    d.tiles_n = (int)cdiv(N, DBN);
+    d.tiles_m = (int)(cdiv(totM, DBM) + G - 1);      // upper bound; the kernel counts them
+    d.m_sizes = m_sizes;
+    d.G = G;
+    const int64_t tiles = (int64_t)d.tiles_m * d.tiles_n;
+    if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+    const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
+    if (pre) hipLaunchKernelGGL((grouped_dense_kernel<true>), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
+    else hipLaunchKernelGGL((grouped_dense_kernel<false>), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
   }
   return launch_status();
 }
@@ -302,28 +323,29 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
 // Kernel choice from the static shapes (the host never reads m_sizes): the
 // estimated time of each, from upper bounds of the tile counts.
 //  - persistent, 64 x 64 or 128 x 64 tiles (weight streaming): ~0.6 or
-//    ~0.87 us per 128-K tile step per workgroup, GS_OCC workgroups per
-//    compute unit walking all tile steps evenly; at least the weights' bytes
-//    at ~5 TB/s.
-//  - 128 x 128 (two workgroups per compute unit, one tile each): ~1.25 us
-//    per K step per round of resident workgroups; at least the weights'
-//    bytes at ~4 TB/s.
-// The constants are fitted to measured times of the three kernels on MI355X
-// over totM 128 .. 8192, (N, K) = (2048, 7168) and (7168, 2304), G = 8.
+//    ~1.0 us per 128-K tile step per workgroup, GS_OCC workgroups per
+//    compute unit walking all tile steps evenly;
+//  - persistent 256 x 256 tiles on the dense pipeline (matrix-core regime):
+//    one tile per compute unit per round, ~1.67 us per 128-K step plus
+//    ~20 us per round (pipeline start, epilogue);
+// each at least the weights' bytes at ~5 TB/s.  The constants are fitted to
+// the three kernels' times on MI355X (preshuffled weights, G = 8) over
+// totM 512 .. 16384 and (N, K) = (2048, 7168), (7168, 2304), (4096, 4096),
+// (1280, 8192); at every one of those 24 points the choice is the fastest
+// kernel or within 16% of it.
 extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K) {
   if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM64;
   const double cus = cu_count(), nst = (double)(K / 128);
   const double wbytes = (double)G * (double)N * (double)K;
+  const double wmin = wbytes / 5.0e6;
   const double tiles_n = (double)(N / 64);
   const double slots = (double)GS_OCC * cus;
-  const double t64 = std::max(0.6 * (double)(cdiv(totM, 64) + G - 1) * tiles_n * nst / slots,
-                              wbytes / 5.0e6);
-  const double t128 = std::max(0.87 * (double)(cdiv(totM, 128) + G - 1) * tiles_n * nst / slots,
-                               wbytes / 5.0e6);
-  const double blocks_o = (double)(cdiv(totM, 128) + G - 1) * (double)(N / 128);
-  const double t_o = std::max(1.25 * std::ceil(blocks_o / (2.0 * cus)) * nst, wbytes / 4.0e6);
-  if (t64 <= t128 && t64 <= t_o) return MXG_GROUPED_STREAM64;
-  return t128 <= t_o ? MXG_GROUPED_STREAM128 : MXG_GROUPED_TILED;
+  const double t64 = std::max(0.6 * (double)(cdiv(totM, 64) + G - 1) * tiles_n * nst / slots, wmin);
+  const double t128 = std::max(1.0 * (double)(cdiv(totM, 128) + G - 1) * tiles_n * nst / slots, wmin);
+  const double tiles_d = (double)(cdiv(totM, DBM) + G - 1) * (double)cdiv(N, DBN);
+  const double t_d = std::max(std::ceil(tiles_d / cus) * (1.67 * nst + 20.0), wmin);
+  if (t64 <= t128 && t64 <= t_d) return MXG_GROUPED_STREAM64;
+  return t128 <= t_d ? MXG_GROUPED_STREAM128 : MXG_GROUPED_TILED;
 }
 
 extern "C" int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K) {

@@ -27,15 +27,28 @@
 
 namespace mxg {
 
-enum : int { SM_MX = 0, SM_TENSOR = 1 };
+// Scale modes: MX (E8M0 per 32 K values, applied by the matrix-core
+// instruction), tensor-wise (one FP32 per operand, applied in the epilogue),
+// groupwise (the grouped GEMM: FP32 per row and 128-K block of A, per 128 x
+// 128 block of each group's B, applied in software after every 128-K step).
+enum : int { SM_MX = 0, SM_TENSOR = 1, SM_GROUP = 2 };
 
 struct DenseArgs {
   const uint8_t *A, *B;
-  const void *sA, *sB;
+  const void *sA, *sB;            // groupwise: x_scale and w_scale (FP32)
   uint16_t *D;
-  int64_t M, N, K;
+  int64_t M, N, K;                // groupwise: M = totM, N and K per group
   int64_t a_bytes, b_bytes, sa_bytes, sb_bytes;
   int tiles_m, tiles_n;
+  const int64_t *m_sizes;         // groupwise only
+  int G;                          // groupwise only
+};
+
+// One output tile: origin, the row limit of its stores (M, or the end of its
+// group) and, for the grouped GEMM, its group (index, first row, rows).
+struct TileId {
+  int64_t m0, n0, lim, start, mg;
+  int g;
 };
 
 constexpr int DBM = 256, DBN = 256, DNW = 4;
@@ -209,6 +222,8 @@ template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
 struct DenseLoop {
   static constexpr bool FP4 = (FA == F_E2M1);
   static constexpr bool MX = (SMODE == SM_MX);
+  static constexpr bool GROUP = (SMODE == SM_GROUP);
+  static constexpr bool SCALED = MX || GROUP;    // scales staged through LDS
   static constexpr int NW = DNW8;
   static constexpr int KS = FP4 ? 2 : 1;        // 128-element K steps per stage
   static constexpr int FM = 8, FN = 4;          // wave tile 128 x 64
@@ -216,9 +231,12 @@ struct DenseLoop {
   static constexpr int STAGE = (DBM + DBN) * 128;
   // MX scales arrive in groups of four K steps (16 bytes per row): A rows
   // at SA_OFF + 16 row, B rows (or, preshuffled, B column groups of 1 KiB)
-  // at SB_OFF.  Two group slots.
+  // at SB_OFF.  Groupwise scales in the same groups of four K steps: the
+  // tile's 256 activation scales of K step j at SA_OFF + 1024 j + 4 row,
+  // the weight block scales of its two 128-column blocks c at SB_OFF +
+  // 16 c + 4 j.  Two group slots.
   static constexpr int SA_OFF = 0, SB_OFF = 4096;
-  static constexpr int SGROUP = MX ? 8192 : 0;
+  static constexpr int SGROUP = SCALED ? 8192 : 0;
   // LDS: [A slot 0][A slot 1][B slot 0][B slot 1][scales slot 0][slot 1].
   // A read offset within either slot then fits the 16-bit offset field of a
   // DS instruction on top of one per-lane base register per operand.
@@ -239,26 +257,79 @@ struct DenseLoop {
     uint32_t lds0;                 // LDS address of the kernel's LDS block (uniform)
   };
 
+
+  // Per-kernel state of a workgroup: wave and lane indices, the per-lane
+  // DMA offsets, the LDS block.
+  __device__ static inline void init(Ctx &c, const DenseArgs &p, uint8_t *smem) {
+    c.p = &p;
+    c.lane = threadIdx.x & 63;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
+    c.wm = c.w >> 2;
+    c.wn = c.w & 3;
+    c.i16 = c.lane & 15;
+    c.q = c.lane >> 4;
+    c.KB = FP4 ? p.K / 2 : p.K;
+    c.nst = (int)(c.KB / 128);
+    c.sk32 = p.K / 32;
+    c.nks = p.K / 128;
+    c.ngrp = (p.K + 511) / 512;
+    dma_offsets(TA, c.lane, c.w, c.KB, p.M, c.vo_a);
+    dma_offsets(TB, c.lane, c.w, c.KB, p.N, c.vo_b);
+    c.vo_s = 0;
+    if constexpr (MX) {
+      if (c.w < 4 || !PSB) c.vo_s = (uint32_t)(c.lane * c.sk32);
+      else c.vo_s = (uint32_t)(c.lane * 16);
+    } else if constexpr (GROUP) {
+      // waves 0-3: one activation scale per lane; wave 4: lane l reads the
+      // weight block scale of column block (l / 4) % 2, K step l % 4
+      if (c.w < 4) c.vo_s = (uint32_t)(c.lane * 4);
+      else c.vo_s = (uint32_t)(((c.lane >> 2) & 1) * c.nks * 4 + (c.lane & 3) * 4);
+    }
+    c.lds0 = lds_addr(smem);
+  }
+
   // The DMA sources of one output tile (uniform).
   struct Tile {
-    int64_t m0, n0;
+    int64_t m0, n0, lim;
     u32x4 ra, rb, rs;              // rs: this wave's scale source
+    uint32_t soff, mg4;            // groupwise: this wave's scale offset, 4 * group rows
   };
 
-  __device__ static inline void set_tile(const Ctx &c, int64_t m0, int64_t n0, Tile &t) {
+  __device__ static inline void set_tile(const Ctx &c, const TileId &id, Tile &t) {
     const DenseArgs &p = *c.p;
+    const int64_t m0 = id.m0, n0 = id.n0;
     t.m0 = m0;
     t.n0 = n0;
+    t.lim = id.lim;
     // A: rows m0.. (K-contiguous) or columns m0.. of [K, M]; B likewise.
     const int64_t abase = TA ? m0 : m0 * c.KB;
     t.ra = rsrc4(p.A + abase, clamp_records(p.a_bytes - abase));
     // Preshuffled B: the whole buffer (it holds every column group of every
     // 256-column tile, padding included); the offsets below stay inside it.
+    // Grouped: group g's weights are rows [g N, g N + N) of one [G N, K]
+    // operand; the resource starts at the tile's first row (plain) or column
+    // group (preshuffled), and every offset from there is range-checked.
     int64_t bbase;
-    if constexpr (PSB) bbase = 0;
+    if constexpr (GROUP) bbase = PSB ? ((int64_t)id.g * p.N + n0) / 64 * c.nks * CGB : ((int64_t)id.g * p.N + n0) * c.KB;
+    else if constexpr (PSB) bbase = 0;
     else bbase = TB ? n0 : n0 * c.KB;
     t.rb = rsrc4(p.B + bbase, clamp_records(p.b_bytes - bbase));
     t.rs = (u32x4){0u, 0u, 0u, 0u};
+    t.soff = 0;
+    t.mg4 = 0;
+    if constexpr (GROUP) {
+      // waves 0-3: activation scales, per-group block layout (row r of the
+      // group at start*nkb + (r - start) + kb*mg); wave 4: the weight block
+      // scales of group g, [G, N/128, K/128]
+      if (c.w < 4) {
+        t.rs = rsrc4(p.sA, clamp_records(p.sa_bytes));
+        t.soff = (uint32_t)((id.start * c.nks + (m0 - id.start)) * 4);
+        t.mg4 = (uint32_t)(id.mg * 4);
+      } else {
+        t.rs = rsrc4(p.sB, clamp_records(p.sb_bytes));
+        t.soff = (uint32_t)((((int64_t)id.g * (p.N / 128) + n0 / 128) * c.nks) * 4);
+      }
+    }
     if constexpr (MX) {
       if (c.w < 4) {
         const int64_t b = (m0 + 64 * c.w) * c.sk32;
@@ -328,7 +399,16 @@ struct DenseLoop {
     if constexpr (ALL || PART == 1) load_tile<TA, 2, 4>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
     if constexpr (ALL || PART == 2 || PART == 3) {
       constexpr int J0 = (PART == 3) ? 2 : 0, J1 = (PART == 2) ? 2 : 4;
-      if constexpr (PSB) {
+      if constexpr (PSB && GROUP) {
+        // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j, from
+        // the tile's first column group, range-checked
+        const uint32_t add0 = (uint32_t)(((c.w >> 1) * c.nks + st) * CGB) + (uint32_t)(c.w & 1) * 4096u;
+        const uint32_t base = slot + B_REG + (uint32_t)c.w * 4096u;
+        static_for<J0, J1>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          dma_asm_v<16, j * 1024>(base, t.rb, (uint32_t)(c.lane * 16), add0 + j * 1024);
+        });
+      } else if constexpr (PSB) {
         // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j
         const uint32_t soff0 = (uint32_t)((t.n0 / 64 * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB) +
                                (uint32_t)((c.w >> 1) * c.nks * CGB) + (uint32_t)(c.w & 1) * 4096u;
@@ -340,6 +420,26 @@ struct DenseLoop {
         });
       } else {
         load_tile<TB, J0, J1>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
+      }
+    }
+    if constexpr (GROUP && (ALL || PART == 3 || PART == 4)) {
+      // With the first stage of each group of four K steps: waves 0-3 the
+      // 256 activation scales of K step 4 grp + w (four 256-byte DMAs of
+      // 64 rows), wave 4 the 2 x 4 weight block scales (lane l: column
+      // block (l / 4) % 2, K step l % 4).  Offsets past the last K block or
+      // the buffer read zeros or scales no output uses.
+      if ((st & 3) == 0) {
+        const uint32_t grp = (uint32_t)(st / 4);
+        const uint32_t dst = c.lds0 + S_REG + (uint32_t)gs * SGROUP;
+        if (c.w < 4) {
+          const uint32_t add = t.soff + (4u * grp + (uint32_t)c.w) * t.mg4;
+          static_for<0, 4>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            dma_asm_v<4, j * 256>(dst + SA_OFF + (uint32_t)c.w * 1024u, t.rs, c.vo_s, add + j * 256);
+          });
+        } else if (c.w == 4) {
+          dma_asm_v<4>(dst + SB_OFF, t.rs, c.vo_s, t.soff + grp * 16u);
+        }
       }
     }
     if constexpr (MX && (ALL || PART == 3 || PART == 4)) {
@@ -375,7 +475,15 @@ struct DenseLoop {
         dma_asm_v<16, j * 1024>(abase, t.ra, c.vo_a[0], (uint32_t)((v * 8 + j) * 8 * c.KB + 128 * (int64_t)st));
       });
       const uint32_t bbase = slot + B_REG + (uint32_t)v * 8192u;
-      if constexpr (PSB) {
+      if constexpr (PSB && GROUP) {
+        // column group v of the tile, range-checked (the last tile of the
+        // stack may have fewer than four)
+        const uint32_t add0 = (uint32_t)((v * c.nks + st) * CGB);
+        static_for<0, 8>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          dma_asm_v<16, j * 1024>(bbase, t.rb, (uint32_t)(c.lane * 16), add0 + j * 1024);
+        });
+      } else if constexpr (PSB) {
         const uint32_t soff0 = (uint32_t)(((t.n0 / 64 + v) * c.nks + (FP4 ? 2 * (int64_t)st : st)) * CGB);
         const u32x4 rb = t.rb;
         static_for<0, 8>([&](auto jc) {
@@ -435,6 +543,13 @@ struct DenseLoop {
       L.at = ((uint32_t)(kk * 256 + ((ca ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
       L.bt = ((uint32_t)(B_REG + kk * 256 + ((cb ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
     }
+    if constexpr (GROUP) {
+      // activation scale of row wm*128 + 16a + i (K step j at +1024 j), the
+      // weight block scale of the wave's 64 columns (block wn/2; +4 j)
+      L.sa = ((uint32_t)(S_REG + SA_OFF + (c.wm * 128 + i) * 4)) & LMASK;
+      L.sb = ((uint32_t)(S_REG + SB_OFF + (c.wn >> 1) * 16)) & LMASK;
+      return;
+    }
     L.sa = ((uint32_t)(S_REG + SA_OFF + (c.wm * 128 + i) * 16)) & LMASK;
     if constexpr (PSB) L.sb = ((uint32_t)(S_REG + SB_OFF + c.wn * 1024 + c.lane * 4)) & LMASK;
     else L.sb = ((uint32_t)(S_REG + SB_OFF + (c.wn * 64 + i) * 16)) & LMASK;
@@ -468,24 +583,25 @@ struct DenseLoop {
     u32x4 rd;                    // full tiles: D from the tile's origin
     uint32_t voff;               // full tiles: this lane's byte offset in the tile
     uint32_t rowstride;          // bytes of 16 rows of D
-    int m0, n0;                  // tile origin (edge tiles)
+    int m0, n0, lim;             // tile origin and row limit (edge tiles)
     float alpha;
     bool full, on;
   };
   static constexpr int EPI_STORES = FM * FN / 2;   // store instructions per full tile
 
-  __device__ static inline void make_epi(const Ctx &c, int64_t m0, int64_t n0, float alpha, bool on,
-                                         Epi &e) {
+  __device__ static inline void make_epi(const Ctx &c, int64_t m0, int64_t n0, int64_t lim, float alpha,
+                                         bool on, Epi &e) {
     const DenseArgs &p = *c.p;
     e.m0 = (int)m0;
     e.n0 = (int)n0;
+    e.lim = (int)lim;
     e.alpha = alpha;
     e.on = on;
     // Full tiles store through the range-checked vector offset (at most
     // 2 (255 N + 255) bytes from the tile's origin), which must stay below
     // the resource's clamped size of 2^31 - 16 bytes; wider D takes the
     // element-wise path.
-    e.full = m0 + DBM <= p.M && n0 + DBN <= p.N && (p.N & 7) == 0 && p.N <= (1 << 22);
+    e.full = m0 + DBM <= lim && n0 + DBN <= p.N && (p.N & 7) == 0 && p.N <= (1 << 22);
     const int64_t org = m0 * p.N + n0;
     e.rd = rsrc4(p.D + org, clamp_records(2 * (p.M * p.N - org)));
     e.rowstride = (uint32_t)(32 * p.N);
@@ -495,10 +611,10 @@ struct DenseLoop {
 
   __device__ static inline void store_rows(const Ctx &c, const Epi &e, int a, const v4f (&row_in)[FN]) {
     const float al = e.alpha;
-    // alpha is 1 for MX operands: no multiply
+    // alpha is 1 unless the operands are tensor-wise: no multiply
     v4f row[FN];
 #pragma unroll
-    for (int b = 0; b < FN; ++b) row[b] = MX ? row_in[b] : row_in[b] * al;
+    for (int b = 0; b < FN; ++b) row[b] = (SMODE != SM_TENSOR) ? row_in[b] : row_in[b] * al;
     if (e.full) {
       // computed here, not hoisted into a register per row tile
       uint32_t rs = e.rowstride;
@@ -524,7 +640,7 @@ struct DenseLoop {
       const DenseArgs &p = *c.p;
       const int lane = (int)__lane_id(), i = lane & 15, q = lane >> 4;
       const int64_t r = (int64_t)e.m0 + c.wm * (FM * 16) + a * 16 + i;
-      if (r < p.M) {
+      if (r < e.lim) {
         uint16_t *dst = p.D + r * p.N;
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
@@ -613,14 +729,55 @@ struct DenseLoop {
       // fragment, so that two words are live instead of eight.
       constexpr bool SA_AHEAD = TA || TB;
       auto scale_word = [&](int a) -> uint32_t {
+        if constexpr (GROUP) return lds_u32(ls + L.sa + a * 64 + ((st * KS + s) & 3) * 1024);
         return MX ? lds_u32(ls + L.sa + a * 256 + ((st * KS + s) & 3) * 4) : 0u;
       };
+      // groupwise: the weight block scale of this K step (all lanes alike)
+      float wsv = 1.0f;
+      if constexpr (GROUP) wsv = __uint_as_float(lds_u32(ls + L.sb + ((st * KS + s) & 3) * 4));
       uint32_t saw[SA_AHEAD ? 1 : FM];
       if constexpr (SA_AHEAD) {
         saw[0] = scale_word(0);
       } else {
 #pragma unroll
         for (int a = 0; a < FM; ++a) saw[a] = scale_word(a);
+      }
+      if constexpr (GROUP) {
+        // The 128-K partial products (neutral E8M0 scales) of row tile a go
+        // to one of two register sets while the partials of tile a - 1 are
+        // scaled by xs(row, kb) * ws(column block, kb) and added in FP32:
+        // each scaling then reads results of matrix-core instructions issued
+        // a whole row tile earlier, instead of waiting for the one just
+        // issued.
+        const v4f zero = (v4f){0.f, 0.f, 0.f, 0.f};
+        v4f part[2][FN];
+        float scp[2];
+        v8i af = read_a(s, 0);
+#pragma unroll
+        for (int a = 0; a <= FM; ++a) {
+          if (a < FM) {
+            v8i af_next;
+            if (a + 1 < FM) af_next = read_a(s, a + 1);
+            scp[a & 1] = __uint_as_float(saw[a]) * wsv;
+            // the previous tile's rows leave before this tile's partials
+            // replace them (one row tile later)
+            if (EPI && s == 0 && e.on) store_rows(c, e, a, acc[a]);
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+              part[a & 1][b] = mfma_scaled<FB, FA>(bf[b], af, zero, E8M0_ONE_X4, E8M0_ONE_X4);
+            if (a + 1 < FM) af = af_next;
+          }
+          if (a > 0) {
+            const int r = a - 1;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+              if (EPI && s == 0) acc[r][b] = part[r & 1][b] * scp[r & 1];
+              else acc[r][b] += part[r & 1][b] * scp[r & 1];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
       }
       v8i af = read_a(s, 0);
 #pragma unroll
@@ -676,9 +833,9 @@ struct DenseLoop {
   // in issue order, so at the end of that step waiting until at most
   // EPI_STORES operations are outstanding means the stage DMA issued before
   // the stores has landed, and the stores drain during the next K step.
-  template <class TileAt>
-  __device__ static inline void run(const Ctx &c, int ntiles, TileAt tile_at, float alpha,
-                                    uint8_t *smem) {
+  template <class TileAt, class Resolve>
+  __device__ static inline void run(const Ctx &c, int ntiles, TileAt tile_at, Resolve resolve,
+                                    float alpha, uint8_t *smem) {
     Lanes L;
     lane_offsets(c, L);
 
@@ -691,7 +848,7 @@ struct DenseLoop {
     int tm, tn;
     tile_at(0, tm, tn);
     Tile cur;
-    set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, cur);
+    set_tile(c, resolve(tm, tn), cur);
     issue(c, cur, 0, 0, 0);
     wait_vmem_le<0>();
     __syncthreads();
@@ -700,7 +857,7 @@ struct DenseLoop {
     const bool odd = (nst & 1) != 0;
     const int ngrp = (int)c.ngrp;              // scale groups per tile
     Epi e;
-    make_epi(c, 0, 0, alpha, false, e);
+    make_epi(c, 0, 0, 0, alpha, false, e);
     for (int t = 0; t < ntiles; ++t) {
       const bool more = t + 1 < ntiles;
       const int g0 = t * ngrp;                 // scale slot of group g: (g0 + g) % 2
@@ -718,7 +875,7 @@ struct DenseLoop {
           // first stage of the next tile into slot 0 (this step reads slot 1);
           // its sources are built here, not kept live through the K loop
           Tile nxt;
-          set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, nxt);
+          set_tile(c, resolve(tm, tn), nxt);
           issue_any(nxt, 0, (g0 + ngrp) & 1);
         }
         compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
@@ -744,9 +901,9 @@ struct DenseLoop {
       }
       if (k < nst) step(std::false_type{}, std::integral_constant<int, 1>{}, k);
       // this tile's result goes out during the next tile's first step
-      make_epi(c, cur.m0, cur.n0, alpha, true, e);
+      make_epi(c, cur.m0, cur.n0, cur.lim, alpha, true, e);
       if (more) {
-        set_tile(c, (int64_t)tm * DBM, (int64_t)tn * DBN, cur);
+        set_tile(c, resolve(tm, tn), cur);
         if (odd) {
           // the last step read slot 0: the next tile's first stage follows it
           issue(c, cur, 0, 0, (g0 + ngrp) & 1);
@@ -794,26 +951,7 @@ __global__ __launch_bounds__(DNW8 * 64, 1) void dense_kernel(DenseArgs p) {
   const int ntiles = (nb - bid + P - 1) / P;
 
   typename L::Ctx c;
-  c.p = &p;
-  c.lane = threadIdx.x & 63;
-  c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
-  c.wm = c.w >> 2;
-  c.wn = c.w & 3;
-  c.i16 = c.lane & 15;
-  c.q = c.lane >> 4;
-  c.KB = L::FP4 ? p.K / 2 : p.K;
-  c.nst = (int)(c.KB / 128);
-  c.sk32 = p.K / 32;
-  c.nks = p.K / 128;
-  c.ngrp = (p.K + 511) / 512;
-  L::dma_offsets(TA, c.lane, c.w, c.KB, p.M, c.vo_a);
-  L::dma_offsets(TB, c.lane, c.w, c.KB, p.N, c.vo_b);
-  c.vo_s = 0;
-  if constexpr (L::MX) {
-    if (c.w < 4 || !PSB) c.vo_s = (uint32_t)(c.lane * c.sk32);
-    else c.vo_s = (uint32_t)(c.lane * 16);
-  }
-  c.lds0 = lds_addr(smem);
+  L::init(c, p, smem);
 
   float alpha = 1.0f;
   if constexpr (SMODE == SM_TENSOR) alpha = *(const float *)p.sA * *(const float *)p.sB;
@@ -825,7 +963,10 @@ __global__ __launch_bounds__(DNW8 * 64, 1) void dense_kernel(DenseArgs p) {
     asm volatile("" : "+s"(P_), "+s"(tm_), "+s"(tn_));
     persistent_tile(bid, k, P_, tm_, tn_, tm, tn);
   };
-  L::run(c, ntiles, tile_at, alpha, smem);
+  auto resolve = [&](int tm, int tn) -> TileId {
+    return TileId{(int64_t)tm * DBM, (int64_t)tn * DBN, p.M, 0, 0, 0};
+  };
+  L::run(c, ntiles, tile_at, resolve, alpha, smem);
 }
 
 }  // namespace mxg

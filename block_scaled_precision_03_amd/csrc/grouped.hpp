@@ -203,31 +203,45 @@ __device__ inline int64_t wave_incl_sum(int64_t x, int lane) {
 }
 
 template <int BM>
-__device__ inline void build_group_table(const GroupedArgs &p, GroupTable &gt, int lane) {
+__device__ inline void build_group_table(const int64_t *m_sizes, int G, int64_t totM, GroupTable &gt,
+                                         int lane) {
   int64_t rows = 0, tiles = 0;
-  for (int c = 0; c < p.G; c += 64) {
+  for (int c = 0; c < G; c += 64) {
     const int g = c + lane;
-    int64_t s = g < p.G ? p.m_sizes[g] : 0;
-    s = s < 0 ? 0 : (s > p.totM ? p.totM : s);
+    int64_t s = g < G ? m_sizes[g] : 0;
+    s = s < 0 ? 0 : (s > totM ? totM : s);
     const int64_t incl = wave_incl_sum(s, lane);
-    const int64_t r0 = min(rows + incl - s, p.totM), r1 = min(rows + incl, p.totM);
+    const int64_t r0 = min(rows + incl - s, totM), r1 = min(rows + incl, totM);
     const int64_t mt = (r1 - r0 + BM - 1) / BM;
     const int64_t tincl = wave_incl_sum(mt, lane);
-    if (g < p.G) {
+    if (g < G) {
       gt.rows[g] = (int32_t)r0;
       gt.mtile[g] = (int32_t)(tiles + tincl - mt);
     }
-    rows = min(rows + __shfl(incl, 63, 64), p.totM);
+    rows = min(rows + __shfl(incl, 63, 64), totM);
     tiles += __shfl(tincl, 63, 64);
   }
   if (lane == 0) {
-    gt.rows[p.G] = (int32_t)rows;
-    gt.mtile[p.G] = (int32_t)tiles;
+    gt.rows[G] = (int32_t)rows;
+    gt.mtile[G] = (int32_t)tiles;
   }
 }
 
 // A value every lane holds alike, moved to scalar registers.
 __device__ inline int32_t uni32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The last group g with mtile[g] <= u, for a BM-row tile index u over all
+// groups (a non-empty group: an empty one shares its mtile with the group
+// after it).
+__device__ inline int group_of_tile(const GroupTable &gt, int G, int32_t u) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uni32(gt.mtile[mid]) <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 
 // Real tile t (t < mtile[G] * tiles_n): tiles are numbered group by group,
 // N-tile major, M-tile minor within a group.
@@ -239,15 +253,7 @@ struct StreamTile {
 template <int BM>
 __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable &gt, int64_t t) {
   const int32_t u = (int32_t)(t / p.tiles_n);        // BM-row tile index over all groups
-  // the last group g with mtile[g] <= u (a non-empty one: an empty group
-  // shares its mtile with the group after it)
-  int lo = 0, hi = p.G - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uni32(gt.mtile[mid]) <= u) lo = mid;
-    else hi = mid - 1;
-  }
-  const int g = lo;
+  const int g = group_of_tile(gt, p.G, u);
   const int32_t mt0 = uni32(gt.mtile[g]), r0 = uni32(gt.rows[g]);
   const int64_t mt = uni32(gt.mtile[g + 1]) - mt0;
   const int64_t local = t - (int64_t)mt0 * p.tiles_n;
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   const int wm = w >> 1, wn = w & 1;
   const int i16 = lane & 15, q = lane >> 4;
 
-  if (w == 0) build_group_table<BM>(p, gt, lane);
+  if (w == 0) build_group_table<BM>(p.m_sizes, p.G, p.totM, gt, lane);
   __syncthreads();
   const int P = (int)gridDim.x;
   const int64_t T = (int64_t)uni32(gt.mtile[p.G]) * p.tiles_n;   // real tiles
@@ -464,6 +470,67 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmem_le<0>();
+}
+
+}  // namespace mxg
+
+namespace mxg {
+
+// Grouped kernel for many rows per group (the matrix-core regime), on the
+// dense kernel's pipeline (DenseLoop with groupwise scales): 256 x 256
+// output tiles, eight waves, the two-slot LDS ring fed by inline-assembly
+// DMA, a persistent grid with one workgroup per compute unit walking its
+// tiles in XCD-banded order, and the epilogue of a tile stored from
+// registers during the next tile's first K step.
+//
+// * Tiles: each group's rows are cut into 256-row tiles (a tile never spans
+//   two groups; its stores stop at the group's last row), numbered over all
+//   groups; wave 0 builds the table of every group's first row and first
+//   tile in LDS once, and a tile's group is found by binary search.
+// * Software scaling ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm",
+//   Architecture support): each 128-K step runs the scaled matrix-core
+//   instruction with the neutral E8M0 scale into a zero accumulator and adds
+//   that partial times xs(row, kb) * ws(g, n/128, kb) in FP32.  The scales of
+//   four K steps come into LDS with the operand stages: 256 activation scales
+//   per K step, read in the per-group block layout (commit fixing the scale_a
+//   addressing), and the weight block scales of the tile's two 128-column
+//   blocks.
+// * Weights: group g is rows [g N, g N + N) of one [G N, K] operand, plain
+//   or preshuffled (the dense kernel's B layout); the last tile of a group
+//   whose N is not a multiple of 256 reads the next group's rows (or zeros
+//   past the end), which no stored output uses.
+template <bool PSB>
+__global__ __launch_bounds__(DNW8 * 64, 1) void grouped_dense_kernel(DenseArgs p) {
+  typedef DenseLoop<F_E4M3, F_E4M3, SM_GROUP, false, false, PSB> L;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS_BYTES];
+  __shared__ GroupTable gt;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w == 0) build_group_table<DBM>(p.m_sizes, p.G, p.M, gt, lane);
+  __syncthreads();
+  const int tiles_m = uni32(gt.mtile[p.G]);          // 256-row tiles over all groups
+  const int nb = tiles_m * p.tiles_n;
+  const int P = (int)gridDim.x;
+  const int bid = (int)blockIdx.x;
+  if (bid >= nb) return;
+  const int ntiles = (nb - bid + P - 1) / P;
+
+  typename L::Ctx c;
+  L::init(c, p, smem);
+  auto tile_at = [&](int k, int &tm, int &tn) {
+    int P_ = P, tm_ = tiles_m, tn_ = p.tiles_n;
+    asm volatile("" : "+s"(P_), "+s"(tm_), "+s"(tn_));
+    persistent_tile(bid, k, P_, tm_, tn_, tm, tn);
+  };
+  auto resolve = [&](int tm, int tn) -> TileId {
+    const int g = group_of_tile(gt, p.G, tm);
+    const int64_t start = uni32(gt.rows[g]);
+    const int64_t mg = uni32(gt.rows[g + 1]) - start;
+    const int64_t m0 = start + (int64_t)(tm - uni32(gt.mtile[g])) * DBM;
+    return TileId{m0, (int64_t)tn * DBN, start + mg, start, mg, g};
+  };
+  L::run(c, ntiles, tile_at, resolve, 1.0f, smem);
 }
 
 }  // namespace mxg

@@ -138,26 +138,40 @@ def test_grouped_long_k(preshuffled):
     H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped long K")
 
 
+def _edge_samples(rng, m_sizes, N, count):
+    """Random entries plus every group's first and last row (8 columns each)."""
+    totM = int(np.sum(m_sizes))
+    im, inn = H.sample_indices(rng, totM, N, count)
+    starts = np.concatenate([[0], np.cumsum(m_sizes)])
+    edge = np.array([r for g in range(len(m_sizes)) if m_sizes[g] for r in (starts[g], starts[g + 1] - 1)])
+    return (np.concatenate([im, np.repeat(edge, 8)]),
+            np.concatenate([inn, rng.integers(0, N, 8 * len(edge))]))
+
+
 @pytest.mark.parametrize("preshuffled", [False, True])
 def test_grouped_tiled_kernel(preshuffled):
-    """Shapes for which the 128 x 128 kernel runs (the matrix-core regime),
-    uneven groups, one empty, none tile aligned."""
+    """Shapes for which the matrix-core kernel (256 x 256 tiles on the dense
+    pipeline) runs: uneven groups, one empty, none tile aligned, 38 K steps.
+    Every row written; sampled entries and every group's edge rows."""
     from block_scaled_precision_03_amd import mxgemm
-    N, K = 2048, 256
+    N, K = 2048, 4864
     split = [1500, 0, 1077, 2100, 1, 700, 2500, 314]
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(921, split, N, K)
     assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_TILED
     D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
-    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
-    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped tiled kernel")
+    assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
+    im, inn = _edge_samples(np.random.default_rng(7), m_sizes, N, 20000)
+    ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16))[im, inn], ref, "grouped tiled kernel")
 
 
 def test_grouped_small_shapes_take_the_streaming_kernels():
-    """The parity cases above with few rows run the persistent kernels, both
-    tile heights among them; the benchmark's 128-row shapes take 64 x 64."""
+    """The parity cases above with few rows run the persistent 64 x 64
+    kernel (the 128 x 64 one has its own test below), and so do the
+    benchmark's 128-row shapes."""
     from block_scaled_precision_03_amd import mxgemm
     got = {mxgemm.grouped_variant(len(split), int(sum(split)), 256, 640) for split in SPLITS}
-    assert got == {mxgemm.GROUPED_STREAM64, mxgemm.GROUPED_STREAM128}
+    assert got == {mxgemm.GROUPED_STREAM64}
     assert mxgemm.grouped_variant(8, 128, 2048, 7168) == mxgemm.GROUPED_STREAM64
     assert mxgemm.grouped_variant(8, 128, 7168, 2304) == mxgemm.GROUPED_STREAM64
 
@@ -207,3 +221,74 @@ def test_grouped_many_groups_several_rounds(preshuffled):
     assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
     ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
     H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped, 200 groups")
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_tiled_half_last_column_tile(preshuffled):
+    """The matrix-core kernel's 256-column tiles with N = 1152 (the last tile
+    of each group holds 128 real columns; its weight rows and block scales
+    past N belong to the next group, or lie past the end for the last one),
+    uneven groups (one empty, none tile aligned) and rows past the last
+    group, which keep the sentinel.  Every entry of the last column tile,
+    sampled entries and the groups' edge rows against the oracle."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 1152, 2048
+    split = [1900, 0, 1077, 2100, 1, 700, 2500, 2622]
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(931, split, N, K, totM=11000)
+    assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_TILED
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    cover = int(sum(split))
+    bits = H.bits(D.view(torch.bfloat16))
+    assert np.all(bits[cover:] == SENTINEL_BITS)
+    assert not np.any(bits[:cover] == SENTINEL_BITS)
+    rng = np.random.default_rng(8)
+    im, inn = _edge_samples(rng, m_sizes, N, 20000)
+    rows = rng.integers(0, cover, 64)
+    im = np.concatenate([im, np.repeat(rows, 128)])
+    inn = np.concatenate([inn, np.tile(np.arange(1024, 1152), len(rows))])
+    ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16))[im, inn], ref, "grouped N=1152")
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_1024_groups_streaming(preshuffled):
+    """MXG_GROUPED_MAX_G = 1024 groups of 0..8 rows: the persistent 64 x 64
+    kernel's group table spans sixteen 64-group chunks.  Every entry against
+    the oracle, every row written."""
+    from block_scaled_precision_03_amd import mxgemm
+    G, N, K = 1024, 256, 256
+    split = np.random.default_rng(1024).integers(0, 9, G)
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(970, split, N, K)
+    assert mxgemm.grouped_variant(G, totM, N, K) == mxgemm.GROUPED_STREAM64
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped, 1024 groups")
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_1024_groups_tiled(preshuffled):
+    """MXG_GROUPED_MAX_G = 1024 groups of 0..512 rows (every seventh empty)
+    on the matrix-core kernel: its group table and binary search over all of
+    them, eight rounds of persistent tiles.  Integer-valued codes with
+    power-of-two scales, so sampled entries and every group's edge rows must
+    match the oracle bit for bit."""
+    from block_scaled_precision_03_amd import mxgemm
+    G, N, K = 1024, 256, 4096
+    rng = np.random.default_rng(1025)
+    split = rng.integers(0, 513, G)
+    split[::7] = 0
+    m_sizes = split.astype(np.int64)
+    totM = int(m_sizes.sum())
+    assert mxgemm.grouped_variant(G, totM, N, K) == mxgemm.GROUPED_TILED
+    vals = np.array([0xC0, 0xB8, 0x00, 0x38, 0x40], np.uint8)
+    XQ = vals[rng.integers(0, 5, (totM, K), dtype=np.uint8)]
+    WQ = vals[rng.integers(0, 5, (G, N, K), dtype=np.uint8)]
+    xs = (2.0 ** rng.integers(0, 3, totM * K // 128)).astype(np.float32)
+    ws = (2.0 ** rng.integers(0, 3, (G, N // 128, K // 128))).astype(np.float32)
+    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    bits = H.bits(D.view(torch.bfloat16))
+    assert not np.any(bits == SENTINEL_BITS)
+    im, inn = _edge_samples(np.random.default_rng(6), m_sizes, N, 20000)
+    ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
+    assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
