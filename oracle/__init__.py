@@ -18,6 +18,7 @@ from . import build as _build
 
 E4M3, E5M2, E2M1 = 0, 1, 4
 SCALE_MX, SCALE_TENSOR = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3
 
 _lib = None
 
@@ -59,6 +60,10 @@ def lib():
         L.oracle_bf16_rne.argtypes = [d]
         L.oracle_bf16_rne_array.restype = None
         L.oracle_bf16_rne_array.argtypes = [p, i64, p]
+        L.oracle_activation.restype = d
+        L.oracle_activation.argtypes = [i, d]
+        L.oracle_epilogue.restype = i
+        L.oracle_epilogue.argtypes = [p, i64, i64, p, i]
         _lib = L
     return _lib
 
@@ -256,3 +261,21 @@ def quant_tensor(fmt, x):
     if lib().oracle_quant_tensor(fmt, _ptr(x), x.size, _ptr(codes), _ptr(s)) != 0:
         raise ValueError("oracle_quant_tensor: format must be E4M3 or E5M2")
     return codes, np.float32(s[0])
+
+
+def activation(act, z):
+    """The epilogue's activation of one FP64 value (see oracle.c)."""
+    return float(lib().oracle_activation(int(act), float(z)))
+
+
+def epilogue(D, bias_bits=None, act=ACT_NONE):
+    """act(D + bias[n]) in FP64 on a copy of the FP64 [M, N] product; bias as
+    BF16 bit patterns [N] (uint16) or None."""
+    out = np.array(D, dtype=np.float64, order="C", copy=True)
+    M, N = out.shape
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    if b is not None and b.size != N:
+        raise ValueError("bias must have N entries")
+    if lib().oracle_epilogue(_ptr(out), M, N, _ptr(b), int(act)) != 0:
+        raise ValueError("oracle_epilogue: unknown activation")
+    return out

@@ -517,3 +517,57 @@ int oracle_quant_group_weight(int G, const float *w, int64_t N, int64_t K, uint8
     }
     return 0;
 }
+
+/* ---- epilogue: bias and activation ---------------------------------------
+ *
+ * "[gfx1250] Add MXFP4 GEMM support to FlyDSL backend" (Description): the
+ * GEMM's activation and bias are the follow-up to the plain product.  The
+ * pages name no function, so this project reads it as the fused epilogue of
+ * a linear layer's forward GEMM:
+ *     D[m,n] = act( sum_k a(m,k) b(n,k) + bias[n] )
+ * with bias a BF16 vector over N (NULL: none) and act one of
+ *     0 none, 1 ReLU max(z, 0),
+ *     2 GELU, tanh form: z/2 (1 + tanh( sqrt(2/pi) (z + 0.044715 z^3) )),
+ *     3 SiLU z / (1 + e^-z),
+ * all in FP64 on the FP64 sum, rounded once to BF16 by the caller.  D is
+ * [M, N] row-major, updated in place. */
+#define ORC_ACT_NONE 0
+#define ORC_ACT_RELU 1
+#define ORC_ACT_GELU_TANH 2
+#define ORC_ACT_SILU 3
+
+static double orc_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+double oracle_activation(int act, double z)
+{
+    switch (act) {
+    case ORC_ACT_NONE: return z;
+    case ORC_ACT_RELU: return z > 0.0 ? z : 0.0;
+    case ORC_ACT_GELU_TANH: {
+        const double c = sqrt(2.0 / 3.14159265358979323846);
+        return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+    }
+    case ORC_ACT_SILU: return z / (1.0 + exp(-z));
+    default: return NAN;
+    }
+}
+
+int oracle_epilogue(double *D, int64_t M, int64_t N, const uint16_t *bias, int act)
+{
+    int64_t m;
+    if (act < ORC_ACT_NONE || act > ORC_ACT_SILU) return -1;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double z = D[m * N + n];
+            if (bias) z += orc_bf16_value(bias[n]);
+            D[m * N + n] = oracle_activation(act, z);
+        }
+    return 0;
+}
