@@ -479,6 +479,43 @@ def mxfp4_bench(torch, synth, mxgemm, dev):
     return {"M": M, "N": N, "K": K, "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP4_TFLOPS}
 
 
+def fused_bench(torch, synth, mxgemm, dev):
+    """The forward GEMM of a linear layer with its epilogue: MXFP8 NT
+    16384 x 14336 x 4096, preshuffled B, + bias and GELU (tanh form) or
+    SiLU, fused into the kernel (mxgemm_run_fused) against the plain GEMM
+    followed by torch's bias add and activation on the BF16 output."""
+    import torch.nn.functional as F
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    M, N, K = 16384, 14336, 4096
+    qa, sa = synth.quant_mx(synth.normal(synth.seed_for(2, 1, 0), (M, K)), "e4m3")
+    qb, sb = synth.quant_mx(synth.normal(synth.seed_for(2, 2, 1), (N, K), 0.02), "e4m3")
+    A, SA = t(qa), t(sa)
+    fB = mxgemm.MXFP8_E4M3 | mxgemm.PRESHUFFLED
+    B = torch.empty(mxgemm.preshuffle_b_bytes(mxgemm.MXFP8_E4M3, N, K), dtype=torch.uint8, device=dev)
+    SB = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=dev)
+    mxgemm.preshuffle_b(mxgemm.MXFP8_E4M3, mxgemm.NT, t(qb), B, N, K)
+    mxgemm.preshuffle_scales(t(sb), SB, N, K)
+    bias = (torch.randn(N, device=dev, generator=torch.Generator(device=dev).manual_seed(7)) * 0.5).to(torch.bfloat16)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    plain = lambda: mxgemm.run(mxgemm.MXFP8_E4M3, fB, mxgemm.NT, A, SA, B, SB, D, M, N, K)
+    res = {"M": M, "N": N, "K": K, "gemm_us": time_calls(torch, plain)}
+    for name, act, tf in (("gelu_tanh", mxgemm.ACT_GELU_TANH, lambda y: F.gelu(y, approximate="tanh")),
+                          ("silu", mxgemm.ACT_SILU, F.silu)):
+        fused = lambda: mxgemm.run_fused(mxgemm.MXFP8_E4M3, fB, mxgemm.NT, A, SA, B, SB, D, M, N, K,
+                                         bias=bias, activation=act)
+
+        def unfused():
+            plain()
+            tf(D + bias)
+        res[name] = {"fused_us": time_calls(torch, fused), "unfused_us": time_calls(torch, unfused)}
+        log("fused epilogue bias + %s (16384,14336,4096): fused %.1f us, GEMM alone %.1f us, "
+            "GEMM + torch bias and activation %.1f us"
+            % (name, res[name]["fused_us"], res["gemm_us"], res[name]["unfused_us"]))
+    del A, B, D
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -672,6 +709,8 @@ def main():
         result["quantizers"] = quant_bench(torch, synth, mxgemm, dev)
         log("MXFP4 ...")
         result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
+        log("fused epilogue ...")
+        result["fused_epilogue"] = fused_bench(torch, synth, mxgemm, dev)
         result["mfma_ceiling"] = mfma_ceiling(torch, mxgemm, dev)
         result["roofline"]["frac_of_mfma_ceiling"] = (
             result["roofline"]["achieved"] / result["mfma_ceiling"]["fp8"]["tflops"])

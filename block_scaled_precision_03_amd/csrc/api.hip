@@ -139,7 +139,20 @@ namespace {
 typedef void (*dense_fn)(DenseArgs);
 
 template <int FA, int FB>
-dense_fn pick_layout(bool mx, int layout, bool psb) {
+dense_fn pick_layout(bool mx, int layout, bool psb, bool fuse) {
+  if (fuse) {
+    // bias / activation epilogue: the forward (NT) kernels
+    if (layout != MXG_NT) return nullptr;
+    if constexpr (FA == F_E2M1 || FB == F_E2M1) {
+      if (!mx) return nullptr;
+      return psb ? dense_kernel<FA, FB, SM_MX, false, false, true, true> : dense_kernel<FA, FB, SM_MX, false, false, false, true>;
+    } else if (mx) {
+      return psb ? dense_kernel<FA, FB, SM_MX, false, false, true, true> : dense_kernel<FA, FB, SM_MX, false, false, false, true>;
+    } else {
+      return psb ? dense_kernel<FA, FB, SM_TENSOR, false, false, true, true>
+                 : dense_kernel<FA, FB, SM_TENSOR, false, false, false, true>;
+    }
+  }
   if constexpr (FA == F_E2M1 || FB == F_E2M1) {
     if (!mx || layout != MXG_NT) return nullptr;
     return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
@@ -164,12 +177,12 @@ dense_fn pick_layout(bool mx, int layout, bool psb) {
   }
 }
 
-dense_fn pick_dense(int ea, int eb, bool mx, int layout, bool psb) {
-  if (ea == F_E2M1 && eb == F_E2M1) return mx ? pick_layout<F_E2M1, F_E2M1>(true, layout, psb) : nullptr;
-  if (ea == F_E4M3 && eb == F_E4M3) return pick_layout<F_E4M3, F_E4M3>(mx, layout, psb);
-  if (ea == F_E4M3 && eb == F_E5M2) return pick_layout<F_E4M3, F_E5M2>(mx, layout, psb);
-  if (ea == F_E5M2 && eb == F_E4M3) return pick_layout<F_E5M2, F_E4M3>(mx, layout, psb);
-  if (ea == F_E5M2 && eb == F_E5M2) return pick_layout<F_E5M2, F_E5M2>(mx, layout, psb);
+dense_fn pick_dense(int ea, int eb, bool mx, int layout, bool psb, bool fuse) {
+  if (ea == F_E2M1 && eb == F_E2M1) return mx ? pick_layout<F_E2M1, F_E2M1>(true, layout, psb, fuse) : nullptr;
+  if (ea == F_E4M3 && eb == F_E4M3) return pick_layout<F_E4M3, F_E4M3>(mx, layout, psb, fuse);
+  if (ea == F_E4M3 && eb == F_E5M2) return pick_layout<F_E4M3, F_E5M2>(mx, layout, psb, fuse);
+  if (ea == F_E5M2 && eb == F_E4M3) return pick_layout<F_E5M2, F_E4M3>(mx, layout, psb, fuse);
+  if (ea == F_E5M2 && eb == F_E5M2) return pick_layout<F_E5M2, F_E5M2>(mx, layout, psb, fuse);
   return nullptr;
 }
 
@@ -177,25 +190,35 @@ __global__ void zero_bf16_kernel(uint16_t *D, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) D[i] = 0;
 }
-}  // namespace
 
-extern "C" int mxgemm_run(int fmtA, int fmtB, int layout, const void *A, const void *sA, const void *B,
-               const void *sB, void *D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  const int v = mxgemm_validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K);
-  if (v != MXG_OK) return v;
+// K == 0 with the fused epilogue: D[m, n] = act(0 + bias[n]).
+__global__ void bias_act_fill_kernel(uint16_t *D, int64_t M, int64_t N, const uint16_t *bias, int act) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  const float z = bias ? __uint_as_float((uint32_t)bias[i % N] << 16) : 0.0f;
+  D[i] = (uint16_t)pack_bf16x2(activate(act, z), 0.0f);
+}
+
+int run_dense(int fmtA, int fmtB, int layout, const void *A, const void *sA, const void *B, const void *sB,
+              void *D, int64_t M, int64_t N, int64_t K, const void *bias, int act, hipStream_t stream) {
+  const bool fuse = bias != nullptr || act != MXG_ACT_NONE;
   if (M == 0 || N == 0) return MXG_OK;
   if (K == 0) {
     const int64_t n = M * N;
-    hipLaunchKernelGGL(zero_bf16_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
-                       (uint16_t *)D, n);
+    if (fuse)
+      hipLaunchKernelGGL(bias_act_fill_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
+                         (uint16_t *)D, M, N, (const uint16_t *)bias, act);
+    else
+      hipLaunchKernelGGL(zero_bf16_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
+                         (uint16_t *)D, n);
     return launch_status();
   }
   const bool psb = (fmtB & MXG_PRESHUFFLED) != 0;
   const FmtInfo fa = fmt_info(fmtA), fb = fmt_info(fmtB & ~MXG_PRESHUFFLED);
-  dense_fn fn = pick_dense(fa.elem, fb.elem, fa.mx, layout, psb);
+  dense_fn fn = pick_dense(fa.elem, fb.elem, fa.mx, layout, psb, fuse);
   if (!fn) return MXG_ERR_UNSUPPORTED;
   const bool fp4 = fa.elem == F_E2M1;
-  DenseArgs a;
+  DenseArgs a = {};
   a.A = (const uint8_t *)A;
   a.B = (const uint8_t *)B;
   a.sA = sA;
@@ -210,12 +233,46 @@ extern "C" int mxgemm_run(int fmtA, int fmtB, int layout, const void *A, const v
   a.sb_bytes = fb.mx ? (psb ? mxgemm_preshuffle_scales_bytes(N, K) : N * (K / 32)) : 4;
   a.tiles_m = (int)cdiv(M, DBM);
   a.tiles_n = (int)cdiv(N, DBN);
+  a.bias = (const uint16_t *)bias;
+  a.act = act;
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
   // Persistent grid: one workgroup per compute unit, each walking its tiles.
   const int64_t blocks = tiles < cu_count() ? tiles : cu_count();
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(DNW8 * 64), 0, stream, a);
   return launch_status();
+}
+}  // namespace
+
+extern "C" int mxgemm_run(int fmtA, int fmtB, int layout, const void *A, const void *sA, const void *B,
+               const void *sB, void *D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int v = mxgemm_validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K);
+  if (v != MXG_OK) return v;
+  return run_dense(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, nullptr, MXG_ACT_NONE, stream);
+}
+
+extern "C" int mxgemm_validate_fused(int fmtA, int fmtB, int layout, const void *A, const void *sA,
+                                     const void *B, const void *sB, const void *D, int64_t M, int64_t N,
+                                     int64_t K, const void *bias, int activation) {
+  if (activation < MXG_ACT_NONE || activation > MXG_ACT_SILU) return MXG_ERR_INVALID_ARG;
+  const int v = mxgemm_validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K);
+  if (v != MXG_OK) return v;
+  if (bias == nullptr && activation == MXG_ACT_NONE) return MXG_OK;
+  if (layout != MXG_NT) return MXG_ERR_UNSUPPORTED;
+  if (bias != nullptr) {
+    // the bias is staged by 4-byte DMAs of column pairs
+    if (N % 2 != 0) return MXG_ERR_UNSUPPORTED;
+    if (!aligned(bias, 4)) return MXG_ERR_MISALIGNED;
+  }
+  return MXG_OK;
+}
+
+extern "C" int mxgemm_run_fused(int fmtA, int fmtB, int layout, const void *A, const void *sA, const void *B,
+                                const void *sB, void *D, int64_t M, int64_t N, int64_t K, const void *bias,
+                                int activation, hipStream_t stream) {
+  const int v = mxgemm_validate_fused(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, bias, activation);
+  if (v != MXG_OK) return v;
+  return run_dense(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, bias, activation, stream);
 }
 
 extern "C" int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
@@ -482,6 +539,9 @@ extern "C" int mxgemm_quantize_tensor(int fmt, const float *x, void *codes, floa
 }
 
 static_assert(QG_MAX == MXG_GROUPED_MAX_G, "group table of the activation quantizer");
+static_assert(ACT_NONE == MXG_ACT_NONE && ACT_RELU == MXG_ACT_RELU && ACT_GELU_TANH == MXG_ACT_GELU_TANH &&
+                  ACT_SILU == MXG_ACT_SILU,
+              "activation codes");
 
 extern "C" int grouped_fp8_quantize_act(int G, const int64_t *m_sizes, const float *x, void *codes,
                                         float *x_scale, int64_t totM, int64_t K, hipStream_t stream) {

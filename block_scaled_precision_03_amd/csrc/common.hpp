@@ -170,6 +170,28 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// Epilogue activations (after the bias, on the FP32 result).
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
+
+// Logistic function 1 / (1 + e^-y) from the hardware base-2 exponential and
+// reciprocal (each within about an ulp of FP32); saturates to 0 and 1.
+__device__ inline float logistic_f32(float y) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * 1.4426950408889634f));
+}
+
+// GELU in its tanh form, z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z +
+// 0.044715 z^3), written as z * logistic(2u) (the two are equal since
+// (1 + tanh(u)) / 2 = 1 / (1 + e^-2u)); SiLU z * logistic(z).
+__device__ inline float activate(int act, float z) {
+  if (act == ACT_RELU) return fmaxf(z, 0.0f);
+  if (act == ACT_GELU_TANH) {
+    const float u = 0.7978845608028654f * fmaf(0.044715f * z, z * z, z);
+    return z * logistic_f32(2.0f * u);
+  }
+  if (act == ACT_SILU) return z * logistic_f32(z);
+  return z;
+}
+
 __device__ inline uint32_t lds_load_u32(const void *p) { return *(const lds_u32_t *)p; }
 __device__ inline void lds_store8(void *p, v2i v) { *(__attribute__((address_space(3))) v2i *)p = v; }
 

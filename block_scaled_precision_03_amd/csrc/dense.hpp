@@ -42,6 +42,8 @@ struct DenseArgs {
   int tiles_m, tiles_n;
   const int64_t *m_sizes;         // groupwise only
   int G;                          // groupwise only
+  const uint16_t *bias;           // fused epilogue: BF16 [N] or null
+  int act;                        // fused epilogue: ACT_*
 };
 
 // One output tile: origin, the row limit of its stores (M, or the end of its
@@ -218,7 +220,7 @@ __device__ inline void wait_vmem_le() {
 // from registers while that stage streams in, so no compute unit idles on an
 // epilogue, a workgroup launch or a cold first stage between tiles.
 //
-template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
+template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB, bool FUSE = false>
 struct DenseLoop {
   static constexpr bool FP4 = (FA == F_E2M1);
   static constexpr bool MX = (SMODE == SM_MX);
@@ -241,7 +243,11 @@ struct DenseLoop {
   // A read offset within either slot then fits the 16-bit offset field of a
   // DS instruction on top of one per-lane base register per operand.
   static constexpr int B_REG = 2 * AB, S_REG = 4 * AB;
-  static constexpr int LDS_BYTES = S_REG + 2 * SGROUP;
+  // Fused epilogue: the BF16 bias of a tile's 256 columns, two slots by the
+  // parity of the tile's index (tile t's bias is read while tile t + 1's
+  // first K step stores tile t, and replaced by tile t + 2's).
+  static constexpr int BIAS_OFF = S_REG + 2 * SGROUP, BIAS_SLOT = DBN * 2;
+  static constexpr int LDS_BYTES = BIAS_OFF + (FUSE ? 2 * BIAS_SLOT : 0);
   static constexpr int CGB = FP4 ? 4096 : 8192;
   static constexpr bool PIN = !TA && !TB && (PSB || !MX || FP4);
 
@@ -293,6 +299,7 @@ struct DenseLoop {
     int64_t m0, n0, lim;
     u32x4 ra, rb, rs;              // rs: this wave's scale source
     uint32_t soff, mg4;            // groupwise: this wave's scale offset, 4 * group rows
+    int bslot;                     // fused epilogue: bias slot of the tile
   };
 
   __device__ static inline void set_tile(const Ctx &c, const TileId &id, Tile &t) {
@@ -317,6 +324,7 @@ struct DenseLoop {
     t.rs = (u32x4){0u, 0u, 0u, 0u};
     t.soff = 0;
     t.mg4 = 0;
+    t.bslot = 0;
     if constexpr (GROUP) {
       // waves 0-3: activation scales, per-group block layout (row r of the
       // group at start*nkb + (r - start) + kb*mg); wave 4: the weight block
@@ -420,6 +428,19 @@ struct DenseLoop {
         });
       } else {
         load_tile<TB, J0, J1>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
+      }
+    }
+    if constexpr (FUSE && (ALL || PART == 3 || PART == 4)) {
+      // with the tile's first stage: its 256 BF16 bias values (two 256-byte
+      // DMAs by wave 3; columns past N read zeros).  Without a bias (an
+      // activation alone) the resource is empty: the DMAs write zeros and
+      // read no memory.
+      if (st == 0 && c.w == 3) {
+        const u32x4 rb = p.bias ? rsrc4(p.bias + t.n0, clamp_records(2 * (p.N - t.n0)))
+                                : rsrc4(p.D, 0u);
+        const uint32_t dst = c.lds0 + BIAS_OFF + (uint32_t)t.bslot * BIAS_SLOT;
+        dma_asm_v<4, 0>(dst, rb, (uint32_t)(c.lane * 4), 0u);
+        dma_asm_v<4, 256>(dst, rb, (uint32_t)(c.lane * 4), 256u);
       }
     }
     if constexpr (GROUP && (ALL || PART == 3 || PART == 4)) {
@@ -586,15 +607,18 @@ struct DenseLoop {
     int m0, n0, lim;             // tile origin and row limit (edge tiles)
     float alpha;
     bool full, on;
+    int bslot, act;              // fused epilogue
   };
   static constexpr int EPI_STORES = FM * FN / 2;   // store instructions per full tile
 
   __device__ static inline void make_epi(const Ctx &c, int64_t m0, int64_t n0, int64_t lim, float alpha,
-                                         bool on, Epi &e) {
+                                         bool on, Epi &e, int bslot = 0) {
     const DenseArgs &p = *c.p;
     e.m0 = (int)m0;
     e.n0 = (int)n0;
     e.lim = (int)lim;
+    e.bslot = bslot;
+    e.act = FUSE ? p.act : ACT_NONE;
     e.alpha = alpha;
     e.on = on;
     // Full tiles store through the range-checked vector offset (at most
@@ -615,6 +639,28 @@ struct DenseLoop {
     v4f row[FN];
 #pragma unroll
     for (int b = 0; b < FN; ++b) row[b] = (SMODE != SM_TENSOR) ? row_in[b] : row_in[b] * al;
+    // Fused epilogue: + bias[n] (BF16 from the tile's bias slot), then the
+    // activation, both in FP32 before the one rounding to BF16; applied to
+    // one matrix-core tile at a time, right before it is packed.
+    auto finish = [&](v4f v, int b) -> v4f {
+      if constexpr (FUSE) {
+        const int lane = (int)__lane_id();
+        const uint32_t bs = c.lds0 + BIAS_OFF + (uint32_t)e.bslot * BIAS_SLOT + (c.wn * 64 + 4 * (lane >> 4)) * 2;
+        const v2i w = *(const lds_v2i *)(uintptr_t)(bs + b * 32);
+        v.x += __uint_as_float((uint32_t)w.x << 16);
+        v.y += __uint_as_float((uint32_t)w.x & 0xFFFF0000u);
+        v.z += __uint_as_float((uint32_t)w.y << 16);
+        v.w += __uint_as_float((uint32_t)w.y & 0xFFFF0000u);
+        const int act = e.act;
+        if (act != ACT_NONE) {
+          v.x = activate(act, v.x);
+          v.y = activate(act, v.y);
+          v.z = activate(act, v.z);
+          v.w = activate(act, v.w);
+        }
+      }
+      return v;
+    };
     if (e.full) {
       // computed here, not hoisted into a register per row tile
       uint32_t rs = e.rowstride;
@@ -624,7 +670,7 @@ struct DenseLoop {
       const int partner = (lane ^ 16) << 2;
 #pragma unroll
       for (int pr = 0; pr < FN / 2; ++pr) {
-        const v4f x = row[2 * pr], y = row[2 * pr + 1];
+        const v4f x = finish(row[2 * pr], 2 * pr), y = finish(row[2 * pr + 1], 2 * pr + 1);
         const uint32_t xlo = pack_bf16x2(x.x, x.y), xhi = pack_bf16x2(x.z, x.w);
         const uint32_t ylo = pack_bf16x2(y.x, y.y), yhi = pack_bf16x2(y.z, y.w);
         // q even keeps its tile-2p chunk and takes the partner's; q odd the
@@ -644,7 +690,7 @@ struct DenseLoop {
         uint16_t *dst = p.D + r * p.N;
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
-          const v4f v = row[b];
+          const v4f v = finish(row[b], b);
           const uint32_t u[2] = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
           const int64_t col = (int64_t)e.n0 + c.wn * (FN * 16) + b * 16 + 4 * q;
 #pragma unroll
@@ -696,10 +742,12 @@ struct DenseLoop {
     };
     // A stage of two K steps (FP4) reads both steps' B fragments and scales
     // up front, so that the second step's reads overlap the first step's
-    // matrix work instead of stalling between the two.
+    // matrix work instead of stalling between the two (not in the first step
+    // of a fused epilogue, which needs those registers).
+    constexpr bool PRE = KS > 1 && !(FUSE && EPI);
     v8i bpre[KS][FN];
     int spre[KS][FN];
-    if constexpr (KS > 1) {
+    if constexpr (PRE) {
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -714,7 +762,7 @@ struct DenseLoop {
       int sb[FN];
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
-        if constexpr (KS > 1) {
+        if constexpr (PRE) {
           bf[b] = bpre[s][b];
           sb[b] = spre[s][b];
         } else {
@@ -876,13 +924,12 @@ struct DenseLoop {
           // its sources are built here, not kept live through the K loop
           Tile nxt;
           set_tile(c, resolve(tm, tn), nxt);
+          nxt.bslot = (t + 1) & 1;
           issue_any(nxt, 0, (g0 + ngrp) & 1);
         }
         compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
         // Only where registers allow: for the transposed variants and MX FP8
-        // with plain B it costs spills in the K loop (and with a transposed A
-        // it gave rare non-finite outputs at full size, which the full-size
-        // determinism tests now guard against).
+        // with plain B it costs spills in the K loop.
         if constexpr (PIN) pin(acc);
         __builtin_amdgcn_sched_barrier(0);
         // This wave's part of the next stage has landed (and, with no
@@ -901,9 +948,10 @@ struct DenseLoop {
       }
       if (k < nst) step(std::false_type{}, std::integral_constant<int, 1>{}, k);
       // this tile's result goes out during the next tile's first step
-      make_epi(c, cur.m0, cur.n0, cur.lim, alpha, true, e);
+      make_epi(c, cur.m0, cur.n0, cur.lim, alpha, true, e, cur.bslot);
       if (more) {
         set_tile(c, resolve(tm, tn), cur);
+        cur.bslot = (t + 1) & 1;
         if (odd) {
           // the last step read slot 0: the next tile's first stage follows it
           issue(c, cur, 0, 0, (g0 + ngrp) & 1);
@@ -939,9 +987,9 @@ __device__ inline void persistent_tile(int bid, int k, int P, int tiles_m, int t
   tn = in / rows;
 }
 
-template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB>
+template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB, bool FUSE = false>
 __global__ __launch_bounds__(DNW8 * 64, 1) void dense_kernel(DenseArgs p) {
-  typedef DenseLoop<FA, FB, SMODE, TA, TB, PSB> L;
+  typedef DenseLoop<FA, FB, SMODE, TA, TB, PSB, FUSE> L;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS_BYTES];
 
   const int nb = p.tiles_m * p.tiles_n;

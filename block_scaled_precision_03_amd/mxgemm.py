@@ -19,9 +19,11 @@ PRESHUFFLED = 0x100
 NT, NN, TN = 0, 1, 2
 GROUPED_MAX_G = 1024
 GROUPED_STREAM64, GROUPED_TILED, GROUPED_STREAM128 = 0, 1, 2
+ACT_NONE, ACT_RELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3
 
 EXPORTS = (
     "mxgemm_init", "mxgemm_status_string", "mxgemm_run", "mxgemm_validate",
+    "mxgemm_run_fused", "mxgemm_validate_fused",
     "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate", "grouped_fp8_gemm_variant",
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
@@ -43,6 +45,10 @@ _lib.mxgemm_run.restype = _i
 _lib.mxgemm_run.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]
 _lib.mxgemm_validate.restype = _i
 _lib.mxgemm_validate.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64]
+_lib.mxgemm_run_fused.restype = _i
+_lib.mxgemm_run_fused.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _p]
+_lib.mxgemm_validate_fused.restype = _i
+_lib.mxgemm_validate_fused.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i]
 _lib.grouped_fp8_gemm_run.restype = _i
 _lib.grouped_fp8_gemm_run.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p]
 _lib.grouped_fp8_gemm_validate.restype = _i
@@ -118,6 +124,18 @@ def run(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, stream=None):
 def validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K):
     return _lib.mxgemm_validate(fmtA, fmtB, layout, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB),
                                 _ptr(D), M, N, K)
+
+
+def run_fused(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, bias=None, activation=ACT_NONE,
+              stream=None):
+    """D = act(sum_k a(m,k) b(n,k) + bias[n]) in BF16; bias: BF16 [N] or None."""
+    _check(_lib.mxgemm_run_fused(fmtA, fmtB, layout, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(D),
+                                 M, N, K, _ptr(bias), activation, _stream(stream)), "mxgemm_run_fused")
+
+
+def validate_fused(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, bias=None, activation=ACT_NONE):
+    return _lib.mxgemm_validate_fused(fmtA, fmtB, layout, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB),
+                                      _ptr(D), M, N, K, _ptr(bias), activation)
 
 
 def grouped_run(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_preshuffled=False,

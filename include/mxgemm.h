@@ -133,6 +133,42 @@ int mxgemm_validate(int fmtA, int fmtB, int layout,
                     const void *D, int64_t M, int64_t N, int64_t K);
 
 /*
+ * mxgemm_run_fused -- mxgemm_run with the epilogue of a linear layer's
+ * forward GEMM fused into the kernel:
+ *
+ *     D[m,n] = act( sum_k a(m,k) b(n,k) + bias[n] )
+ *
+ * "[gfx1250] Add MXFP4 GEMM support to FlyDSL backend" (Description): the
+ * GEMM's activation and bias are its stated follow-up; the pages name no
+ * function, so the set below is this library's reading.  The sum (scaled by
+ * sA*sB for tensor-wise operands) stays in FP32, the bias is added and the
+ * activation applied in FP32, and the result is rounded once to BF16.
+ *
+ * bias        device BF16 [N] (raw uint16 bits), 4-byte aligned, or NULL.
+ * activation  MXG_ACT_NONE, MXG_ACT_RELU (max(z, 0)), MXG_ACT_GELU_TANH
+ *             (z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))) or MXG_ACT_SILU
+ *             (z / (1 + e^-z)); the GPU evaluates both logistic forms with
+ *             its base-2 exponential and reciprocal instructions.
+ * Everything else as mxgemm_run.  With a bias or an activation only the NT
+ * layout (the forward GEMM) is built, and a bias needs N even
+ * (MXG_ERR_UNSUPPORTED otherwise); an unknown activation is
+ * MXG_ERR_INVALID_ARG, a misaligned bias MXG_ERR_MISALIGNED.  With
+ * bias == NULL and MXG_ACT_NONE the call is mxgemm_run.  K == 0 writes
+ * act(bias[n]).
+ */
+enum { MXG_ACT_NONE = 0, MXG_ACT_RELU = 1, MXG_ACT_GELU_TANH = 2, MXG_ACT_SILU = 3 };
+int mxgemm_run_fused(int fmtA, int fmtB, int layout,
+                     const void *A, const void *sA, const void *B, const void *sB,
+                     void *D, int64_t M, int64_t N, int64_t K,
+                     const void *bias, int activation, hipStream_t stream);
+
+/* Host-only check of mxgemm_run_fused's arguments (no device call). */
+int mxgemm_validate_fused(int fmtA, int fmtB, int layout,
+                          const void *A, const void *sA, const void *B, const void *sB,
+                          const void *D, int64_t M, int64_t N, int64_t K,
+                          const void *bias, int activation);
+
+/*
  * grouped_fp8_gemm_run -- grouped groupwise FP8 GEMM (one GEMM per group of
  * rows, e.g. per expert): "Add FlyDSL grouped groupwise FP8 GEMM for ROCm"
  * (PR body: E4M3 X and W with FP32 1x128 activation and 128x128 weight

@@ -141,3 +141,27 @@ def test_package_has_no_cpu_fallback():
     for f in os.listdir(os.path.join(ROOT, "block_scaled_precision_03_amd")):
         if f.endswith(".py"):
             assert "import oracle" not in open(os.path.join(ROOT, "block_scaled_precision_03_amd", f)).read()
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 0, 0, P, P, P, P, P, 256, 256, 256, P, 2), 0),           # MX NT, bias + GELU
+    ((16, 17, 0, P, P, P, P, P, 256, 256, 256, None, 3), 0),      # tensor-wise NT, SiLU alone
+    ((4, 0x104, 0, P, P, P, P, P, 256, 256, 256, P, 1), 0),       # FP4 preshuffled, bias + ReLU
+    ((0, 0, 0, P, P, P, P, P, 256, 256, 256, P, 4), -1),          # unknown activation
+    ((0, 0, 0, P, P, P, P, P, 256, 256, 256, None, -1), -1),
+    ((0, 0, 1, P, P, P, P, P, 256, 256, 256, P, 0), -2),          # bias: NT only
+    ((16, 17, 2, P, P, P, P, P, 256, 256, 256, None, 1), -2),     # activation: NT only
+    ((16, 17, 2, P, P, P, P, P, 256, 256, 256, None, 0), 0),      # neither: any layout
+    ((0, 0, 0, P, P, P, P, P, 256, 255, 256, P, 0), -2),          # bias needs N even
+    ((0, 0, 0, P, P, P, P, P, 256, 256, 256, P + 2, 0), -3),      # misaligned bias
+    ((0, 0, 0, P, P, P, P, P, 256, 256, 100, P, 0), -2),          # mxgemm_run's own checks first
+])
+def test_validate_fused(args, expect):
+    m = _mx()
+    assert m.validate_fused(*args[:11], bias=args[11], activation=args[12]) == expect
+
+
+def test_fused_rejects_before_device_use():
+    lib = _mx().lib()
+    assert lib.mxgemm_run_fused(0, 0, 1, P, P, P, P, P, 256, 256, 256, P, 0, None) == -2
+    assert lib.mxgemm_run_fused(0, 0, 0, P, P, P, P, P, 256, 256, 256, None, 9, None) == -1
