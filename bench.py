@@ -302,19 +302,45 @@ def time_calls(torch, call, reps=20, warmup=3):
 
 
 def small_bench(torch, synth, mxgemm, dev):
-    """MXFP8 NT 256 x 256 x 256 (one output tile, one workgroup): launch- and
-    latency-bound, so µs per call of back-to-back launches, not a fraction
-    of peak."""
+    """MXFP8 NT 256 x 256 x 256: launch- and latency-bound, so µs per call,
+    not a fraction of peak.  Two figures: back-to-back launches from the
+    host (each call's host-side launch included), and 20 calls captured in
+    one HIP graph and replayed (the device-side cost per call, as the pages
+    quote their grouped GEMMs); the graph's output is checked against the
+    eager call's."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     M = N = K = 256
     qa, sa = synth.quant_mx(synth.normal(synth.seed_for(1, 1), (M, K)), "e4m3")
     qb, sb = synth.quant_mx(synth.normal(synth.seed_for(1, 2), (N, K)), "e4m3")
     A, SA, B, SB = t(qa), t(sa), t(qb), t(sb)
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    us = time_calls(torch, lambda: mxgemm.run(mxgemm.MXFP8_E4M3, mxgemm.MXFP8_E4M3, mxgemm.NT, A, SA, B, SB,
-                                              D, M, N, K), reps=200, warmup=20)
-    log("mxfp8 256^3: %.2f us per call (back-to-back launches)" % us)
-    return {"M": M, "N": N, "K": K, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}
+    call = lambda: mxgemm.run(mxgemm.MXFP8_E4M3, mxgemm.MXFP8_E4M3, mxgemm.NT, A, SA, B, SB, D, M, N, K)
+    us = time_calls(torch, call, reps=200, warmup=20)
+    call()
+    torch.cuda.synchronize()
+    eager = D.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    calls = 20
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            call()
+    D.zero_()
+    torch.cuda.synchronize()
+    g_us = time_calls(torch, graph.replay, reps=20, warmup=3) / calls
+    same = bool(torch.equal(D.view(torch.int16), eager.view(torch.int16)))
+    kernel = ["persistent 256x256", "64x64 tiles"][mxgemm.dense_variant(mxgemm.MXFP8_E4M3, mxgemm.MXFP8_E4M3,
+                                                                        mxgemm.NT, M, N, K)]
+    log("mxfp8 256^3: %.2f us per call (back-to-back launches), %.2f us per call in a %d-call graph "
+        "(output %s the eager call's) [%s]" % (us, g_us, calls, "equals" if same else "DIFFERS FROM", kernel))
+    return {"M": M, "N": N, "K": K, "us": us, "graph_us_per_call": g_us, "graph_output_equal": same,
+            "kernel": kernel, "tflops": 2.0 * M * N * K / (g_us * 1e-6) / 1e12}
 
 
 def tensorwise_bench(torch, synth, mxgemm, dev):

@@ -9,8 +9,7 @@
 #include <stdio.h>
 
 #include "../../include/mxgemm.h"
-#include "dense.hpp"
-#include "grouped.hpp"
+#include "kernels.hpp"
 #include "preshuffle.hpp"
 #include "quant.hpp"
 #include "diag.hpp"
@@ -74,6 +73,26 @@ int cu_count() {
 
 }  // namespace
 
+// Kernel choice for a dense call from its static shapes: the persistent
+// 256 x 256 kernel, or (NT only) 64 x 64 tiles with one workgroup each when
+// the output has too few 256 x 256 tiles to occupy the compute units.
+// Estimated times, fitted to both kernels on MI355X (MXFP8, preshuffled B,
+// M x N from 256 x 256 to 4096 x 4096, K from 256 to 8192): the persistent
+// kernel ~6 us + 1.3 us per 128-K step per round of one tile per compute
+// unit; 64 x 64 tiles ~3 us + 0.72 us per step per round (their fragments
+// come straight from memory, three steps ahead, so a step costs a fraction
+// of a load's latency).  Over that sweep the choice is the faster kernel
+// everywhere but at 2048 x 2048 x 256 (2.7 us slower).
+extern "C" int mxgemm_dense_variant(int fmtA, int fmtB, int layout, int64_t M, int64_t N, int64_t K) {
+  (void)fmtA;
+  (void)fmtB;
+  if (layout != MXG_NT || M <= 0 || N <= 0 || K <= 0) return MXG_DENSE_TILE256;
+  const double cus = cu_count(), nst = (double)(K / 128);
+  const double t256 = 6.0 + std::ceil((double)(cdiv(M, DBM) * cdiv(N, DBN)) / cus) * 1.3 * nst;
+  const double t64 = 3.0 + std::ceil((double)(cdiv(M, SBM) * cdiv(N, SBN)) / cus) * 0.72 * nst;
+  return t64 < t256 ? MXG_DENSE_TILE64 : MXG_DENSE_TILE256;
+}
+
 extern "C" const char *mxgemm_status_string(int s) {
   switch (s) {
     case MXG_OK: return "ok";
@@ -90,7 +109,7 @@ extern "C" int mxgemm_init(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MXG_ERR_HIP;
   hipFuncAttributes attr;
-  if (hipFuncGetAttributes(&attr, (const void *)dense_kernel<F_E4M3, F_E4M3, SM_MX, false, false, false>) != hipSuccess)
+  if (hipFuncGetAttributes(&attr, (const void *)pick_dense_mx_a4(F_E4M3, MXG_NT, false, false)) != hipSuccess)
     return MXG_ERR_HIP;
   (void)cu_count();
   return MXG_OK;
@@ -135,54 +154,13 @@ extern "C" int mxgemm_validate(int fmtA, int fmtB, int layout, const void *A, co
 }
 
 namespace {
-// Kernel selection for the dense path.
-typedef void (*dense_fn)(DenseArgs);
-
-template <int FA, int FB>
-dense_fn pick_layout(bool mx, int layout, bool psb, bool fuse) {
-  if (fuse) {
-    // bias / activation epilogue: the forward (NT) kernels
-    if (layout != MXG_NT) return nullptr;
-    if constexpr (FA == F_E2M1 || FB == F_E2M1) {
-      if (!mx) return nullptr;
-      return psb ? dense_kernel<FA, FB, SM_MX, false, false, true, true> : dense_kernel<FA, FB, SM_MX, false, false, false, true>;
-    } else if (mx) {
-      return psb ? dense_kernel<FA, FB, SM_MX, false, false, true, true> : dense_kernel<FA, FB, SM_MX, false, false, false, true>;
-    } else {
-      return psb ? dense_kernel<FA, FB, SM_TENSOR, false, false, true, true>
-                 : dense_kernel<FA, FB, SM_TENSOR, false, false, false, true>;
-    }
-  }
-  if constexpr (FA == F_E2M1 || FB == F_E2M1) {
-    if (!mx || layout != MXG_NT) return nullptr;
-    return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
-  } else if (mx) {
-    // MX scales are blocked along K whatever the code layout, so the
-    // transposed variants load them exactly as NT does.
-    switch (layout) {
-      case MXG_NT:
-        return psb ? dense_kernel<FA, FB, SM_MX, false, false, true> : dense_kernel<FA, FB, SM_MX, false, false, false>;
-      case MXG_NN: return dense_kernel<FA, FB, SM_MX, false, true, false>;
-      case MXG_TN: return dense_kernel<FA, FB, SM_MX, true, true, false>;
-      default: return nullptr;
-    }
-  } else {
-    switch (layout) {
-      case MXG_NT:
-        return psb ? dense_kernel<FA, FB, SM_TENSOR, false, false, true> : dense_kernel<FA, FB, SM_TENSOR, false, false, false>;
-      case MXG_NN: return dense_kernel<FA, FB, SM_TENSOR, false, true, false>;
-      case MXG_TN: return dense_kernel<FA, FB, SM_TENSOR, true, true, false>;
-      default: return nullptr;
-    }
-  }
-}
-
+// Kernel selection for the dense path (the instantiations live in the k_*.hip
+// translation units).
 dense_fn pick_dense(int ea, int eb, bool mx, int layout, bool psb, bool fuse) {
-  if (ea == F_E2M1 && eb == F_E2M1) return mx ? pick_layout<F_E2M1, F_E2M1>(true, layout, psb, fuse) : nullptr;
-  if (ea == F_E4M3 && eb == F_E4M3) return pick_layout<F_E4M3, F_E4M3>(mx, layout, psb, fuse);
-  if (ea == F_E4M3 && eb == F_E5M2) return pick_layout<F_E4M3, F_E5M2>(mx, layout, psb, fuse);
-  if (ea == F_E5M2 && eb == F_E4M3) return pick_layout<F_E5M2, F_E4M3>(mx, layout, psb, fuse);
-  if (ea == F_E5M2 && eb == F_E5M2) return pick_layout<F_E5M2, F_E5M2>(mx, layout, psb, fuse);
+  if (ea == F_E2M1 || eb == F_E2M1)
+    return (ea == F_E2M1 && eb == F_E2M1 && mx) ? pick_dense_fp4(layout, psb, fuse) : nullptr;
+  if (ea == F_E4M3) return mx ? pick_dense_mx_a4(eb, layout, psb, fuse) : pick_dense_tw_a4(eb, layout, psb, fuse);
+  if (ea == F_E5M2) return mx ? pick_dense_mx_a5(eb, layout, psb, fuse) : pick_dense_tw_a5(eb, layout, psb, fuse);
   return nullptr;
 }
 
@@ -215,7 +193,8 @@ int run_dense(int fmtA, int fmtB, int layout, const void *A, const void *sA, con
   }
   const bool psb = (fmtB & MXG_PRESHUFFLED) != 0;
   const FmtInfo fa = fmt_info(fmtA), fb = fmt_info(fmtB & ~MXG_PRESHUFFLED);
-  dense_fn fn = pick_dense(fa.elem, fb.elem, fa.mx, layout, psb, fuse);
+  const bool small = mxgemm_dense_variant(fmtA, fmtB, layout, M, N, K) == MXG_DENSE_TILE64;
+  dense_fn fn = small ? pick_small(fa.elem, fb.elem, fa.mx, psb, fuse) : pick_dense(fa.elem, fb.elem, fa.mx, layout, psb, fuse);
   if (!fn) return MXG_ERR_UNSUPPORTED;
   const bool fp4 = fa.elem == F_E2M1;
   DenseArgs a = {};
@@ -231,12 +210,17 @@ int run_dense(int fmtA, int fmtB, int layout, const void *A, const void *sA, con
   a.b_bytes = psb ? mxgemm_preshuffle_b_bytes(fmtB & ~MXG_PRESHUFFLED, N, K) : (fp4 ? N * K / 2 : N * K);
   a.sa_bytes = fa.mx ? M * (K / 32) : 4;
   a.sb_bytes = fb.mx ? (psb ? mxgemm_preshuffle_scales_bytes(N, K) : N * (K / 32)) : 4;
-  a.tiles_m = (int)cdiv(M, DBM);
-  a.tiles_n = (int)cdiv(N, DBN);
+  a.tiles_m = (int)cdiv(M, small ? SBM : DBM);
+  a.tiles_n = (int)cdiv(N, small ? SBN : DBN);
   a.bias = (const uint16_t *)bias;
   a.act = act;
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  if (small) {
+    // one workgroup of four waves per 64 x 64 tile
+    hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+    return launch_status();
+  }
   // Persistent grid: one workgroup per compute unit, each walking its tiles.
   const int64_t blocks = tiles < cu_count() ? tiles : cu_count();
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(DNW8 * 64), 0, stream, a);
@@ -342,12 +326,8 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   // persistent kernels: GS_OCC workgroups per compute unit (fewer if fewer tiles)
   const unsigned P = (unsigned)std::min<int64_t>(blocks, (int64_t)GS_OCC * cu_count());
   const bool pre = b_preshuffled != 0;
-  if (variant == MXG_GROUPED_STREAM64) {
-    if (pre) hipLaunchKernelGGL((grouped_stream_kernel<true, 64, 2, 2>), dim3(P), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((grouped_stream_kernel<false, 64, 2, 2>), dim3(P), dim3(256), 0, stream, a);
-  } else if (variant == MXG_GROUPED_STREAM128) {
-    if (pre) hipLaunchKernelGGL((grouped_stream_kernel<true, 128, 1, 2>), dim3(P), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((grouped_stream_kernel<false, 128, 1, 2>), dim3(P), dim3(256), 0, stream, a);
+  if (variant == MXG_GROUPED_STREAM64 || variant == MXG_GROUPED_STREAM128) {
+    hipLaunchKernelGGL(pick_grouped_stream(BM, pre), dim3(P), dim3(256), 0, stream, a);
   } else {
     // matrix-core regime: the dense pipeline with groupwise scales, 256 x
     // 256 tiles, one persistent workgroup per compute unit
@@ -371,8 +351,7 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
     const int64_t tiles = (int64_t)d.tiles_m * d.tiles_n;
     if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
     const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
-    if (pre) hipLaunchKernelGGL((grouped_dense_kernel<true>), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
-    else hipLaunchKernelGGL((grouped_dense_kernel<false>), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
+    hipLaunchKernelGGL(pick_grouped_dense(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
   }
   return launch_status();
 }

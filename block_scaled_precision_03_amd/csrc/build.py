@@ -13,7 +13,8 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libmxgemm.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip"]
+SOURCES = ["api.hip", "k_dense_mx4.hip", "k_dense_mx5.hip", "k_dense_tw4.hip", "k_dense_tw5.hip",
+           "k_dense_fp4.hip", "k_small.hip", "k_grouped.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

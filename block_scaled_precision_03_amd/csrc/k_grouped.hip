@@ -1,0 +1,14 @@
+// The grouped groupwise FP8 kernels.
+#include "kernels.hpp"
+
+namespace mxg {
+dense_fn pick_grouped_dense(bool psb) {
+  return psb ? grouped_dense_kernel<true> : grouped_dense_kernel<false>;
+}
+
+grouped_fn pick_grouped_stream(int bm, bool psb) {
+  if (bm == 64) return psb ? grouped_stream_kernel<true, 64, 2, 2> : grouped_stream_kernel<false, 64, 2, 2>;
+  if (bm == 128) return psb ? grouped_stream_kernel<true, 128, 1, 2> : grouped_stream_kernel<false, 128, 1, 2>;
+  return nullptr;
+}
+}  // namespace mxg

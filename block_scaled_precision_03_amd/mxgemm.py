@@ -20,10 +20,11 @@ NT, NN, TN = 0, 1, 2
 GROUPED_MAX_G = 1024
 GROUPED_STREAM64, GROUPED_TILED, GROUPED_STREAM128 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3
+DENSE_TILE256, DENSE_TILE64 = 0, 1
 
 EXPORTS = (
     "mxgemm_init", "mxgemm_status_string", "mxgemm_run", "mxgemm_validate",
-    "mxgemm_run_fused", "mxgemm_validate_fused",
+    "mxgemm_run_fused", "mxgemm_validate_fused", "mxgemm_dense_variant",
     "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate", "grouped_fp8_gemm_variant",
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
@@ -45,6 +46,8 @@ _lib.mxgemm_run.restype = _i
 _lib.mxgemm_run.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]
 _lib.mxgemm_validate.restype = _i
 _lib.mxgemm_validate.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64]
+_lib.mxgemm_dense_variant.restype = _i
+_lib.mxgemm_dense_variant.argtypes = [_i, _i, _i, _i64, _i64, _i64]
 _lib.mxgemm_run_fused.restype = _i
 _lib.mxgemm_run_fused.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _p]
 _lib.mxgemm_validate_fused.restype = _i
@@ -124,6 +127,12 @@ def run(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, stream=None):
 def validate(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K):
     return _lib.mxgemm_validate(fmtA, fmtB, layout, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB),
                                 _ptr(D), M, N, K)
+
+
+def dense_variant(fmtA, fmtB, layout, M, N, K):
+    """DENSE_TILE256 or DENSE_TILE64: the kernel run / run_fused launch for
+    these shapes on the current device."""
+    return _lib.mxgemm_dense_variant(fmtA, fmtB, layout, M, N, K)
 
 
 def run_fused(fmtA, fmtB, layout, A, sA, B, sB, D, M, N, K, bias=None, activation=ACT_NONE,

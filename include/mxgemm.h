@@ -126,6 +126,20 @@ int mxgemm_run(int fmtA, int fmtB, int layout,
                const void *A, const void *sA, const void *B, const void *sB,
                void *D, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * mxgemm_dense_variant: which kernel mxgemm_run / mxgemm_run_fused launch
+ * for these static shapes on the current device: MXG_DENSE_TILE256, the
+ * persistent kernel with 256 x 256 tiles, or MXG_DENSE_TILE64 (NT only),
+ * 64 x 64 tiles with one workgroup each, for outputs too small to occupy
+ * the device with 256 x 256 tiles ("Add FlyDSL grouped groupwise FP8 GEMM
+ * for ROCm", Tile selection and Performance: the tile is picked per shape,
+ * and narrow outputs lose when they cannot produce enough tiles).  Both
+ * compute the same function with the same per-element sequence of
+ * matrix-core instructions, so their outputs are identical.  Never fails.
+ */
+enum { MXG_DENSE_TILE256 = 0, MXG_DENSE_TILE64 = 1 };
+int mxgemm_dense_variant(int fmtA, int fmtB, int layout, int64_t M, int64_t N, int64_t K);
+
 /* Host-only check of mxgemm_run's arguments (no device call).  Returns the
  * status mxgemm_run would return before enqueueing anything. */
 int mxgemm_validate(int fmtA, int fmtB, int layout,

@@ -22,6 +22,9 @@ NT, NN, TN = 0, 1, 2
 
 
 def _sampled(layout, opA, opB, M, N, K, what, preshuffle_b=False, count=3000):
+    from block_scaled_precision_03_amd import mxgemm
+    # these shapes run the persistent kernel (not the 64 x 64 one)
+    assert mxgemm.dense_variant(opA.lib_fmt, opB.lib_fmt, layout, M, N, K) == mxgemm.DENSE_TILE256
     D = H.run_dense(layout, opA, opB, M, N, K, preshuffle_b=preshuffle_b)
     d = H.bf16_to_f64(D)
     rng = np.random.default_rng(M * 7 + N * 3 + K)

@@ -195,16 +195,25 @@ def sgpr_hazards(f):
 
 
 def _disassemble(tmp_path, lib=LIB):
+    """Every gfx950 code object of the library (one offload bundle per
+    translation unit, concatenated in the .hip_fatbin section), parsed."""
     fatbin = tmp_path / "fatbin.bin"
-    code = tmp_path / "gfx950.co"
     subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section=.hip_fatbin=%s" % fatbin,
                     lib, str(tmp_path / "lib.copy")], check=True, capture_output=True)
-    subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
-                    "--input=%s" % fatbin, "--targets=%s" % TARGET, "--output=%s" % code],
-                   check=True, capture_output=True)
-    out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", str(code)],
-                         check=True, capture_output=True, text=True).stdout
-    return _parse(out)
+    data = fatbin.read_bytes()
+    starts = [m.start() for m in re.finditer(re.escape(b"__CLANG_OFFLOAD_BUNDLE__"), data)]
+    funcs = []
+    for i, st in enumerate(starts):
+        part = tmp_path / ("bundle%d.bin" % i)
+        part.write_bytes(data[st:starts[i + 1] if i + 1 < len(starts) else len(data)])
+        code = tmp_path / ("gfx950_%d.co" % i)
+        subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
+                        "--input=%s" % part, "--targets=%s" % TARGET, "--output=%s" % code],
+                       check=True, capture_output=True)
+        out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", str(code)],
+                             check=True, capture_output=True, text=True).stdout
+        funcs += _parse(out)
+    return funcs
 
 
 def test_store_checker_flags_a_planted_hazard():
@@ -266,3 +275,8 @@ def test_library_has_no_valu_sgpr_to_vmem_hazard(tmp_path):
     assert dmas > 0, "no LDS DMA found: disassembly not parsed"
     bad = [(f.name, h) for f in funcs for h in sgpr_hazards(f)]
     assert not bad, "%d VALU-SGPR -> vector-memory hazards, e.g. %s" % (len(bad), bad[:3])
+    # every translation unit's kernels were seen
+    names = " ".join(f.name for f in funcs)
+    for k in ("dense_kernel", "dense_small_kernel", "grouped_dense_kernel", "grouped_stream_kernel",
+              "quant_mx_kernel", "preshuffle_b_kernel"):
+        assert k in names, k
