@@ -317,7 +317,7 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   a.N = N;
   a.K = K;
   a.G = G;
-  const int variant = grouped_fp8_gemm_variant(G, totM, N, K);
+  const int variant = grouped_fp8_gemm_variant(G, totM, N, K, b_preshuffled);
   const int BM = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
   const int BN = variant == MXG_GROUPED_TILED ? 128 : 64;
   a.tiles_n = (int)(N / BN);
@@ -356,8 +356,98 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   return launch_status();
 }
 
+namespace {
+// Static tile table of the grouped GEMM, keyed as "Add FlyDSL grouped
+// groupwise FP8 GEMM for ROCm" (Tile selection) keys its autotuned winners:
+// (nextPow2(totM), N, K, b_preshuffled), here for G = 8 (the pages' G).
+// Each entry is the fastest of the three kernels measured on MI355X at
+// totM = 2^log2m with the benchmark's kind of m_sizes (one empty group,
+// uneven cuts); the times after each entry are 64 x 64 streaming,
+// 128 x 64 streaming and 256 x 256 dense-pipeline, in that order.
+struct GroupedTile {
+  int32_t N, K;
+  int8_t log2m, pre, variant;
+};
+const GroupedTile GROUPED_TILES[] = {
+    {1280, 8192, 7, 0, 0},   //   27.0   42.1  103.6 us
+    {1280, 8192, 7, 1, 0},   //   27.0   42.3  104.2 us
+    {1280, 8192, 8, 0, 0},   //   27.6   42.4  105.8 us
+    {1280, 8192, 8, 1, 0},   //   27.1   42.9  106.9 us
+    {1280, 8192, 9, 0, 0},   //   31.9   43.2  122.7 us
+    {1280, 8192, 9, 1, 0},   //   31.9   43.7  123.3 us
+    {1280, 8192, 10, 0, 0},   //   34.4   44.3  128.9 us
+    {1280, 8192, 10, 1, 0},   //   35.0   45.2  130.2 us
+    {1280, 8192, 11, 0, 2},   //   56.6   53.6  120.8 us
+    {1280, 8192, 11, 1, 2},   //   57.4   55.2  123.5 us
+    {1280, 8192, 12, 0, 2},   //   99.0   93.7  133.5 us
+    {1280, 8192, 12, 1, 2},   //  101.9   95.7  134.3 us
+    {1280, 8192, 13, 0, 1},   //  211.2  191.1  141.3 us
+    {1280, 8192, 13, 1, 1},   //  208.4  179.1  146.0 us
+    {1280, 8192, 14, 0, 1},   //  409.6  361.4  265.3 us
+    {1280, 8192, 14, 1, 1},   //  408.8  352.6  267.0 us
+    {2048, 7168, 7, 0, 0},   //   25.1   38.3   92.5 us
+    {2048, 7168, 7, 1, 0},   //   25.3   39.1   94.4 us
+    {2048, 7168, 8, 0, 0},   //   26.0   38.7   95.8 us
+    {2048, 7168, 8, 1, 0},   //   26.2   39.2   97.6 us
+    {2048, 7168, 9, 0, 0},   //   30.7   39.7  113.3 us
+    {2048, 7168, 9, 1, 0},   //   31.5   40.6  115.0 us
+    {2048, 7168, 10, 0, 2},   //   49.7   47.1  123.1 us
+    {2048, 7168, 10, 1, 2},   //   50.2   48.6  124.3 us
+    {2048, 7168, 11, 0, 0},   //   77.5   83.6  117.0 us
+    {2048, 7168, 11, 1, 0},   //   76.4   82.5  116.4 us
+    {2048, 7168, 12, 0, 2},   //  131.6  126.9  133.0 us
+    {2048, 7168, 12, 1, 2},   //  134.8  127.6  131.9 us
+    {2048, 7168, 13, 0, 1},   //  290.3  264.4  232.4 us
+    {2048, 7168, 13, 1, 1},   //  291.0  258.6  231.8 us
+    {2048, 7168, 14, 0, 1},   //  565.5  506.9  349.4 us
+    {2048, 7168, 14, 1, 1},   //  563.4  496.6  346.4 us
+    {4096, 4096, 7, 0, 0},   //   22.2   29.0   59.6 us
+    {4096, 4096, 7, 1, 0},   //   22.4   29.6   60.4 us
+    {4096, 4096, 8, 0, 0},   //   22.6   28.9   61.8 us
+    {4096, 4096, 8, 1, 0},   //   22.6   30.0   63.8 us
+    {4096, 4096, 9, 0, 2},   //   37.1   31.4   79.4 us
+    {4096, 4096, 9, 1, 2},   //   37.5   32.2   81.2 us
+    {4096, 4096, 10, 0, 0},   //   47.4   50.6   90.9 us
+    {4096, 4096, 10, 1, 0},   //   47.4   50.9   90.9 us
+    {4096, 4096, 11, 0, 0},   //   81.8   87.7   84.7 us
+    {4096, 4096, 11, 1, 0},   //   82.1   88.4   84.5 us
+    {4096, 4096, 12, 0, 2},   //  157.7  144.3  151.9 us
+    {4096, 4096, 12, 1, 2},   //  161.1  142.2  151.0 us
+    {4096, 4096, 13, 0, 1},   //  337.2  301.1  233.3 us
+    {4096, 4096, 13, 1, 1},   //  345.7  290.5  231.0 us
+    {4096, 4096, 14, 0, 1},   //  664.2  558.7  384.0 us
+    {4096, 4096, 14, 1, 1},   //  659.7  565.7  376.5 us
+    {7168, 2304, 7, 0, 0},   //   25.3   32.8   40.7 us
+    {7168, 2304, 7, 1, 0},   //   25.1   33.7   41.7 us
+    {7168, 2304, 8, 0, 0},   //   25.6   33.1   43.1 us
+    {7168, 2304, 8, 1, 0},   //   25.6   34.0   44.3 us
+    {7168, 2304, 9, 0, 0},   //   35.3   35.7   61.0 us
+    {7168, 2304, 9, 1, 0},   //   35.9   36.8   62.6 us
+    {7168, 2304, 10, 0, 2},   //   50.0   48.4   70.2 us
+    {7168, 2304, 10, 1, 2},   //   49.2   48.1   70.3 us
+    {7168, 2304, 11, 0, 2},   //   91.1   89.2  106.0 us
+    {7168, 2304, 11, 1, 2},   //   91.0   90.6  106.3 us
+    {7168, 2304, 12, 0, 1},   //  177.2  146.6  140.0 us
+    {7168, 2304, 12, 1, 1},   //  175.8  160.0  139.5 us
+    {7168, 2304, 13, 0, 1},   //  363.6  318.0  213.3 us
+    {7168, 2304, 13, 1, 1},   //  353.9  315.4  212.6 us
+    {7168, 2304, 14, 0, 1},   //  693.1  611.4  400.2 us
+    {7168, 2304, 14, 1, 1},   //  686.1  597.0  390.9 us
+};
+
+int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
+  if (G != 8 || totM <= 0) return -1;
+  int log2m = 0;
+  while ((1ll << log2m) < totM) ++log2m;          // nextPow2(totM) = 2^log2m
+  for (const GroupedTile &t : GROUPED_TILES)
+    if (t.N == N && t.K == K && t.log2m == log2m && t.pre == (pre != 0)) return t.variant;
+  return -1;
+}
+}  // namespace
+
 // Kernel choice from the static shapes (the host never reads m_sizes): the
-// estimated time of each, from upper bounds of the tile counts.
+// static table above when it lists the shape, else the estimated time of
+// each kernel from upper bounds of the tile counts.
 //  - persistent, 64 x 64 or 128 x 64 tiles (weight streaming): ~0.6 or
 //    ~1.0 us per 128-K tile step per workgroup, GS_OCC workgroups per
 //    compute unit walking all tile steps evenly;
@@ -365,12 +455,12 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
 //    one tile per compute unit per round, ~1.67 us per 128-K step plus
 //    ~20 us per round (pipeline start, epilogue);
 // each at least the weights' bytes at ~5 TB/s.  The constants are fitted to
-// the three kernels' times on MI355X (preshuffled weights, G = 8) over
-// totM 512 .. 16384 and (N, K) = (2048, 7168), (7168, 2304), (4096, 4096),
-// (1280, 8192); at every one of those 24 points the choice is the fastest
-// kernel or within 16% of it.
-extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K) {
+// the table's measurements; at 50 of its 64 points the estimate picks the
+// table's kernel, and at the other 14 one within 18% of it.
+extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K, int b_preshuffled) {
   if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM64;
+  const int listed = grouped_table_variant(G, totM, N, K, b_preshuffled);
+  if (listed >= 0) return listed;
   const double cus = cu_count(), nst = (double)(K / 128);
   const double wbytes = (double)G * (double)N * (double)K;
   const double wmin = wbytes / 5.0e6;

@@ -57,7 +57,7 @@ _lib.grouped_fp8_gemm_run.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i
 _lib.grouped_fp8_gemm_validate.restype = _i
 _lib.grouped_fp8_gemm_validate.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i]
 _lib.grouped_fp8_gemm_variant.restype = _i
-_lib.grouped_fp8_gemm_variant.argtypes = [_i, _i64, _i64, _i64]
+_lib.grouped_fp8_gemm_variant.argtypes = [_i, _i64, _i64, _i64, _i]
 _lib.mxgemm_preshuffle_b_bytes.restype = _i64
 _lib.mxgemm_preshuffle_b_bytes.argtypes = [_i, _i64, _i64]
 _lib.mxgemm_preshuffle_b.restype = _i
@@ -160,10 +160,10 @@ def grouped_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_pres
                                           int(bool(b_preshuffled)))
 
 
-def grouped_variant(G, totM, N, K):
+def grouped_variant(G, totM, N, K, b_preshuffled=True):
     """GROUPED_STREAM64, GROUPED_STREAM128 or GROUPED_TILED: the kernel
     grouped_run launches for these shapes on the current device."""
-    return _lib.grouped_fp8_gemm_variant(G, totM, N, K)
+    return _lib.grouped_fp8_gemm_variant(G, totM, N, K, int(bool(b_preshuffled)))
 
 
 def preshuffle_b_bytes(fmtB, N, K):

@@ -225,16 +225,20 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
 
 /*
  * grouped_fp8_gemm_variant: which kernel grouped_fp8_gemm_run launches for
- * these static shapes on the current device (the choice never depends on
- * m_sizes' contents): MXG_GROUPED_STREAM64 or MXG_GROUPED_STREAM128, the
- * persistent kernel with 64 x 64 or 128 x 64 tiles for the weight-streaming
- * regime (few rows per group), or MXG_GROUPED_TILED, 128 x 128 tiles for the
- * matrix-core regime.  All compute the same function; their results may
- * differ in the last bit of a BF16 output only where their FP32 sums do.
- * Never fails.
+ * these static shapes (and b_preshuffled) on the current device (the
+ * choice never depends on m_sizes' contents): MXG_GROUPED_STREAM64 or
+ * MXG_GROUPED_STREAM128, the persistent kernel with 64 x 64 or 128 x 64
+ * tiles for the weight-streaming regime (few rows per group), or
+ * MXG_GROUPED_TILED, the persistent 256 x 256 kernel on the dense pipeline
+ * for the matrix-core regime.  A static table keyed on (nextPow2(totM), N,
+ * K, b_preshuffled) decides for the shapes it lists ("Add FlyDSL grouped
+ * groupwise FP8 GEMM for ROCm", Tile selection: the same key), an estimate
+ * of each kernel's time otherwise.  All compute the same function; their
+ * results may differ in the last bit of a BF16 output only where their FP32
+ * sums do.  Never fails.
  */
 enum { MXG_GROUPED_STREAM64 = 0, MXG_GROUPED_TILED = 1, MXG_GROUPED_STREAM128 = 2 };
-int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K);
+int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K, int b_preshuffled);
 
 /*
  * Preshuffle: one-time re-layout of a B operand (weights) into the order in

@@ -206,7 +206,7 @@ def _grouped_samples(m_sizes, totM, N, seed, count=3000):
 def test_grouped_full_size(si):
     totM, N, K = C4[si]
     m_sizes, XQ, xs, WQ, ws = _grouped_full_inputs(si, totM, N, K)
-    pres = (True, False) if totM == 1024 else (True,)
+    pres = (True, False)
     im, inn = _grouped_samples(m_sizes, totM, N, 100 + si)
     ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
     for pre in pres:
