@@ -39,7 +39,7 @@ PEAK_MXFP8_TFLOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 FLOP/clk/CU (dense)
 PEAK_FP8_TFLOPS = 5033.2
 PEAK_MXFP4_TFLOPS = 10066.3
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_mxfp8_nt_psb_llm_shapes_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_mxfp8_nt_psb_llm_shapes_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_03_amd", "csrc", f)
                   for f in ("common.hpp", "dense.hpp", "api.hip")]
 C3_CASES = [("fwd", 0, 8192, 11008, 4096), ("dgrad", 1, 8192, 4096, 11008),
@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--plain-b", action="store_true", help="time with plain (not preshuffled) B")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the tensor-wise FP8 and MXFP4 measurements")
+    ap.add_argument("--profile-leg", choices=("grouped", "mxfp4", "mx_backward"),
+                    help="only launch one leg's kernels, three times per shape (no graphs, no "
+                         "cold rotation): the short program a profiler's counter passes run")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB read + 256 MiB write elementwise kernel "
                          "(the calibration of the HBM byte counters)")
@@ -542,6 +545,64 @@ def fused_bench(torch, synth, mxgemm, dev):
     return res
 
 
+def profile_leg(torch, synth, mxgemm, dev, leg, launches=3):
+    """Launch one leg's kernels `launches` times per shape, in a fixed order
+    (for counter collection: the dispatches of each kernel and shape are
+    consecutive), and print the order as one JSON line."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    order = []
+    if leg == "grouped":
+        G = 8
+        for si, (totM, N, K) in enumerate(C4_SHAPES):
+            m_sizes = synth.m_sizes_for(totM, G, synth.seed_for(4, 4, si))
+            xq, xsc = synth.quant_group_act(synth.normal(synth.seed_for(4, 1, si), (totM, K)), m_sizes)
+            wq, wsc = synth.quant_group_weight(synth.normal(synth.seed_for(4, 2, si), (G, N, K), 0.02))
+            W = t(wq)
+            Wp = torch.empty_like(W)
+            mxgemm.grouped_preshuffle_b(G, W, Wp, N, K)
+            torch.cuda.synchronize()
+            dm, dx, dxs, dws = t(m_sizes), t(xq), t(xsc), t(wsc)
+            D = torch.empty((totM, N), dtype=torch.bfloat16, device=dev)
+            for _ in range(launches):
+                mxgemm.grouped_run(G, dm, dx, dxs, Wp, dws, D, totM, N, K, b_preshuffled=True)
+            torch.cuda.synchronize()
+            order.append({"totM": totM, "N": N, "K": K, "G": G,
+                          "nonempty_groups": int((m_sizes > 0).sum()),
+                          "variant": mxgemm.grouped_variant(G, totM, N, K, True)})
+    elif leg == "mxfp4":
+        M = N = K = 8192
+        qa, sa = synth.quant_mx(synth.normal(synth.seed_for(5, 1), (M, K)), "e2m1")
+        qb, sb = synth.quant_mx(synth.normal(synth.seed_for(5, 2), (N, K)), "e2m1")
+        B = torch.empty(mxgemm.preshuffle_b_bytes(mxgemm.MXFP4_E2M1, N, K), dtype=torch.uint8, device=dev)
+        SB = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=dev)
+        mxgemm.preshuffle_b(mxgemm.MXFP4_E2M1, mxgemm.NT, t(qb), B, N, K)
+        mxgemm.preshuffle_scales(t(sb), SB, N, K)
+        A, SA = t(qa), t(sa)
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            mxgemm.run(mxgemm.MXFP4_E2M1, mxgemm.MXFP4_E2M1 | mxgemm.PRESHUFFLED, mxgemm.NT, A, SA, B, SB, D, M, N, K)
+        torch.cuda.synchronize()
+        order.append({"M": M, "N": N, "K": K, "fmt": "e2m1"})
+    elif leg == "mx_backward":
+        for idx, (name, layout, M, N, K) in enumerate(C3_CASES):
+            if layout == mxgemm.NT:
+                continue
+            qa, sa = synth.quant_mx(synth.normal(synth.seed_for(6, 1, idx), (M, K)), "e5m2")
+            qb, sb = synth.quant_mx(synth.normal(synth.seed_for(6, 2, idx), (N, K),
+                                                 0.02 if name == "dgrad" else 1.0), "e4m3")
+            if layout == mxgemm.TN:
+                qa = qa.T
+            A, SA, B, SB = t(qa), t(sa), t(qb.T), t(sb)
+            D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(launches):
+                mxgemm.run(mxgemm.MXFP8_E5M2, mxgemm.MXFP8_E4M3, layout, A, SA, B, SB, D, M, N, K)
+            torch.cuda.synchronize()
+            order.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "M": M, "N": N, "K": K})
+    print(json.dumps({"profile_leg": leg, "launches_per_shape": launches, "order": order}), flush=True)
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -657,6 +718,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     mxgemm.init()
+    if args.profile_leg:
+        profile_leg(torch, synth, mxgemm, dev, args.profile_leg)
+        return
     pre = not args.plain_b
     log("generating MXFP8 inputs ...")
     t0 = time.perf_counter()
