@@ -132,7 +132,10 @@ extern "C" int mxgemm_validate(int fmtA, int fmtB, int layout, const void *A, co
   if (fa.mx != fb.mx) return MXG_ERR_UNSUPPORTED;
   if ((fa.elem == F_E2M1) != (fb.elem == F_E2M1)) return MXG_ERR_UNSUPPORTED;
   const bool fp4 = fa.elem == F_E2M1;
-  if (fp4 && layout != MXG_NT) return MXG_ERR_UNSUPPORTED;
+  // A transposed packed E2M1 operand holds two columns per byte: its
+  // contiguous dimension must fill whole 16-byte pieces.
+  if (fp4 && layout == MXG_TN && M % 32 != 0) return MXG_ERR_UNSUPPORTED;
+  if (fp4 && layout != MXG_NT && N % 32 != 0) return MXG_ERR_UNSUPPORTED;
   if (psb && layout != MXG_NT) return MXG_ERR_UNSUPPORTED;
   if (K % (fp4 ? 256 : 128) != 0) return MXG_ERR_UNSUPPORTED;
   const int64_t kb = fp4 ? K / 2 : K;

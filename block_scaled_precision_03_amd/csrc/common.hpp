@@ -155,6 +155,13 @@ __device__ inline v2i lds_read_tr8(const void *p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)p);
 }
 
+// ds_read_b64_tr_b4: each group of 16 lanes reads 8 bytes per lane (16
+// nibbles) and receives the 16 x 16 nibble transpose: nibble j of lane i's
+// result is nibble i of what lane j of its group read.
+__device__ inline v2i lds_read_tr4(const void *p) {
+  return __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i *)p);
+}
+
 // D += sum over a 16x16x128 block: first operand rows = output rows.
 template <int FX, int FY>
 __device__ inline v4f mfma_scaled(const v8i &x, const v8i &y, const v4f &c, int sx, int sy) {

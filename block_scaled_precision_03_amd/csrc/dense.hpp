@@ -17,7 +17,7 @@
 // inline assembly with explicit waits, into XOR-swizzled rows so that the
 // fragment reads are free of bank conflicts.  Transposed operands (the 'T'
 // side of NN/TN) are kept in LDS k-major and read with the transposing
-// ds_read_b64_tr_b8.  The grid is persistent (one workgroup per compute
+// ds_read_b64_tr_b8 (packed E2M1: ds_read_b64_tr_b4).  The grid is persistent (one workgroup per compute
 // unit): the tiles of a workgroup share one K pipeline, the next tile's first
 // stage streams in during the current tile's last K step, and a finished
 // tile is stored from registers (BF16, 16-byte rows after a cross-lane
@@ -79,6 +79,15 @@ __device__ constexpr int kswz(int r) { return r & 6; }
 // clear) at 8-byte offset i % 2; a 4-bit XOR of j and q' spreads them over
 // all 32 eight-byte bank groups.
 __device__ constexpr int tswz(int kk) { return (kk & 7) | ((kk & 16) >> 1); }
+
+// Transposed packed E2M1 tiles (k-rows of 128 B: 256 columns, two per
+// byte): 16-byte piece p of k-row kk sits at p ^ fswz(kk).  A fragment read
+// (ds_read_b64_tr_b4) has the 32 lanes of a phase read 8 bytes at one
+// column chunk from k-rows k0 + i and k0 + 32 + i (i < 16); rows 128 B apart
+// split them over the two bank halves by parity, and fswz gives the 8 rows
+// of one parity in each 16-row run 8 distinct pieces, so at most two lanes
+// share a bank (the read half of a piece is the same for every lane).
+__device__ constexpr int fswz(int kk) { return (kk >> 1) & 7; }
 
 // K-contiguous operand rows [r0, r0+R) x bytes [128*st, 128*st+128).
 template <int R, int NW = DNW>
@@ -249,6 +258,11 @@ struct DenseLoop {
   static constexpr int BIAS_OFF = S_REG + 2 * SGROUP, BIAS_SLOT = DBN * 2;
   static constexpr int LDS_BYTES = BIAS_OFF + (FUSE ? 2 * BIAS_SLOT : 0);
   static constexpr int CGB = FP4 ? 4096 : 8192;
+  // Operand tile kinds in LDS: K-contiguous rows, transposed 8-bit k-rows,
+  // transposed packed E2M1 k-rows.
+  static constexpr int OP_K = 0, OP_T8 = 1, OP_T4 = 2;
+  static constexpr int OPA = TA ? (FP4 ? OP_T4 : OP_T8) : OP_K;
+  static constexpr int OPB = TB ? (FP4 ? OP_T4 : OP_T8) : OP_K;
   static constexpr bool PIN = !TA && !TB && (PSB || !MX || FP4);
 
   // Loop-invariant state.  Every global load of the loop is one buffer
@@ -279,8 +293,8 @@ struct DenseLoop {
     c.sk32 = p.K / 32;
     c.nks = p.K / 128;
     c.ngrp = (p.K + 511) / 512;
-    dma_offsets(TA, c.lane, c.w, c.KB, p.M, c.vo_a);
-    dma_offsets(TB, c.lane, c.w, c.KB, p.N, c.vo_b);
+    dma_offsets(OPA, c.lane, c.w, c.KB, p.M, c.vo_a);
+    dma_offsets(OPB, c.lane, c.w, c.KB, p.N, c.vo_b);
     c.vo_s = 0;
     if constexpr (MX) {
       if (c.w < 4 || !PSB) c.vo_s = (uint32_t)(c.lane * c.sk32);
@@ -308,8 +322,9 @@ struct DenseLoop {
     t.m0 = m0;
     t.n0 = n0;
     t.lim = id.lim;
-    // A: rows m0.. (K-contiguous) or columns m0.. of [K, M]; B likewise.
-    const int64_t abase = TA ? m0 : m0 * c.KB;
+    // A: rows m0.. (K-contiguous) or columns m0.. of [K, M] (packed E2M1:
+    // byte m0 / 2 of each k-row); B likewise.
+    const int64_t abase = TA ? (FP4 ? m0 / 2 : m0) : m0 * c.KB;
     t.ra = rsrc4(p.A + abase, clamp_records(p.a_bytes - abase));
     // Preshuffled B: the whole buffer (it holds every column group of every
     // 256-column tile, padding included); the offsets below stay inside it.
@@ -319,7 +334,7 @@ struct DenseLoop {
     int64_t bbase;
     if constexpr (GROUP) bbase = PSB ? ((int64_t)id.g * p.N + n0) / 64 * c.nks * CGB : ((int64_t)id.g * p.N + n0) * c.KB;
     else if constexpr (PSB) bbase = 0;
-    else bbase = TB ? n0 : n0 * c.KB;
+    else bbase = TB ? (FP4 ? n0 / 2 : n0) : n0 * c.KB;
     t.rb = rsrc4(p.B + bbase, clamp_records(p.b_bytes - bbase));
     t.rs = (u32x4){0u, 0u, 0u, 0u};
     t.soff = 0;
@@ -361,11 +376,18 @@ struct DenseLoop {
   //    4blk + lane/16; position c of k-row kk holds column chunk c ^ tswz(kk),
   //    so the lane reads chunk (lane%16) ^ tswz(4blk + lane/16), which
   //    depends on j%2 (vo[j%2]) and w%2.  Uniform part: (4blk + 128 st) * Rtot.
-  __device__ static inline void dma_offsets(bool transposed, int lane, int w, int64_t KB, int64_t Rtot,
+  //  transposed packed E2M1 (256 k-rows x 128 B, Rtot/2 bytes per k-row in
+  //    memory): DMA block blk covers k-rows 8blk + lane/8; position p of
+  //    k-row kk holds piece p ^ fswz(kk), which depends on blk%2 (vo[j%2]).
+  //    Uniform part: (8blk + 256 st) * Rtot/2.
+  __device__ static inline void dma_offsets(int kind, int lane, int w, int64_t KB, int64_t Rtot,
                                             uint32_t (&vo)[2]) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      if (transposed) {
+      if (kind == OP_T4) {
+        const int r8 = lane >> 3;
+        vo[par] = (uint32_t)(r8 * (Rtot / 2)) + (uint32_t)(((lane & 7) ^ fswz(8 * par + r8)) << 4);
+      } else if (kind == OP_T8) {
         // DMA j of wave w covers k-rows 16w + 4j .. +3 of the stage
         const int kk = 16 * (w & 1) + par * 4 + (lane >> 4);
         vo[par] = (uint32_t)((lane >> 4) * Rtot) + (uint32_t)(((lane & 15) ^ tswz(kk)) << 4);
@@ -380,13 +402,14 @@ struct DenseLoop {
   // address `tile`.  The whole offset goes through the range check (the
   // resource ends where the operand ends), so rows past M (N), and columns
   // past the end of a transposed operand's last k-row, read zeros.
-  template <bool T, int J0, int J1>
+  template <int KIND, int J0, int J1>
   __device__ static inline void load_tile(const Ctx &c, const u32x4 &r, const uint32_t (&vo)[2],
                                           int64_t KB, int64_t Rtot, int st, uint32_t tile) {
     const uint32_t base = tile + (uint32_t)c.w * 4096u;
     auto add = [&](int blk) {
-      return T ? (uint32_t)((4 * blk + 128 * (int64_t)st) * Rtot)
-               : (uint32_t)(blk * 8 * KB + 128 * (int64_t)st);
+      if constexpr (KIND == OP_T4) return (uint32_t)((8 * blk + 256 * (int64_t)st) * (Rtot / 2));
+      else if constexpr (KIND == OP_T8) return (uint32_t)((4 * blk + 128 * (int64_t)st) * Rtot);
+      else return (uint32_t)(blk * 8 * KB + 128 * (int64_t)st);
     };
     static_for<J0, J1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
@@ -403,8 +426,8 @@ struct DenseLoop {
     const DenseArgs &p = *c.p;
     const uint32_t slot = c.lds0 + (uint32_t)si * AB;
     constexpr bool ALL = PART < 0;
-    if constexpr (ALL || PART == 0) load_tile<TA, 0, 2>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
-    if constexpr (ALL || PART == 1) load_tile<TA, 2, 4>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
+    if constexpr (ALL || PART == 0) load_tile<OPA, 0, 2>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
+    if constexpr (ALL || PART == 1) load_tile<OPA, 2, 4>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
     if constexpr (ALL || PART == 2 || PART == 3) {
       constexpr int J0 = (PART == 3) ? 2 : 0, J1 = (PART == 2) ? 2 : 4;
       if constexpr (PSB && GROUP) {
@@ -427,7 +450,7 @@ struct DenseLoop {
           dma_asm<16, j * 1024>(base, rb, (uint32_t)(c.lane * 16), soff0 + j * 1024);
         });
       } else {
-        load_tile<TB, J0, J1>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
+        load_tile<OPB, J0, J1>(c, t.rb, c.vo_b, c.KB, p.N, st, slot + B_REG);
       }
     }
     if constexpr (FUSE && (ALL || PART == 3 || PART == 4)) {
@@ -533,7 +556,8 @@ struct DenseLoop {
   struct Lanes {
     uint32_t a[2], b[2];           // FP8 K-contiguous / preshuffled: the two 16-byte halves;
                                    // FP4: the two k steps of the stage
-    uint32_t at, bt;               // transposed: 8-byte piece 0 of tile 0
+    uint32_t at, bt;               // transposed: 8-byte piece 0 of tile 0 (packed E2M1:
+                                   // k-row 32q + i, column chunk of tile 0)
     uint32_t sa, sb;               // scale words
   };
 
@@ -558,7 +582,17 @@ struct DenseLoop {
     // or 4wn) is aligned to the tile count, so its offset is the tile-0
     // offset ^ (x << 4), and XOR on bits 4-6 commutes with adding those
     // distances (multiples of 2048).
-    {
+    if constexpr (FP4) {
+      // Packed E2M1 k-rows (128 B): tile x of the wave covers 16 columns, the
+      // 8-byte chunk c0 + x (A: c0 = 8 wm, B: c0 = 4 wn), inside 16-byte piece
+      // (c0 + x) / 2.  Lane (i, q) reads k-row 32 q + i (+ 16 for the second
+      // half of its 32 K values, + 128 for the stage's second K step), whose
+      // swizzle fswz is i / 2 in all of them; c0 / 2 has bits 0-1 clear, so
+      // piece (c0/2 + x/2) ^ (i/2) = (c0/2 ^ i/2) ^ x/2 (rdt4).
+      const int kk = 32 * q + i;
+      L.at = ((uint32_t)(kk * 128 + (((c.wm * 4) ^ fswz(kk)) << 4))) & LMASK;
+      L.bt = ((uint32_t)(B_REG + kk * 128 + (((c.wn * 2) ^ fswz(kk)) << 4))) & LMASK;
+    } else {
       const int kk = 16 * q + (i >> 1);
       const int ca = c.wm * 8, cb = c.wn * 4;
       L.at = ((uint32_t)(kk * 256 + ((ca ^ tswz(kk)) << 4) + ((i & 1) << 3))) & LMASK;
@@ -590,6 +624,17 @@ struct DenseLoop {
     v2i p2 = lds_read_tr8(base + off + 16384);
     v2i p3 = lds_read_tr8(base + off + 18432);
     return (v8i){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  }
+
+  // Transposed packed E2M1 fragment of tile x in K step s of the stage: two
+  // 16 x 16 nibble transposes (k-rows 32q + i and 32q + 16 + i), lane (i, q)
+  // receiving column i at k = 32q .. 32q + 15, then 32q + 16 .. 32q + 31: the
+  // matrix-core operand order of a 4-bit fragment.
+  __device__ static inline v8i rdt4(const uint8_t *base, uint32_t off, int x, int s) {
+    const uint32_t o = (off ^ ((uint32_t)(x >> 1) << 4)) + (uint32_t)((x & 1) << 3) + (uint32_t)s * 16384u;
+    const v2i lo = lds_read_tr4(base + o);
+    const v2i hi = lds_read_tr4(base + o + 2048);
+    return widen((v4i){lo.x, lo.y, hi.x, hi.y});
   }
 
   // Epilogue of one finished tile: its accumulators (times alpha) as BF16.
@@ -712,7 +757,8 @@ struct DenseLoop {
     // The B and scale lane offsets include their regions' bases.
     const uint8_t *la = smem + si * AB, *lb = smem + si * AB, *ls = smem + gs * SGROUP;
     auto read_a = [&](int s, int a) -> v8i {
-      if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
+      if constexpr (FP4 && TA) return rdt4(la, L.at, a, s);
+      else if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
       else if constexpr (TA) {
         return rdt(la, L.at ^ ((uint32_t)a << 4));
       } else return rd8(la, L.a[0], L.a[1], a * 2048);
@@ -721,6 +767,8 @@ struct DenseLoop {
       if constexpr (PSB) {
         if constexpr (FP4) return widen(lds_read16(lb + L.b[0] + s * 4096 + b * 1024));
         else return rd8(lb, L.b[0], L.b[1], b * 2048);
+      } else if constexpr (FP4 && TB) {
+        return rdt4(lb, L.bt, b, s);
       } else if constexpr (FP4) {
         return widen(lds_read16(lb + L.b[s] + b * 2048));
       } else if constexpr (TB) {
@@ -743,8 +791,9 @@ struct DenseLoop {
     // A stage of two K steps (FP4) reads both steps' B fragments and scales
     // up front, so that the second step's reads overlap the first step's
     // matrix work instead of stalling between the two (not in the first step
-    // of a fused epilogue, which needs those registers).
-    constexpr bool PRE = KS > 1 && !(FUSE && EPI);
+    // of a fused epilogue, nor with a transposed operand: both need those
+    // registers).
+    constexpr bool PRE = KS > 1 && !(FUSE && EPI) && !TA && !TB;
     v8i bpre[KS][FN];
     int spre[KS][FN];
     if constexpr (PRE) {

@@ -22,11 +22,7 @@ dense_fn pick_big(int layout, bool psb, bool fuse) {
     return psb ? dense_kernel<FA, FB, SMODE, false, false, true, true>
                : dense_kernel<FA, FB, SMODE, false, false, false, true>;
   }
-  if constexpr (FA == F_E2M1 || FB == F_E2M1) {
-    // packed E2M1 is K-contiguous only
-    if (layout != NT) return nullptr;
-    return psb ? dense_kernel<FA, FB, SMODE, false, false, true> : dense_kernel<FA, FB, SMODE, false, false, false>;
-  } else {
+  {
     // MX scales are blocked along K whatever the code layout, so the
     // transposed variants load them exactly as NT does
     switch (layout) {

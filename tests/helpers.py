@@ -79,9 +79,33 @@ def make_operand(lib_fmt, x, transposed):
     else:
         codes, s = synth.quant_tensor(x, elem)
     if transposed:
-        assert elem != "e2m1"
-        codes = np.ascontiguousarray(codes.T)
+        if elem == "e2m1":
+            # [rows, K/2] packed along K -> [K, rows/2] packed along rows
+            codes = synth.pack_e2m1(np.ascontiguousarray(unpack_e2m1(codes).T))
+        else:
+            codes = np.ascontiguousarray(codes.T)
     return Operand(lib_fmt, codes, s, transposed, rows, K)
+
+
+def unpack_e2m1(packed):
+    """Packed E2M1 codes (two per byte along the last axis, even index in
+    the low nibble) -> one nibble code per byte."""
+    p = np.asarray(packed, np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def k_contiguous(op):
+    """The same logical operand stored K-contiguous (codes and scales)."""
+    if not op.transposed:
+        return op
+    if op.lib_fmt == 4:
+        codes = synth.pack_e2m1(np.ascontiguousarray(unpack_e2m1(op.codes).T))
+    else:
+        codes = np.ascontiguousarray(op.codes.T)
+    return Operand(op.lib_fmt, codes, op.scales, False, op.rows, op.K)
 
 
 def run_dense(layout, opA, opB, M, N, K, preshuffle_b=False, d_fill=None):

@@ -51,7 +51,12 @@ P = 1 << 20       # a fake, 16-byte aligned address (never dereferenced)
     ((0, 0, 0, P, P, P, P, P, 256, 256, 100), -2),          # K % 128
     ((4, 4, 0, P, P, P, P, P, 256, 256, 128), -2),          # FP4 needs K % 256
     ((4, 4, 0, P, P, P, P, P, 256, 256, 256), 0),
-    ((4, 4, 1, P, P, P, P, P, 256, 256, 256), -2),          # FP4 only NT
+    ((4, 4, 1, P, P, P, P, P, 256, 256, 256), 0),           # FP4 NN
+    ((4, 4, 2, P, P, P, P, P, 256, 256, 256), 0),           # FP4 TN
+    ((4, 4, 1, P, P, P, P, P, 256, 272, 256), -2),          # FP4 NN: N % 32
+    ((4, 4, 1, P, P, P, P, P, 272, 256, 256), 0),           # FP4 NN: A is K-contiguous
+    ((4, 4, 2, P, P, P, P, P, 272, 256, 256), -2),          # FP4 TN: M % 32
+    ((4, 4 | 0x100, 1, P, P, P, P, P, 256, 256, 256), -2),  # preshuffled B: NT only
     ((0, 16, 0, P, P, P, P, P, 256, 256, 256), -2),         # MX x tensor mix
     ((4, 0, 0, P, P, P, P, P, 256, 256, 256), -2),          # FP4 x FP8
     ((7, 0, 0, P, P, P, P, P, 256, 256, 256), -1),          # bad format

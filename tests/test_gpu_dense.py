@@ -223,3 +223,45 @@ def test_integer_valued_bit_exact_mx_backward(layout, ta, tb):
     D = H.run_dense(layout, opA, opB, M, N, K)
     ref = oracle.gemm(opA.orc(), opB.orc(), M, N, K)
     assert np.array_equal(H.bits(D), oracle.bf16_rne(ref))
+
+
+# MXFP4 backward layouts: packed E2M1 stored [K, rows] with two columns per
+# byte along the contiguous dimension, E8M0 scales blocked along K.
+@pytest.mark.parametrize("layout,ta,tb", MX_T_CASES)
+@pytest.mark.parametrize("M,N,K", [(288, 416, 512), (96, 64, 768), (544, 512, 1024), (32, 32, 256)])
+def test_mxfp4_backward_layouts(layout, ta, tb, M, N, K):
+    x = synth.normal(650 + M + layout, (M, K))
+    w = synth.normal(651 + N + layout, (N, K))
+    opA = H.make_operand(F4, x, ta)
+    opB = H.make_operand(F4, w, tb)
+    _check(layout, opA, opB, M, N, K, "mxfp4 layout %d %dx%dx%d" % (layout, M, N, K))
+
+
+def test_mxfp4_layout_equivalence_bit_exact():
+    """Packed E2M1 operands stored K-contiguous or transposed (same logical
+    codes, same K-blocked scales) give identical bits in NT, NN and TN: the
+    nibble-transposing reads feed the matrix cores in the row reads' K order."""
+    M, N, K = 288, 416, 1024
+    x = synth.normal(31, (M, K))
+    w = synth.normal(32, (N, K))
+    outs = []
+    for layout, ta, tb in LAYOUT_CASES:
+        opA = H.make_operand(F4, x, ta)
+        opB = H.make_operand(F4, w, tb)
+        outs.append(H.bits(H.run_dense(layout, opA, opB, M, N, K, d_fill=float("nan"))))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("layout,ta,tb", MX_T_CASES)
+def test_integer_valued_bit_exact_mxfp4_backward(layout, ta, tb):
+    """Integer-valued E2M1 codes with E8M0 scales 2^0..2^2: D equals the
+    rounded exact result bit for bit, which pins each nibble to its row,
+    column and K index and each scale to its 32-K block."""
+    rng = np.random.default_rng(191 + layout)
+    M, N, K = 416, 288, 1280
+    opA = H.int_operand(rng, F4, M, K, ta)
+    opB = H.int_operand(rng, F4, N, K, tb)
+    D = H.run_dense(layout, opA, opB, M, N, K, d_fill=float("nan"))
+    ref = oracle.gemm(opA.orc(), opB.orc(), M, N, K)
+    assert np.array_equal(H.bits(D), oracle.bf16_rne(ref))
+

@@ -103,6 +103,25 @@ def test_mxfp4_8192_cube():
     _check_sampled(D, opA, opB, M, N, K, "mxfp4 8192^3")
 
 
+@pytest.mark.parametrize("layout,ta,tb", [(NN, False, True), (TN, True, True)])
+def test_mxfp4_backward_8192_cube(layout, ta, tb):
+    """The MXFP4 data- and weight-gradient layouts at 8192^3: sampled
+    entries against the oracle, and bit for bit equal to the NT product of
+    the same logical operands stored K-contiguous."""
+    M = N = K = 8192
+    x = synth.normal(synth.seed_for(5, 1), (M, K))
+    w = synth.normal(synth.seed_for(5, 2), (N, K))
+    opA = H.make_operand(F4, x, ta)
+    opB = H.make_operand(F4, w, tb)
+    del x, w
+    D = H.run_dense(layout, opA, opB, M, N, K, d_fill=float("nan"))
+    _check_sampled(D, opA, opB, M, N, K, "mxfp4 layout %d 8192^3" % layout)
+    bits = H.bits(D)
+    del D
+    ref = H.bits(H.run_dense(NT, H.k_contiguous(opA), H.k_contiguous(opB), M, N, K))
+    assert np.array_equal(bits, ref)
+
+
 def _bits_of(run):
     D = run()
     return H.bits(D)

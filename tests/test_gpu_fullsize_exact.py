@@ -43,8 +43,11 @@ def _pick(rng, total, tile, count, extra=()):
 
 
 def _subset(op, idx):
-    """The operand restricted to logical rows idx (codes and MX scales)."""
-    assert not (op.transposed and op.lib_fmt == F4)
+    """The operand restricted to logical rows idx (codes and MX scales);
+    a transposed packed E2M1 operand is first stored K-contiguous (an odd
+    number of its columns cannot be packed two per byte)."""
+    if op.transposed and op.lib_fmt == F4:
+        op = H.k_contiguous(op)
     codes = np.ascontiguousarray(op.codes[:, idx] if op.transposed else op.codes[idx])
     s = op.scales
     if oracle.SCALE_MX == H.LIB2ORC[op.lib_fmt][1]:
@@ -101,6 +104,11 @@ def test_mxfp8_backward_exact(layout, M, N, K):
 
 def test_mxfp4_8192_cube_exact():
     _dense_exact(NT, F4, F4, 8192, 8192, 8192, 4000, preshuffle_b=True)
+
+
+@pytest.mark.parametrize("layout", [NN, TN])
+def test_mxfp4_backward_8192_cube_exact(layout):
+    _dense_exact(layout, F4, F4, 8192, 8192, 8192, 4100 + layout, preshuffle_b=False)
 
 
 # Grouped groupwise FP8, G = 8, totM = 16384, the benchmark's m_sizes (one

@@ -120,3 +120,16 @@ def test_mxfp8_backward_layouts_multitile(layout, ta, tb, K):
     opA = H.make_operand(E5, x, ta)
     opB = H.make_operand(E4, w, tb)
     _sampled(layout, opA, opB, M, N, K, "mx layout %d K=%d" % (layout, K))
+
+
+@pytest.mark.parametrize("layout,ta,tb", [(NN, False, True), (TN, True, True)])
+def test_mxfp4_backward_layouts_multitile(layout, ta, tb):
+    """17 x 17 tiles of 256 with ragged last ones (rows and columns past
+    the end of a transposed operand's k-row read the next k-row)."""
+    M, N, K = 4384, 4128, 768
+    x = synth.normal(7061 + layout, (M, K))
+    w = synth.normal(7062 + layout, (N, K))
+    opA = H.make_operand(F4, x, ta)
+    opB = H.make_operand(F4, w, tb)
+    _sampled(layout, opA, opB, M, N, K, "mxfp4 layout %d" % layout)
+
