@@ -503,9 +503,23 @@ def mxfp4_bench(torch, synth, mxgemm, dev):
                                               mxgemm.NT, A, SA, B, SB, D, M, N, K))
     tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
     log("mxfp4 8192^3: %.1f us, %.0f TFLOP/s (%.1f%% of FP4 peak)" % (us, tf, 100.0 * tf / PEAK_MXFP4_TFLOPS))
-    del A, B, D
+    del B
+    # the backward layouts on the same logical operands: B stored [K, N]
+    # (NN), and A stored [K, M] too (TN), packed along the rows
+    layouts = []
+    BT = t(synth.transpose_e2m1(qb))
+    AT = t(synth.transpose_e2m1(qa))
+    for layout, a_op in ((mxgemm.NN, A), (mxgemm.TN, AT)):
+        ul = time_calls(torch, lambda: mxgemm.run(mxgemm.MXFP4_E2M1, mxgemm.MXFP4_E2M1, layout, a_op, SA, BT, SBp,
+                                                  D, M, N, K))
+        tl = 2.0 * M * N * K / (ul * 1e-6) / 1e12
+        name = ["NT", "NN", "TN"][layout]
+        layouts.append({"layout": name, "us": ul, "tflops": tl, "pct_peak": 100.0 * tl / PEAK_MXFP4_TFLOPS})
+        log("mxfp4 %s 8192^3: %.1f us, %.0f TFLOP/s (%.1f%% of FP4 peak)" % (name, ul, tl, 100.0 * tl / PEAK_MXFP4_TFLOPS))
+    del A, AT, BT, D
     torch.cuda.empty_cache()
-    return {"M": M, "N": N, "K": K, "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP4_TFLOPS}
+    return {"M": M, "N": N, "K": K, "us": us, "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MXFP4_TFLOPS,
+            "backward_layouts": layouts}
 
 
 def fused_bench(torch, synth, mxgemm, dev):
@@ -583,7 +597,14 @@ def profile_leg(torch, synth, mxgemm, dev, leg, launches=3):
         for _ in range(launches):
             mxgemm.run(mxgemm.MXFP4_E2M1, mxgemm.MXFP4_E2M1 | mxgemm.PRESHUFFLED, mxgemm.NT, A, SA, B, SB, D, M, N, K)
         torch.cuda.synchronize()
-        order.append({"M": M, "N": N, "K": K, "fmt": "e2m1"})
+        order.append({"M": M, "N": N, "K": K, "fmt": "e2m1", "layout": "NT"})
+        del B
+        AT, BT, SBp = t(synth.transpose_e2m1(qa)), t(synth.transpose_e2m1(qb)), t(sb)
+        for layout, a_op in ((mxgemm.NN, A), (mxgemm.TN, AT)):
+            for _ in range(launches):
+                mxgemm.run(mxgemm.MXFP4_E2M1, mxgemm.MXFP4_E2M1, layout, a_op, SA, BT, SBp, D, M, N, K)
+            torch.cuda.synchronize()
+            order.append({"M": M, "N": N, "K": K, "fmt": "e2m1", "layout": ["NT", "NN", "TN"][layout]})
     elif leg == "mx_backward":
         for idx, (name, layout, M, N, K) in enumerate(C3_CASES):
             if layout == mxgemm.NT:

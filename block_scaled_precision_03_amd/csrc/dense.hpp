@@ -82,11 +82,12 @@ __device__ constexpr int tswz(int kk) { return (kk & 7) | ((kk & 16) >> 1); }
 
 // Transposed packed E2M1 tiles (k-rows of 128 B: 256 columns, two per
 // byte): 16-byte piece p of k-row kk sits at p ^ fswz(kk).  A fragment read
-// (ds_read_b64_tr_b4) has the 32 lanes of a phase read 8 bytes at one
-// column chunk from k-rows k0 + i and k0 + 32 + i (i < 16); rows 128 B apart
-// split them over the two bank halves by parity, and fswz gives the 8 rows
-// of one parity in each 16-row run 8 distinct pieces, so at most two lanes
-// share a bank (the read half of a piece is the same for every lane).
+// (ds_read_b64_tr_b4) has the 32 lanes of a phase read 8 bytes from k-rows
+// k0 + i (lanes 0-15) and k0 + 32 + i (lanes 16-31), i < 16.  Rows 128 B
+// apart fall in the two bank halves by parity, and fswz gives the 8 rows of
+// one parity in each run of 16 eight distinct pieces; the two lane groups
+// read the two 8-byte halves of a piece (the column chunks of two adjacent
+// tiles, see rdt4_pair), so the phase's 32 reads hit 32 distinct bank pairs.
 __device__ constexpr int fswz(int kk) { return (kk >> 1) & 7; }
 
 // K-contiguous operand rows [r0, r0+R) x bytes [128*st, 128*st+128).
@@ -263,7 +264,7 @@ struct DenseLoop {
   static constexpr int OP_K = 0, OP_T8 = 1, OP_T4 = 2;
   static constexpr int OPA = TA ? (FP4 ? OP_T4 : OP_T8) : OP_K;
   static constexpr int OPB = TB ? (FP4 ? OP_T4 : OP_T8) : OP_K;
-  static constexpr bool PIN = !TA && !TB && (PSB || !MX || FP4);
+  static constexpr bool PIN = FP4 || (!TA && !TB && (PSB || !MX));
 
   // Loop-invariant state.  Every global load of the loop is one buffer
   // instruction: a resource fixed for the tile, a per-lane offset fixed for
@@ -584,14 +585,16 @@ struct DenseLoop {
     // distances (multiples of 2048).
     if constexpr (FP4) {
       // Packed E2M1 k-rows (128 B): tile x of the wave covers 16 columns, the
-      // 8-byte chunk c0 + x (A: c0 = 8 wm, B: c0 = 4 wn), inside 16-byte piece
-      // (c0 + x) / 2.  Lane (i, q) reads k-row 32 q + i (+ 16 for the second
-      // half of its 32 K values, + 128 for the stage's second K step), whose
-      // swizzle fswz is i / 2 in all of them; c0 / 2 has bits 0-1 clear, so
-      // piece (c0/2 + x/2) ^ (i/2) = (c0/2 ^ i/2) ^ x/2 (rdt4).
+      // 8-byte chunk c0 + x (A: c0 = 8 wm, B: c0 = 4 wn), half x % 2 of
+      // 16-byte piece (c0 + x) / 2.  Lane (i, q) reads k-row 32 q + i (+ 16
+      // for the second half of its 32 K values, + 128 for the stage's second
+      // K step), whose swizzle fswz is i / 2 in all of them; c0 / 2 has bits
+      // 0-1 clear, so piece (c0/2 + x/2) ^ (i/2) = (c0/2 ^ i/2) ^ x/2.  Lanes
+      // of odd q start at the other half (bit 3), see rdt4_pair.
       const int kk = 32 * q + i;
-      L.at = ((uint32_t)(kk * 128 + (((c.wm * 4) ^ fswz(kk)) << 4))) & LMASK;
-      L.bt = ((uint32_t)(B_REG + kk * 128 + (((c.wn * 2) ^ fswz(kk)) << 4))) & LMASK;
+      const int half = (q & 1) << 3;
+      L.at = ((uint32_t)(kk * 128 + (((c.wm * 4) ^ fswz(kk)) << 4) + half)) & LMASK;
+      L.bt = ((uint32_t)(B_REG + kk * 128 + (((c.wn * 2) ^ fswz(kk)) << 4) + half)) & LMASK;
     } else {
       const int kk = 16 * q + (i >> 1);
       const int ca = c.wm * 8, cb = c.wn * 4;
@@ -626,15 +629,24 @@ struct DenseLoop {
     return (v8i){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   }
 
-  // Transposed packed E2M1 fragment of tile x in K step s of the stage: two
-  // 16 x 16 nibble transposes (k-rows 32q + i and 32q + 16 + i), lane (i, q)
-  // receiving column i at k = 32q .. 32q + 15, then 32q + 16 .. 32q + 31: the
-  // matrix-core operand order of a 4-bit fragment.
-  __device__ static inline v8i rdt4(const uint8_t *base, uint32_t off, int x, int s) {
-    const uint32_t o = (off ^ ((uint32_t)(x >> 1) << 4)) + (uint32_t)((x & 1) << 3) + (uint32_t)s * 16384u;
-    const v2i lo = lds_read_tr4(base + o);
-    const v2i hi = lds_read_tr4(base + o + 2048);
-    return widen((v4i){lo.x, lo.y, hi.x, hi.y});
+  // Transposed packed E2M1 fragments of tiles x and x + 1 (x even) in K
+  // step s of the stage.  Each fragment is two 16 x 16 nibble transposes
+  // (k-rows 32q + i, then 32q + 16 + i): lane (i, q) receives column i at
+  // k = 32q .. 32q + 15, then 32q + 16 .. 32q + 31, the matrix-core operand
+  // order of a 4-bit fragment.  The two tiles' chunks are the two halves of
+  // one 16-byte piece; lanes of even q read tile x's half in the first pair
+  // of reads and tile x + 1's in the second, lanes of odd q the reverse (so
+  // that every read's phase covers both halves, free of bank conflicts), and
+  // a per-lane select puts each tile's data in its fragment.
+  __device__ static inline void rdt4_pair(const uint8_t *base, uint32_t off, int x, int s, v8i &f0, v8i &f1) {
+    const uint32_t o0 = (off ^ ((uint32_t)(x >> 1) << 4)) + (uint32_t)s * 16384u;
+    const uint32_t o1 = (off ^ (((uint32_t)(x >> 1) << 4) | 8u)) + (uint32_t)s * 16384u;
+    const v2i a0 = lds_read_tr4(base + o0), a1 = lds_read_tr4(base + o0 + 2048);
+    const v2i b0 = lds_read_tr4(base + o1), b1 = lds_read_tr4(base + o1 + 2048);
+    const v4i u = (v4i){a0.x, a0.y, a1.x, a1.y}, v = (v4i){b0.x, b0.y, b1.x, b1.y};
+    const bool odd = ((__lane_id() >> 4) & 1) != 0;
+    f0 = widen(odd ? v : u);
+    f1 = widen(odd ? u : v);
   }
 
   // Epilogue of one finished tile: its accumulators (times alpha) as BF16.
@@ -757,8 +769,7 @@ struct DenseLoop {
     // The B and scale lane offsets include their regions' bases.
     const uint8_t *la = smem + si * AB, *lb = smem + si * AB, *ls = smem + gs * SGROUP;
     auto read_a = [&](int s, int a) -> v8i {
-      if constexpr (FP4 && TA) return rdt4(la, L.at, a, s);
-      else if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
+      if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
       else if constexpr (TA) {
         return rdt(la, L.at ^ ((uint32_t)a << 4));
       } else return rd8(la, L.a[0], L.a[1], a * 2048);
@@ -767,8 +778,6 @@ struct DenseLoop {
       if constexpr (PSB) {
         if constexpr (FP4) return widen(lds_read16(lb + L.b[0] + s * 4096 + b * 1024));
         else return rd8(lb, L.b[0], L.b[1], b * 2048);
-      } else if constexpr (FP4 && TB) {
-        return rdt4(lb, L.bt, b, s);
       } else if constexpr (FP4) {
         return widen(lds_read16(lb + L.b[s] + b * 2048));
       } else if constexpr (TB) {
@@ -809,14 +818,21 @@ struct DenseLoop {
     for (int s = 0; s < KS; ++s) {
       v8i bf[FN];
       int sb[FN];
+      if constexpr (FP4 && TB) {
 #pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        if constexpr (PRE) {
-          bf[b] = bpre[s][b];
-          sb[b] = spre[s][b];
-        } else {
-          bf[b] = read_b(s, b);
-          sb[b] = b_scale(s, b);
+        for (int b = 0; b < FN; b += 2) rdt4_pair(lb, L.bt, b, s, bf[b], bf[b + 1]);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) sb[b] = b_scale(s, b);
+      } else {
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          if constexpr (PRE) {
+            bf[b] = bpre[s][b];
+            sb[b] = spre[s][b];
+          } else {
+            bf[b] = read_b(s, b);
+            sb[b] = b_scale(s, b);
+          }
         }
       }
       // A scale words: with K-contiguous operands all of the step's up front
@@ -876,13 +892,23 @@ struct DenseLoop {
         }
         continue;
       }
-      v8i af = read_a(s, 0);
+      // Transposed packed E2M1 A: tiles come in pairs (rdt4_pair); the pair
+      // after tile a is read at odd a, with tile a + 1 the first of it.
+      constexpr bool A_PAIRS = FP4 && TA;
+      v8i af, apair1;
+      if constexpr (A_PAIRS) rdt4_pair(la, L.at, 0, s, af, apair1);
+      else af = read_a(s, 0);
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         v8i af_next;
         uint32_t sw_next = 0;
         if (a + 1 < FM) {
-          af_next = read_a(s, a + 1);
+          if constexpr (A_PAIRS) {
+            if (a & 1) rdt4_pair(la, L.at, a + 1, s, af_next, apair1);
+            else af_next = apair1;
+          } else {
+            af_next = read_a(s, a + 1);
+          }
           if constexpr (SA_AHEAD) sw_next = scale_word(a + 1);
         }
         int sa = E8M0_ONE_X4;
@@ -977,8 +1003,11 @@ struct DenseLoop {
           issue_any(nxt, 0, (g0 + ngrp) & 1);
         }
         compute<EPI>(c, L, k, smem, SC, (g0 + k * KS / 4) & 1, acc, e);
-        // Only where registers allow: for the transposed variants and MX FP8
-        // with plain B it costs spills in the K loop.
+        // Only where registers allow: for the transposed FP8 variants and MX
+        // FP8 with plain B it costs spills in the K loop.  The transposed E2M1
+        // variants need it: unpinned, the compiler holds a whole stage of
+        // fragments in registers to run the step's matrix work after the
+        // barrier, and spills in the K loop.
         if constexpr (PIN) pin(acc);
         __builtin_amdgcn_sched_barrier(0);
         // This wave's part of the next stage has landed (and, with no

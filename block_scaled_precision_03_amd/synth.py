@@ -64,6 +64,16 @@ def pack_e2m1(nibbles: np.ndarray) -> np.ndarray:
     return (n[..., 0::2] & 15) | ((n[..., 1::2] & 15) << 4)
 
 
+def transpose_e2m1(packed: np.ndarray) -> np.ndarray:
+    """Packed E2M1 codes [rows, K/2] (two per byte along K) -> the same codes
+    stored [K, rows/2], two per byte along rows (even index -> low nibble)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n = np.empty((p.shape[0], 2 * p.shape[1]), np.uint8)
+    n[:, 0::2] = p & 15
+    n[:, 1::2] = p >> 4
+    return pack_e2m1(np.ascontiguousarray(n.T))
+
+
 def _e8m0_exponent(amax: np.ndarray, fmt_max: float) -> np.ndarray:
     """X = floor(log2(amax / fmt_max)) exactly, clamped to [-127, 127]."""
     a = amax.astype(np.float64)

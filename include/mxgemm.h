@@ -106,7 +106,11 @@ const char *mxgemm_status_string(int status);
  *             carry MXG_PRESHUFFLED (NT only).
  * layout      MXG_NT, MXG_NN or MXG_TN (see the header comment).
  * A, B        codes: uint8, row-major in the layout's storage shape.  E2M1 is
- *             packed two per byte along K (NT only).
+ *             packed two per byte along the contiguous dimension (element
+ *             2j in bits 3:0): along K for a K-contiguous operand, along M
+ *             (A 'T') or N (B 'N') for a transposed one ("[gfx1250] Add
+ *             MXFP4 GEMM support to FlyDSL backend", review of the MXFP4
+ *             storage chosen per layout: rowwise or columnwise buffers).
  * sA, sB      MX: uint8 E8M0 [rows, K/32] row-major (rows = M for A, N for B),
  *             always blocked along K whatever the code layout; a preshuffled
  *             sB has the size given by mxgemm_preshuffle_scales_bytes(N, K).
@@ -115,7 +119,7 @@ const char *mxgemm_status_string(int status);
  * D           BF16 [M,N] row-major, written in full.
  * Divisibility: MX needs K % 128 == 0 (E2M1: K % 256 == 0); NN/TN need the
  *             contiguous dimension of each transposed operand (M for A 'T',
- *             N for B 'N') to be a multiple of 16, and each transposed
+ *             N for B 'N') to be a multiple of 16 (E2M1: 32), and each transposed
  *             operand to hold fewer than 2^31 - 16 bytes, and a
  *             preshuffled B to hold fewer than 2^32 - 2^16 bytes.  Otherwise
  *             MXG_ERR_UNSUPPORTED.  A, B, sA, sB and D must be 16-byte

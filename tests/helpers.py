@@ -80,8 +80,7 @@ def make_operand(lib_fmt, x, transposed):
         codes, s = synth.quant_tensor(x, elem)
     if transposed:
         if elem == "e2m1":
-            # [rows, K/2] packed along K -> [K, rows/2] packed along rows
-            codes = synth.pack_e2m1(np.ascontiguousarray(unpack_e2m1(codes).T))
+            codes = synth.transpose_e2m1(codes)
         else:
             codes = np.ascontiguousarray(codes.T)
     return Operand(lib_fmt, codes, s, transposed, rows, K)
