@@ -26,7 +26,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.build(force=False)
+        # ORACLE_LIB: another build of the same source (the sanitizer build
+        # of the CPU test suite)
+        path = os.environ.get("ORACLE_LIB") or _build.build(force=False)
         L = ctypes.CDLL(path)
         d, i64, p, i = ctypes.c_double, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         for name in ("oracle_decode_e4m3", "oracle_decode_e5m2", "oracle_decode_e2m1",

@@ -23,6 +23,16 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+def build_sanitized(out: str) -> str:
+    """The same source with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts), for the CPU test suite's sanitizer run."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-Wall", "-o", out, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(force=True))
     sys.exit(0)

@@ -46,7 +46,7 @@ def test_status_strings():
 P = 1 << 20       # a fake, 16-byte aligned address (never dereferenced)
 
 
-@pytest.mark.parametrize("args,expect", [
+VALIDATE_CASES = [
     ((0, 0, 0, P, P, P, P, P, 256, 256, 256), 0),
     ((0, 0, 0, P, P, P, P, P, 256, 256, 100), -2),          # K % 128
     ((4, 4, 0, P, P, P, P, P, 256, 256, 128), -2),          # FP4 needs K % 256
@@ -79,13 +79,16 @@ P = 1 << 20       # a fake, 16-byte aligned address (never dereferenced)
     ((4, 0x104, 0, P, P, P, P, P, 256, 262144, 16384), 0),   # FP4: half the bytes
     ((4, 0x104, 0, P, P, P, P, P, 256, 262144, 32768), -2),
     ((0, 0, 0, P, P, P, P, P, 256, 262144, 16384), 0),        # plain B is rebased per tile
-])
+]
+
+
+@pytest.mark.parametrize("args,expect", VALIDATE_CASES)
 def test_validate(args, expect):
     m = _mx()
     assert m.validate(*args) == expect
 
 
-@pytest.mark.parametrize("args,expect", [
+GROUPED_CASES = [
     ((8, P, P, P, P, P, P, 1024, 2048, 7168, 0), 0),
     ((0, P, P, P, P, P, P, 1024, 2048, 7168, 0), -2),        # G < 1
     ((2000, P, P, P, P, P, P, 1024, 2048, 7168, 0), -2),     # G > max
@@ -94,7 +97,10 @@ def test_validate(args, expect):
     ((8, 0, P, P, P, P, P, 1024, 2048, 7168, 0), -1),        # null m_sizes
     ((8, P, P, P, P, P, P + 2, 1024, 2048, 7168, 0), -3),    # misaligned D
     ((8, P, P, P, P, P, P, 0, 2048, 7168, 1), 0),            # totM = 0
-])
+]
+
+
+@pytest.mark.parametrize("args,expect", GROUPED_CASES)
 def test_grouped_validate(args, expect):
     m = _mx()
     assert m.grouped_validate(*args) == expect
@@ -110,32 +116,38 @@ def test_preshuffle_sizes():
     assert m.preshuffle_scales_bytes(11008, 11008) == 172 * 22 * 1024
 
 
+# Calls that must fail (or be no-ops) in the host checks, before any device
+# work: (exported function, arguments without the trailing stream, status).
+REJECT_CALLS = [
+    ("mxgemm_run", (0, 0, 0, P, P, P, P, P, 256, 256, 100), -2),
+    ("grouped_fp8_gemm_run", (0, P, P, P, P, P, P, 128, 128, 128, 0), -2),
+    ("mxgemm_preshuffle_b", (0, 0, P, P, 256, 100), -2),
+    ("mxgemm_preshuffle_scales", (P, P, 256, 100), -2),
+    ("grouped_fp8_preshuffle_b", (8, P, P, 2000, 128), -2),
+    ("mxgemm_quantize_mx", (16, P, P, P, 4, 32), -1),        # tensor-wise fmt
+    ("mxgemm_quantize_mx", (0, P, P, P, 4, 48), -2),         # K % 32
+    ("mxgemm_quantize_mx", (0, P + 4, P, P, 4, 32), -3),     # misaligned x
+    ("mxgemm_quantize_mx", (0, P, P, P, 0, 32), 0),          # rows = 0: no-op
+    ("mxgemm_quantize_tensor", (0, P, P, P, 64), -1),       # MX fmt
+    ("mxgemm_quantize_tensor", (16, P, P, P, -8), -1),      # n < 0
+    ("mxgemm_quantize_tensor", (16, P, P, 0, 64), -1),      # null scale
+    ("mxgemm_quantize_tensor", (17, P, P, P, 60), -2),      # n % 8
+    ("mxgemm_quantize_tensor", (16, P + 4, P, P, 64), -3),  # misaligned x
+    ("mxgemm_quantize_tensor", (16, P, P, P + 2, 64), -3),  # misaligned scale
+    ("grouped_fp8_quantize_act", (0, P, P, P, P, 128, 128), -2),    # G < 1
+    ("grouped_fp8_quantize_act", (8, P, P, P, P, 128, 200), -2),    # K % 128
+    ("grouped_fp8_quantize_act", (8, 0, P, P, P, 128, 128), -1),    # null m_sizes
+    ("grouped_fp8_quantize_act", (8, P, P, P, P + 2, 128, 128), -3),  # misaligned scales
+    ("grouped_fp8_quantize_weight", (8, P, P, P, 200, 128), -2),     # N % 128
+    ("grouped_fp8_quantize_weight", (0, P, P, P, 128, 128), -2),     # G < 1
+    ("grouped_fp8_quantize_weight", (8, P + 4, P, P, 128, 128), -3),  # misaligned w
+    ("grouped_fp8_quantize_weight", (8, P, P, P, 0, 128), 0),        # N = 0: no-op
+]
+
 def test_ops_reject_bad_args_before_device_use():
-    m = _mx()
-    lib = m.lib()
-    assert lib.mxgemm_run(0, 0, 0, P, P, P, P, P, 256, 256, 100, None) == -2
-    assert lib.grouped_fp8_gemm_run(0, P, P, P, P, P, P, 128, 128, 128, 0, None) == -2
-    assert lib.mxgemm_preshuffle_b(0, 0, P, P, 256, 100, None) == -2
-    assert lib.mxgemm_preshuffle_scales(P, P, 256, 100, None) == -2
-    assert lib.grouped_fp8_preshuffle_b(8, P, P, 2000, 128, None) == -2
-    assert lib.mxgemm_quantize_mx(16, P, P, P, 4, 32, None) == -1        # tensor-wise fmt
-    assert lib.mxgemm_quantize_mx(0, P, P, P, 4, 48, None) == -2         # K % 32
-    assert lib.mxgemm_quantize_mx(0, P + 4, P, P, 4, 32, None) == -3     # misaligned x
-    assert lib.mxgemm_quantize_mx(0, P, P, P, 0, 32, None) == 0          # rows = 0: no-op
-    assert lib.mxgemm_quantize_tensor(0, P, P, P, 64, None) == -1       # MX fmt
-    assert lib.mxgemm_quantize_tensor(16, P, P, P, -8, None) == -1      # n < 0
-    assert lib.mxgemm_quantize_tensor(16, P, P, 0, 64, None) == -1      # null scale
-    assert lib.mxgemm_quantize_tensor(17, P, P, P, 60, None) == -2      # n % 8
-    assert lib.mxgemm_quantize_tensor(16, P + 4, P, P, 64, None) == -3  # misaligned x
-    assert lib.mxgemm_quantize_tensor(16, P, P, P + 2, 64, None) == -3  # misaligned scale
-    assert lib.grouped_fp8_quantize_act(0, P, P, P, P, 128, 128, None) == -2    # G < 1
-    assert lib.grouped_fp8_quantize_act(8, P, P, P, P, 128, 200, None) == -2    # K % 128
-    assert lib.grouped_fp8_quantize_act(8, 0, P, P, P, 128, 128, None) == -1    # null m_sizes
-    assert lib.grouped_fp8_quantize_act(8, P, P, P, P + 2, 128, 128, None) == -3  # misaligned scales
-    assert lib.grouped_fp8_quantize_weight(8, P, P, P, 200, 128, None) == -2     # N % 128
-    assert lib.grouped_fp8_quantize_weight(0, P, P, P, 128, 128, None) == -2     # G < 1
-    assert lib.grouped_fp8_quantize_weight(8, P + 4, P, P, 128, 128, None) == -3  # misaligned w
-    assert lib.grouped_fp8_quantize_weight(8, P, P, P, 0, 128, None) == 0        # N = 0: no-op
+    lib = _mx().lib()
+    for fn, args, expect in REJECT_CALLS:
+        assert getattr(lib, fn)(*args, None) == expect, (fn, args)
 
 
 def test_package_has_no_cpu_fallback():
@@ -148,7 +160,7 @@ def test_package_has_no_cpu_fallback():
             assert "import oracle" not in open(os.path.join(ROOT, "block_scaled_precision_03_amd", f)).read()
 
 
-@pytest.mark.parametrize("args,expect", [
+FUSED_CASES = [
     ((0, 0, 0, P, P, P, P, P, 256, 256, 256, P, 2), 0),           # MX NT, bias + GELU
     ((16, 17, 0, P, P, P, P, P, 256, 256, 256, None, 3), 0),      # tensor-wise NT, SiLU alone
     ((4, 0x104, 0, P, P, P, P, P, 256, 256, 256, P, 1), 0),       # FP4 preshuffled, bias + ReLU
@@ -160,7 +172,10 @@ def test_package_has_no_cpu_fallback():
     ((0, 0, 0, P, P, P, P, P, 256, 255, 256, P, 0), -2),          # bias needs N even
     ((0, 0, 0, P, P, P, P, P, 256, 256, 256, P + 2, 0), -3),      # misaligned bias
     ((0, 0, 0, P, P, P, P, P, 256, 256, 100, P, 0), -2),          # mxgemm_run's own checks first
-])
+]
+
+
+@pytest.mark.parametrize("args,expect", FUSED_CASES)
 def test_validate_fused(args, expect):
     m = _mx()
     assert m.validate_fused(*args[:11], bias=args[11], activation=args[12]) == expect
