@@ -880,6 +880,11 @@ struct DenseLoop {
               part[a & 1][b] = mfma_scaled<FB, FA>(bf[b], af, zero, E8M0_ONE_X4, E8M0_ONE_X4);
             if (a + 1 < FM) af = af_next;
           }
+          // the scaling of tile a - 1 after tile a's matrix-core
+          // instructions: left free, the scheduler puts these independent
+          // FMAs first, and they then wait on tile a - 1's results, issued
+          // just before
+          __builtin_amdgcn_sched_barrier(0);
           if (a > 0) {
             const int r = a - 1;
 #pragma unroll
