@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--plain-b", action="store_true", help="time with plain (not preshuffled) B")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the tensor-wise FP8 and MXFP4 measurements")
-    ap.add_argument("--profile-leg", choices=("grouped", "mxfp4", "mx_backward"),
+    ap.add_argument("--profile-leg", choices=("grouped", "mxfp4", "mx_backward", "tensorwise"),
                     help="only launch one leg's kernels, three times per shape (no graphs, no "
                          "cold rotation): the short program a profiler's counter passes run")
     ap.add_argument("--copy-probe", action="store_true",
@@ -460,6 +460,47 @@ def quant_bench(torch, synth, mxgemm, dev):
     return out
 
 
+def preshuffle_bench(torch, synth, mxgemm, dev):
+    """The one-time weight shuffles, outside every timed GEMM: MXFP8 B codes
+    and E8M0 scales of the 14336 x 4096 weight of the LLM shapes, MXFP4 B of
+    8192^3, and the grouped [8, 2048, 7168] E4M3 weights.  Byte permutations:
+    algorithmic bytes = bytes read + bytes written."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = []
+
+    def one(name, call, nbytes):
+        us = time_calls(torch, call)
+        out.append({"name": name, "us": us, "bytes": nbytes, "gbs": nbytes / us / 1e3,
+                    "pct_hbm": 100.0 * nbytes / us / 1e3 / PEAK_HBM_GBS})
+        log("%s: %.1f us, %.0f GB/s" % (name, us, nbytes / us / 1e3))
+
+    N, K = 14336, 4096
+    q, s = synth.quant_mx(synth.normal(synth.seed_for(2, 2, 1), (N, K), 0.02), "e4m3")
+    qd, sd = t(q), t(s)
+    qp = torch.empty(mxgemm.preshuffle_b_bytes(mxgemm.MXFP8_E4M3, N, K), dtype=torch.uint8, device=dev)
+    sp = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=dev)
+    one("preshuffle_b e4m3 [14336, 4096]", lambda: mxgemm.preshuffle_b(mxgemm.MXFP8_E4M3, mxgemm.NT, qd, qp, N, K),
+        N * K + qp.numel())
+    one("preshuffle_scales [14336, 4096/32]", lambda: mxgemm.preshuffle_scales(sd, sp, N, K), N * K // 32 + sp.numel())
+    del qd, sd, qp, sp
+    N = K = 8192
+    q, s = synth.quant_mx(synth.normal(synth.seed_for(5, 2), (N, K)), "e2m1")
+    qd = t(q)
+    qp = torch.empty(mxgemm.preshuffle_b_bytes(mxgemm.MXFP4_E2M1, N, K), dtype=torch.uint8, device=dev)
+    one("preshuffle_b e2m1 [8192, 8192]", lambda: mxgemm.preshuffle_b(mxgemm.MXFP4_E2M1, mxgemm.NT, qd, qp, N, K),
+        N * K // 2 + qp.numel())
+    del qd, qp
+    G, N, K = 8, 2048, 7168
+    wq, _ = synth.quant_group_weight(synth.normal(synth.seed_for(4, 2, 0), (G, N, K), 0.02))
+    wd = t(wq)
+    wp = torch.empty_like(wd)
+    one("grouped_preshuffle_b e4m3 [8, 2048, 7168]", lambda: mxgemm.grouped_preshuffle_b(G, wd, wp, N, K),
+        2 * G * N * K)
+    del wd, wp
+    torch.cuda.empty_cache()
+    return out
+
+
 def mfma_ceiling(torch, mxgemm, dev):
     """What the scaled matrix-core instruction sustains with nothing else
     running (FP8 and FP4 operands), and the shader clock meanwhile."""
@@ -619,6 +660,24 @@ def profile_leg(torch, synth, mxgemm, dev, leg, launches=3):
             torch.cuda.synchronize()
             for _ in range(launches):
                 mxgemm.run(mxgemm.MXFP8_E5M2, mxgemm.MXFP8_E4M3, layout, A, SA, B, SB, D, M, N, K)
+            torch.cuda.synchronize()
+            order.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "M": M, "N": N, "K": K})
+    elif leg == "tensorwise":
+        for idx, (name, layout, M, N, K) in enumerate(C3_CASES):
+            x = synth.normal(synth.seed_for(3, 1, idx), (M, K))
+            w = synth.normal(synth.seed_for(3, 2, idx), (N, K), 0.02 if name != "wgrad" else 1.0)
+            qa, sa = synth.quant_tensor(x, "e5m2")
+            qb, sb = synth.quant_tensor(w, "e4m3")
+            if layout == mxgemm.TN:
+                qa = qa.T
+            if layout != mxgemm.NT:
+                qb = qb.T
+            A, B = t(qa), t(qb)
+            SA, SB = t(np.array([sa], np.float32)), t(np.array([sb], np.float32))
+            D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(launches):
+                mxgemm.run(mxgemm.FP8_E5M2_TENSOR, mxgemm.FP8_E4M3_TENSOR, layout, A, SA, B, SB, D, M, N, K)
             torch.cuda.synchronize()
             order.append({"name": name, "layout": ["NT", "NN", "TN"][layout], "M": M, "N": N, "K": K})
     print(json.dumps({"profile_leg": leg, "launches_per_shape": launches, "order": order}), flush=True)
@@ -822,6 +881,8 @@ def main():
         result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
         log("fused epilogue ...")
         result["fused_epilogue"] = fused_bench(torch, synth, mxgemm, dev)
+        log("weight preshuffles ...")
+        result["preshuffle"] = preshuffle_bench(torch, synth, mxgemm, dev)
         result["mfma_ceiling"] = mfma_ceiling(torch, mxgemm, dev)
         result["roofline"]["frac_of_mfma_ceiling"] = (
             result["roofline"]["achieved"] / result["mfma_ceiling"]["fp8"]["tflops"])

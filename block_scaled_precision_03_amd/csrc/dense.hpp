@@ -771,7 +771,13 @@ struct DenseLoop {
     auto read_a = [&](int s, int a) -> v8i {
       if constexpr (FP4) return widen(lds_read16(la + L.a[s] + a * 2048));
       else if constexpr (TA) {
-        return rdt(la, L.at ^ ((uint32_t)a << 4));
+        // MX: the tile's base offset formed here from an opaque copy, not
+        // kept in a register per tile through the loop (with the scale words
+        // beside them, eight of those pushed accumulators into scratch inside
+        // the K loop, each reload waiting on the stage's DMAs)
+        uint32_t o = L.at;
+        if constexpr (MX) asm volatile("" : "+v"(o));
+        return rdt(la, o ^ ((uint32_t)a << 4));
       } else return rd8(la, L.a[0], L.a[1], a * 2048);
     };
     auto read_b = [&](int s, int b) -> v8i {
@@ -781,7 +787,9 @@ struct DenseLoop {
       } else if constexpr (FP4) {
         return widen(lds_read16(lb + L.b[s] + b * 2048));
       } else if constexpr (TB) {
-        return rdt(lb, L.bt ^ ((uint32_t)b << 4));
+        uint32_t o = L.bt;
+        if constexpr (MX) asm volatile("" : "+v"(o));
+        return rdt(lb, o ^ ((uint32_t)b << 4));
       } else return rd8(lb, L.b[0], L.b[1], b * 2048);
     };
     auto b_scale = [&](int s, int b) -> int {
