@@ -1,0 +1,171 @@
+"""GPU: entry points captured into a HIP graph.
+
+The C ABI promises that a call reads no device state on the host and
+enqueues only kernels, so that it can be captured after mxgemm_init().
+Each case here runs the call eagerly, captures the same call into a graph
+(torch.cuda.CUDAGraph), and replays the graph three times; before every
+replay the outputs are overwritten eagerly (NaN or a byte pattern) and the
+device is synchronized, and after it every output must equal the eager
+result bit for bit.  Covered: the persistent and the 64 x 64 dense kernels,
+MX NN/TN, MXFP4 NT/NN, tensor-wise, the fused epilogue, the three grouped
+kernels, the quantizers (the tensor-wise one is four launches) and the
+preshuffles.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_03_amd import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+E4, E5, F4 = 0, 1, 4
+T4, T5 = 16, 17
+NT, NN, TN = 0, 1, 2
+
+
+def _mx():
+    from block_scaled_precision_03_amd import mxgemm
+    mxgemm.init()
+    return mxgemm
+
+
+def _reset(outs):
+    for o in outs:
+        if o.dtype in (torch.bfloat16, torch.float32):
+            o.fill_(float("nan"))
+        else:
+            o.fill_(0x5A)
+
+
+def _bits(t):
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    elif t.dtype == torch.float32:
+        t = t.view(torch.int32)
+    return t.cpu().numpy().copy()
+
+
+def _check_graph(call, outs, replays=3):
+    _reset(outs)
+    call()
+    torch.cuda.synchronize()
+    ref = [_bits(o) for o in outs]
+    # one warm-up call on a side stream, as torch asks before capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(replays):
+        _reset(outs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert np.array_equal(_bits(o), r), "replay %d, output %d differs from the eager call" % (rep, i)
+    del g
+
+
+def _dense_case(fa, fb, layout, M, N, K, pre=False, seed=1):
+    mxgemm = _mx()
+    ta, tb = layout == TN, layout in (NN, TN)
+    opA = H.make_operand(fa, synth.normal(seed, (M, K)), ta)
+    opB = H.make_operand(fb, synth.normal(seed + 1, (N, K), 0.05), tb)
+    A, sA, B, sB = opA.dev_codes(), opA.dev_scales(), opB.dev_codes(), opB.dev_scales()
+    fmtB = fb
+    if pre:
+        Bp = torch.empty(mxgemm.preshuffle_b_bytes(fb, N, K), dtype=torch.uint8, device=H.DEV)
+        mxgemm.preshuffle_b(fb, NT, B, Bp, N, K)
+        B = Bp
+        if H.LIB2ORC[fb][1] == 0:
+            sBp = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=H.DEV)
+            mxgemm.preshuffle_scales(sB, sBp, N, K)
+            sB = sBp
+        fmtB |= mxgemm.PRESHUFFLED
+    D = H.empty_d(M, N)
+    return mxgemm, (fa, fmtB, layout, A, sA, B, sB, D, M, N, K), D
+
+
+@pytest.mark.parametrize("fa,fb,layout,M,N,K,pre,variant", [
+    (E4, E4, NT, 4096, 2304, 1024, True, 0),      # persistent 256 x 256
+    (E4, E4, NT, 256, 256, 256, True, 1),          # 64 x 64 tiles
+    (E5, E4, NN, 528, 768, 1024, False, 0),
+    (E5, E4, TN, 544, 512, 768, False, 0),
+    (F4, F4, NT, 1024, 1024, 1024, True, None),
+    (F4, F4, NN, 544, 768, 1024, False, 0),
+    (T4, T5, NT, 1024, 1280, 512, False, None),
+])
+def test_dense_graph_replay(fa, fb, layout, M, N, K, pre, variant):
+    mxgemm, args, D = _dense_case(fa, fb, layout, M, N, K, pre)
+    if variant is not None:
+        assert mxgemm.dense_variant(args[0], args[1], layout, M, N, K) == variant
+    _check_graph(lambda: mxgemm.run(*args), [D])
+
+
+def test_fused_graph_replay():
+    mxgemm, args, D = _dense_case(E4, E4, NT, 1024, 1536, 1024, True, seed=11)
+    bias = H.dev((synth.normal(13, (1536,)).view(np.uint32) >> 16).astype(np.uint16).view(np.int16))
+    _check_graph(lambda: mxgemm.run_fused(*args, bias=bias, activation=mxgemm.ACT_GELU_TANH), [D])
+
+
+GROUPED_SHAPES = [(128, 2048, 1024), (1024, 2048, 7168), (4096, 2048, 4096)]
+
+
+@pytest.mark.parametrize("totM,N,K", GROUPED_SHAPES)
+def test_grouped_graph_replay(totM, N, K):
+    mxgemm = _mx()
+    G = 8
+    m_sizes = synth.m_sizes_for(totM, G, 7000 + totM)
+    xq, xs = synth.quant_group_act(synth.normal(7001, (totM, K)), m_sizes)
+    wq, ws = synth.quant_group_weight(synth.normal(7002, (G, N, K), 0.02))
+    W = H.dev(wq)
+    Wp = torch.empty_like(W)
+    mxgemm.grouped_preshuffle_b(G, W, Wp, N, K)
+    dm, dx, dxs, dws = H.dev(m_sizes), H.dev(xq), H.dev(xs), H.dev(ws)
+    D = H.empty_d(totM, N)
+    _check_graph(lambda: mxgemm.grouped_run(G, dm, dx, dxs, Wp, dws, D, totM, N, K, b_preshuffled=True), [D])
+
+
+def test_grouped_graph_replay_covers_every_kernel():
+    mxgemm = _mx()
+    picked = {mxgemm.grouped_variant(8, t, n, k, True) for t, n, k in GROUPED_SHAPES}
+    assert picked == {mxgemm.GROUPED_STREAM64, mxgemm.GROUPED_STREAM128, mxgemm.GROUPED_TILED}
+
+
+def test_quantizers_graph_replay():
+    mxgemm = _mx()
+    rows, K = 1024, 2048
+    x = H.dev(synth.normal(7101, (rows, K)))
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=H.DEV)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=H.DEV)
+    _check_graph(lambda: mxgemm.quantize_mx(mxgemm.MXFP8_E4M3, x, codes, scales, rows, K), [codes, scales])
+    c4 = torch.empty((rows, K // 2), dtype=torch.uint8, device=H.DEV)
+    _check_graph(lambda: mxgemm.quantize_mx(mxgemm.MXFP4_E2M1, x, c4, scales, rows, K), [c4, scales])
+    ts = torch.empty((1,), dtype=torch.float32, device=H.DEV)
+    _check_graph(lambda: mxgemm.quantize_tensor(mxgemm.FP8_E4M3_TENSOR, x, codes, ts, rows * K), [codes, ts])
+    G = 8
+    m_sizes = H.dev(synth.m_sizes_for(rows, G, 7102))
+    xs = torch.empty((rows * K // 128,), dtype=torch.float32, device=H.DEV)
+    _check_graph(lambda: mxgemm.grouped_quantize_act(G, m_sizes, x, codes, xs, rows, K), [codes, xs])
+    N = 256
+    w = H.dev(synth.normal(7103, (G, N, K), 0.02))
+    wc = torch.empty((G, N, K), dtype=torch.uint8, device=H.DEV)
+    wsc = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=H.DEV)
+    _check_graph(lambda: mxgemm.grouped_quantize_weight(G, w, wc, wsc, N, K), [wc, wsc])
+
+
+def test_preshuffles_graph_replay():
+    mxgemm = _mx()
+    N, K = 768, 1024
+    q, s = synth.quant_mx(synth.normal(7201, (N, K)), "e4m3")
+    B, sB = H.dev(q), H.dev(s)
+    Bp = torch.empty(mxgemm.preshuffle_b_bytes(E4, N, K), dtype=torch.uint8, device=H.DEV)
+    sBp = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=H.DEV)
+    _check_graph(lambda: mxgemm.preshuffle_b(E4, NT, B, Bp, N, K), [Bp])
+    _check_graph(lambda: mxgemm.preshuffle_scales(sB, sBp, N, K), [sBp])
