@@ -7,7 +7,10 @@
 #include <stdint.h>
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
 #include <stdio.h>
+#include <tuple>
 
 #include "../../include/mxgemm.h"
 #include "kernels.hpp"
@@ -101,6 +104,7 @@ extern "C" const char *mxgemm_status_string(int s) {
     case MXG_ERR_UNSUPPORTED: return "unsupported format, layout or shape";
     case MXG_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case MXG_ERR_HIP: return "HIP runtime error";
+    case MXG_ERR_IO: return "tune cache file could not be read or written, or is malformed";
     default: return "unknown status";
   }
 }
@@ -298,12 +302,11 @@ __global__ void grouped_zero_kernel(const int64_t *m_sizes, int G, uint16_t *D, 
 }
 }  // namespace
 
-extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
-                         const void *WQ, const float *w_scale, void *D, int64_t totM, int64_t N,
-                         int64_t K, int b_preshuffled, hipStream_t stream) {
-  const int v = grouped_fp8_gemm_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K,
-                                          b_preshuffled);
-  if (v != MXG_OK) return v;
+namespace {
+// One grouped GEMM with the given kernel (arguments already validated).
+int launch_grouped(int variant, int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
+                   const void *WQ, const float *w_scale, void *D, int64_t totM, int64_t N, int64_t K,
+                   int b_preshuffled, hipStream_t stream) {
   if (totM == 0 || N == 0) return MXG_OK;
   if (K == 0) {
     hipLaunchKernelGGL(grouped_zero_kernel, dim3((unsigned)cdiv(totM * N, 256)), dim3(256), 0,
@@ -321,7 +324,6 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
   a.N = N;
   a.K = K;
   a.G = G;
-  const int variant = grouped_fp8_gemm_variant(G, totM, N, K, b_preshuffled);
   const int BM = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
   const int BN = variant == MXG_GROUPED_TILED ? 128 : 64;
   a.tiles_n = (int)(N / BN);
@@ -358,6 +360,17 @@ extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *X
     hipLaunchKernelGGL(pick_grouped_dense(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
   }
   return launch_status();
+}
+}  // namespace
+
+extern "C" int grouped_fp8_gemm_run(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
+                         const void *WQ, const float *w_scale, void *D, int64_t totM, int64_t N,
+                         int64_t K, int b_preshuffled, hipStream_t stream) {
+  const int v = grouped_fp8_gemm_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K,
+                                          b_preshuffled);
+  if (v != MXG_OK) return v;
+  return launch_grouped(grouped_fp8_gemm_variant(G, totM, N, K, b_preshuffled), G, m_sizes, XQ, x_scale,
+                        WQ, w_scale, D, totM, N, K, b_preshuffled, stream);
 }
 
 namespace {
@@ -461,8 +474,38 @@ int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
 // each at least the weights' bytes at ~5 TB/s.  The constants are fitted to
 // the table's measurements; at 50 of its 64 points the estimate picks the
 // table's kernel, and at the other 14 one within 18% of it.
+namespace {
+// Autotuned winners of the grouped GEMM, keyed as "Add FlyDSL grouped
+// groupwise FP8 GEMM for ROCm" (Tile selection) keys its persisted cache:
+// (nextPow2(totM), N, K, b_preshuffled), here with G as well, since the tile
+// count depends on it.  Filled by grouped_fp8_gemm_autotune or a cache file;
+// consulted before the static table.
+typedef std::tuple<int, int, int64_t, int64_t, int> TuneKey;   // G, log2 nextPow2(totM), N, K, preshuffled
+std::mutex tune_mutex;
+std::map<TuneKey, int> tune_cache;
+
+int ceil_log2(int64_t x) {
+  int l = 0;
+  while ((1ll << l) < x) ++l;
+  return l;
+}
+
+TuneKey tune_key(int G, int64_t totM, int64_t N, int64_t K, int pre) {
+  return TuneKey(G, ceil_log2(totM), N, K, pre != 0 ? 1 : 0);
+}
+
+bool valid_variant(int v) {
+  return v == MXG_GROUPED_STREAM64 || v == MXG_GROUPED_TILED || v == MXG_GROUPED_STREAM128;
+}
+}  // namespace
+
 extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K, int b_preshuffled) {
   if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM64;
+  {
+    std::lock_guard<std::mutex> lock(tune_mutex);
+    const auto it = tune_cache.find(tune_key(G, totM, N, K, b_preshuffled));
+    if (it != tune_cache.end()) return it->second;
+  }
   const int listed = grouped_table_variant(G, totM, N, K, b_preshuffled);
   if (listed >= 0) return listed;
   const double cus = cu_count(), nst = (double)(K / 128);
@@ -476,6 +519,111 @@ extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t 
   const double t_d = std::max(std::ceil(tiles_d / cus) * (1.67 * nst + 20.0), wmin);
   if (t64 <= t128 && t64 <= t_d) return MXG_GROUPED_STREAM64;
   return t128 <= t_d ? MXG_GROUPED_STREAM128 : MXG_GROUPED_TILED;
+}
+
+extern "C" int grouped_fp8_gemm_autotune(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
+                                         const void *WQ, const float *w_scale, void *D, int64_t totM,
+                                         int64_t N, int64_t K, int b_preshuffled, int reps, int *variant_out,
+                                         float *us_out, hipStream_t stream) {
+  const int v = grouped_fp8_gemm_validate(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K,
+                                          b_preshuffled);
+  if (v != MXG_OK) return v;
+  if (reps < 1 || reps > 1000) return MXG_ERR_INVALID_ARG;
+  if (totM == 0 || N == 0 || K == 0) return MXG_ERR_INVALID_ARG;   // nothing to time
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return MXG_ERR_HIP;
+  if (cap != hipStreamCaptureStatusNone) return MXG_ERR_INVALID_ARG;   // it waits on events
+  const int variants[3] = {MXG_GROUPED_STREAM64, MXG_GROUPED_STREAM128, MXG_GROUPED_TILED};
+  float us[3] = {0.f, 0.f, 0.f};
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return MXG_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return MXG_ERR_HIP;
+  }
+  int rc = MXG_OK;
+  for (int i = 0; i < 3 && rc == MXG_OK; ++i) {
+    // one untimed launch, then reps timed ones back to back
+    rc = launch_grouped(variants[i], G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_preshuffled, stream);
+    if (rc != MXG_OK) break;
+    if (hipEventRecord(e0, stream) != hipSuccess) { rc = MXG_ERR_HIP; break; }
+    for (int r = 0; r < reps && rc == MXG_OK; ++r)
+      rc = launch_grouped(variants[i], G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_preshuffled, stream);
+    if (rc != MXG_OK) break;
+    float ms = 0.f;
+    if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      rc = MXG_ERR_HIP;
+      break;
+    }
+    us[i] = ms * 1000.f / (float)reps;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != MXG_OK) return rc;
+  int best = 0;
+  for (int i = 1; i < 3; ++i)
+    if (us[i] < us[best]) best = i;
+  {
+    std::lock_guard<std::mutex> lock(tune_mutex);
+    tune_cache[tune_key(G, totM, N, K, b_preshuffled)] = variants[best];
+  }
+  if (variant_out) *variant_out = variants[best];
+  if (us_out)
+    for (int i = 0; i < 3; ++i) us_out[variants[i]] = us[i];
+  return MXG_OK;
+}
+
+extern "C" int mxgemm_tune_cache_save(const char *path) {
+  if (!path) return MXG_ERR_INVALID_ARG;
+  FILE *f = fopen(path, "w");
+  if (!f) return MXG_ERR_IO;
+  bool ok = fprintf(f, "# grouped G log2(nextPow2(totM)) N K b_preshuffled variant\n") > 0;
+  {
+    std::lock_guard<std::mutex> lock(tune_mutex);
+    for (const auto &kv : tune_cache)
+      ok = ok && fprintf(f, "grouped %d %d %lld %lld %d %d\n", std::get<0>(kv.first), std::get<1>(kv.first),
+                         (long long)std::get<2>(kv.first), (long long)std::get<3>(kv.first),
+                         std::get<4>(kv.first), kv.second) > 0;
+  }
+  ok = (fclose(f) == 0) && ok;
+  return ok ? MXG_OK : MXG_ERR_IO;
+}
+
+extern "C" int mxgemm_tune_cache_load(const char *path) {
+  if (!path) return MXG_ERR_INVALID_ARG;
+  FILE *f = fopen(path, "r");
+  if (!f) return MXG_ERR_IO;
+  std::map<TuneKey, int> entries;
+  char line[256];
+  bool ok = true;
+  while (ok && fgets(line, sizeof line, f)) {
+    if (line[0] == '#' || line[0] == '\n') continue;
+    int G = 0, l2 = 0, pre = 0, var = 0;
+    long long N = 0, K = 0;
+    char tail = 0;
+    const int n = sscanf(line, "grouped %d %d %lld %lld %d %d %c", &G, &l2, &N, &K, &pre, &var, &tail);
+    ok = n == 6 && G >= 1 && G <= MXG_GROUPED_MAX_G && l2 >= 0 && l2 < 48 && N > 0 && K > 0 &&
+         (pre == 0 || pre == 1) && valid_variant(var);
+    if (ok) entries[TuneKey(G, l2, (int64_t)N, (int64_t)K, pre)] = var;
+  }
+  ok = ok && !ferror(f);
+  fclose(f);
+  if (!ok) return MXG_ERR_IO;
+  std::lock_guard<std::mutex> lock(tune_mutex);
+  for (const auto &kv : entries) tune_cache[kv.first] = kv.second;
+  return MXG_OK;
+}
+
+extern "C" int mxgemm_tune_cache_clear(void) {
+  std::lock_guard<std::mutex> lock(tune_mutex);
+  tune_cache.clear();
+  return MXG_OK;
+}
+
+extern "C" int64_t mxgemm_tune_cache_size(void) {
+  std::lock_guard<std::mutex> lock(tune_mutex);
+  return (int64_t)tune_cache.size();
 }
 
 extern "C" int64_t mxgemm_preshuffle_b_bytes(int fmtB, int64_t N, int64_t K) {

@@ -26,6 +26,8 @@ EXPORTS = (
     "mxgemm_init", "mxgemm_status_string", "mxgemm_run", "mxgemm_validate",
     "mxgemm_run_fused", "mxgemm_validate_fused", "mxgemm_dense_variant",
     "grouped_fp8_gemm_run", "grouped_fp8_gemm_validate", "grouped_fp8_gemm_variant",
+    "grouped_fp8_gemm_autotune", "mxgemm_tune_cache_save", "mxgemm_tune_cache_load",
+    "mxgemm_tune_cache_clear", "mxgemm_tune_cache_size",
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
@@ -58,6 +60,16 @@ _lib.grouped_fp8_gemm_validate.restype = _i
 _lib.grouped_fp8_gemm_validate.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i]
 _lib.grouped_fp8_gemm_variant.restype = _i
 _lib.grouped_fp8_gemm_variant.argtypes = [_i, _i64, _i64, _i64, _i]
+_lib.grouped_fp8_gemm_autotune.restype = _i
+_lib.grouped_fp8_gemm_autotune.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _i, _p, _p, _p]
+_lib.mxgemm_tune_cache_save.restype = _i
+_lib.mxgemm_tune_cache_save.argtypes = [ctypes.c_char_p]
+_lib.mxgemm_tune_cache_load.restype = _i
+_lib.mxgemm_tune_cache_load.argtypes = [ctypes.c_char_p]
+_lib.mxgemm_tune_cache_clear.restype = _i
+_lib.mxgemm_tune_cache_clear.argtypes = []
+_lib.mxgemm_tune_cache_size.restype = _i64
+_lib.mxgemm_tune_cache_size.argtypes = []
 _lib.mxgemm_preshuffle_b_bytes.restype = _i64
 _lib.mxgemm_preshuffle_b_bytes.argtypes = [_i, _i64, _i64]
 _lib.mxgemm_preshuffle_b.restype = _i
@@ -165,6 +177,33 @@ def grouped_variant(G, totM, N, K, b_preshuffled=True):
     grouped_run launches for these shapes on the current device."""
     return _lib.grouped_fp8_gemm_variant(G, totM, N, K, int(bool(b_preshuffled)))
 
+
+def grouped_autotune(G, m_sizes, XQ, x_scale, WQ, w_scale, D, totM, N, K, b_preshuffled=True, reps=10,
+                     stream=None):
+    """Time the three grouped kernels on these buffers, record the fastest in
+    the library's tune cache; returns (variant, [us per call by variant])."""
+    v = ctypes.c_int(-1)
+    us = (ctypes.c_float * 3)()
+    _check(_lib.grouped_fp8_gemm_autotune(G, _ptr(m_sizes), _ptr(XQ), _ptr(x_scale), _ptr(WQ), _ptr(w_scale),
+                                          _ptr(D), totM, N, K, int(bool(b_preshuffled)), reps,
+                                          ctypes.byref(v), us, _stream(stream)), "grouped_fp8_gemm_autotune")
+    return v.value, list(us)
+
+
+def tune_cache_save(path):
+    _check(_lib.mxgemm_tune_cache_save(os.fsencode(path)), "mxgemm_tune_cache_save")
+
+
+def tune_cache_load(path):
+    _check(_lib.mxgemm_tune_cache_load(os.fsencode(path)), "mxgemm_tune_cache_load")
+
+
+def tune_cache_clear():
+    _check(_lib.mxgemm_tune_cache_clear(), "mxgemm_tune_cache_clear")
+
+
+def tune_cache_size():
+    return _lib.mxgemm_tune_cache_size()
 
 def preshuffle_b_bytes(fmtB, N, K):
     return _lib.mxgemm_preshuffle_b_bytes(fmtB, N, K)

@@ -28,7 +28,9 @@
  *  - Calls are stream-ordered and asynchronous: exactly one kernel is
  *    enqueued on `stream` (0 = the null stream) per successful call, with
  *    one exception, mxgemm_quantize_tensor, which enqueues four (its scale
- *    output serves as the amax word between them; see there).
+ *    output serves as the amax word between them; see there).  The tuning
+ *    call grouped_fp8_gemm_autotune is the one call that waits for the
+ *    device (see there).
  *  - All argument checks are synchronous and happen before anything is
  *    enqueued; on error nothing is enqueued and outputs are untouched.
  *  - No C++ exception crosses this ABI.  Returns MXG_OK (0) or a negative
@@ -58,7 +60,8 @@ typedef enum {
   MXG_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum          */
   MXG_ERR_UNSUPPORTED = -2,   /* combination or divisibility not built          */
   MXG_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned               */
-  MXG_ERR_HIP = -4            /* the HIP runtime reported an error              */
+  MXG_ERR_HIP = -4,           /* the HIP runtime reported an error              */
+  MXG_ERR_IO = -5             /* tune cache file unreadable, unwritable, malformed */
 } mxg_status;
 
 /* Operand format = element encoding + scale kind (one per operand). */
@@ -243,6 +246,45 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
  */
 enum { MXG_GROUPED_STREAM64 = 0, MXG_GROUPED_TILED = 1, MXG_GROUPED_STREAM128 = 2 };
 int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K, int b_preshuffled);
+
+/*
+ * Autotuning of the grouped kernel choice ("Add FlyDSL grouped groupwise
+ * FP8 GEMM for ROCm", Tile selection: winners are autotuned per shape and
+ * persisted in a cache keyed on (nextPow2(totM), N, K, b_preshuffled), the
+ * static table being the default).  The cache here is keyed on (G,
+ * nextPow2(totM), N, K, b_preshuffled), lives in the process, is shared by
+ * every thread and device, and is consulted by grouped_fp8_gemm_variant
+ * (and so by grouped_fp8_gemm_run) before the static table.
+ *
+ * grouped_fp8_gemm_autotune: runs the grouped GEMM of these arguments
+ * (validated as grouped_fp8_gemm_run validates them) with each of the three
+ * kernels, once untimed and then `reps` times (1..1000), timed with HIP
+ * events on `stream`; records the fastest in the cache and returns it in
+ * *variant_out (may be NULL) and the three mean times in us_out[variant]
+ * (three floats, microseconds per call, indexed by MXG_GROUPED_*; may be
+ * NULL).  D holds a correct result afterwards.  Unlike every other call it
+ * waits for the device (it synchronizes on its events), so it must not be
+ * called while `stream` is being captured (MXG_ERR_INVALID_ARG); totM, N or
+ * K of 0 is MXG_ERR_INVALID_ARG (nothing to time).  Tune before capture.
+ *
+ * mxgemm_tune_cache_save / _load: write the cache to, or merge entries from,
+ * a text file: a '#' comment line, then one line per entry,
+ * "grouped G log2m N K b_preshuffled variant" (log2m: log2 of nextPow2(totM)).
+ * A file that cannot be opened or written, or any malformed line, is
+ * MXG_ERR_IO; a failed load changes nothing.  NULL path: MXG_ERR_INVALID_ARG.
+ * mxgemm_tune_cache_clear empties the cache; mxgemm_tune_cache_size counts
+ * its entries.  These four never touch the device.
+ */
+int grouped_fp8_gemm_autotune(int G, const int64_t *m_sizes,
+                              const void *XQ, const float *x_scale,
+                              const void *WQ, const float *w_scale,
+                              void *D, int64_t totM, int64_t N, int64_t K,
+                              int b_preshuffled, int reps, int *variant_out,
+                              float *us_out, hipStream_t stream);
+int mxgemm_tune_cache_save(const char *path);
+int mxgemm_tune_cache_load(const char *path);
+int mxgemm_tune_cache_clear(void);
+int64_t mxgemm_tune_cache_size(void);
 
 /*
  * Preshuffle: one-time re-layout of a B operand (weights) into the order in

@@ -33,7 +33,7 @@ int main(void) {
       a[k++] = v;
       p = end;
     }
-    if (k < 1) { printf("malformed: %s", line); ++bad; continue; }
+    if (k < 1) { printf("malformed: %s", line); ++bad; continue; }   /* at least the expected result */
     const long long expect = a[k - 1];
     const int na = k - 1;
     long long got = 0;
@@ -55,6 +55,12 @@ int main(void) {
     } else if (!strcmp(name, "grouped_fp8_gemm_run") && na == 11) {
       got = grouped_fp8_gemm_run((int)a[0], (const int64_t *)PTR(a[1]), PTR(a[2]), PTR(a[3]), PTR(a[4]),
                                  PTR(a[5]), PTR(a[6]), a[7], a[8], a[9], (int)a[10], NULL);
+    } else if (!strcmp(name, "grouped_fp8_gemm_autotune") && na == 14) {
+      got = grouped_fp8_gemm_autotune((int)a[0], (const int64_t *)PTR(a[1]), PTR(a[2]), PTR(a[3]), PTR(a[4]),
+                                      PTR(a[5]), PTR(a[6]), a[7], a[8], a[9], (int)a[10], (int)a[11],
+                                      (int *)PTR(a[12]), (float *)PTR(a[13]), NULL);
+    } else if (!strcmp(name, "mxgemm_tune_cache_size") && na == 0) {
+      got = mxgemm_tune_cache_size();
     } else if (!strcmp(name, "mxgemm_preshuffle_b_bytes") && na == 3) {
       got = mxgemm_preshuffle_b_bytes((int)a[0], a[1], a[2]);
     } else if (!strcmp(name, "mxgemm_preshuffle_scales_bytes") && na == 2) {

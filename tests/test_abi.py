@@ -142,6 +142,11 @@ REJECT_CALLS = [
     ("grouped_fp8_quantize_weight", (0, P, P, P, 128, 128), -2),     # G < 1
     ("grouped_fp8_quantize_weight", (8, P + 4, P, P, 128, 128), -3),  # misaligned w
     ("grouped_fp8_quantize_weight", (8, P, P, P, 0, 128), 0),        # N = 0: no-op
+    ("grouped_fp8_gemm_autotune", (0, P, P, P, P, P, P, 128, 128, 128, 0, 10, 0, 0), -2),     # G < 1
+    ("grouped_fp8_gemm_autotune", (8, P, P, P, P, P, P, 128, 128, 128, 0, 0, 0, 0), -1),     # reps < 1
+    ("grouped_fp8_gemm_autotune", (8, P, P, P, P, P, P, 128, 128, 128, 0, 1001, 0, 0), -1),  # reps > 1000
+    ("grouped_fp8_gemm_autotune", (8, P, P, P, P, P, P, 0, 128, 128, 0, 10, 0, 0), -1),      # nothing to time
+    ("grouped_fp8_gemm_autotune", (8, P, P, P, P, P + 2, P, 128, 128, 128, 0, 10, 0, 0), -3),  # misaligned w_scale
 ]
 
 def test_ops_reject_bad_args_before_device_use():
@@ -185,3 +190,65 @@ def test_fused_rejects_before_device_use():
     lib = _mx().lib()
     assert lib.mxgemm_run_fused(0, 0, 1, P, P, P, P, P, 256, 256, 256, P, 0, None) == -2
     assert lib.mxgemm_run_fused(0, 0, 0, P, P, P, P, P, 256, 256, 256, None, 9, None) == -1
+
+
+# ---- tune cache (host only) -------------------------------------------------
+
+def test_tune_cache_file_round_trip(tmp_path):
+    m = _mx()
+    m.tune_cache_clear()
+    try:
+        # an unusual shape the static table does not list: G = 3, totM = 300
+        # (nextPow2 512, log2m 9), N = 384, K = 640, preshuffled
+        default = m.grouped_variant(3, 300, 384, 640, True)
+        forced = m.GROUPED_STREAM128 if default != m.GROUPED_STREAM128 else m.GROUPED_STREAM64
+        f = tmp_path / "tune.txt"
+        f.write_text("# a comment\ngrouped 3 9 384 640 1 %d\n" % forced)
+        m.tune_cache_load(str(f))
+        assert m.tune_cache_size() == 1
+        assert m.grouped_variant(3, 300, 384, 640, True) == forced
+        assert m.grouped_variant(3, 257, 384, 640, True) == forced        # same nextPow2(totM)
+        assert m.grouped_variant(3, 256, 384, 640, True) == default       # another bucket
+        assert m.grouped_variant(3, 300, 384, 640, False) == default      # plain weights: no entry
+        out = tmp_path / "saved.txt"
+        m.tune_cache_save(str(out))
+        lines = [ln for ln in out.read_text().splitlines() if not ln.startswith("#")]
+        assert lines == ["grouped 3 9 384 640 1 %d" % forced]
+        m.tune_cache_clear()
+        assert m.tune_cache_size() == 0 and m.grouped_variant(3, 300, 384, 640, True) == default
+        m.tune_cache_load(str(out))                                      # what was saved loads back
+        assert m.grouped_variant(3, 300, 384, 640, True) == forced
+    finally:
+        m.tune_cache_clear()
+
+
+@pytest.mark.parametrize("text", [
+    "grouped 3 9 384 640 1 7\n",          # unknown kernel
+    "grouped 0 9 384 640 1 0\n",          # G < 1
+    "grouped 3 9 384 640 2 0\n",          # preshuffled flag not 0/1
+    "grouped 3 9 384 640 1 0 extra\n",    # trailing field
+    "dense 3 9 384 640 1 0\n",            # unknown kind
+    "grouped 3 9 384\n",                  # short line
+])
+def test_tune_cache_rejects_malformed_files_and_loads_nothing(tmp_path, text):
+    m = _mx()
+    m.tune_cache_clear()
+    try:
+        f = tmp_path / "bad.txt"
+        f.write_text("grouped 3 9 384 640 1 0\n" + text)
+        with pytest.raises(m.MxgemmError) as e:
+            m.tune_cache_load(str(f))
+        assert e.value.status == -5
+        assert m.tune_cache_size() == 0
+    finally:
+        m.tune_cache_clear()
+
+
+def test_tune_cache_io_errors(tmp_path):
+    m = _mx()
+    lib = m.lib()
+    assert lib.mxgemm_tune_cache_load(None) == -1
+    assert lib.mxgemm_tune_cache_save(None) == -1
+    assert lib.mxgemm_tune_cache_load(str(tmp_path / "missing.txt").encode()) == -5
+    assert lib.mxgemm_tune_cache_save(str(tmp_path / "no_dir" / "x.txt").encode()) == -5
+    assert m.status_string(-5)

@@ -292,3 +292,44 @@ def test_grouped_1024_groups_tiled(preshuffled):
     im, inn = _edge_samples(np.random.default_rng(6), m_sizes, N, 20000)
     ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
     assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
+
+
+def test_grouped_autotune_records_the_fastest_and_the_run_uses_it():
+    """The tuner times all three kernels on the caller's buffers, records the
+    fastest under (G, nextPow2(totM), N, K, preshuffled), leaves a correct
+    result in D, and every later call with that key launches the recorded
+    kernel; under graph capture it refuses and enqueues nothing."""
+    from block_scaled_precision_03_amd import mxgemm
+    m_sizes = synth.m_sizes_for(1024, 8, 9301)
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(9302, m_sizes, 2048, 1024)
+    N, K, G = 2048, 1024, 8
+    W = H.dev(WQ)
+    Wp = torch.empty_like(W)
+    mxgemm.grouped_preshuffle_b(G, W, Wp, N, K)
+    dm, dx, dxs, dws = H.dev(m_sizes), H.dev(XQ), H.dev(xs), H.dev(ws)
+    ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
+    mxgemm.tune_cache_clear()
+    try:
+        D = torch.full((totM, N), float("nan"), dtype=torch.bfloat16, device=H.DEV)
+        v, us = mxgemm.grouped_autotune(G, dm, dx, dxs, Wp, dws, D, totM, N, K, True, reps=5)
+        torch.cuda.synchronize()
+        assert v in (mxgemm.GROUPED_STREAM64, mxgemm.GROUPED_STREAM128, mxgemm.GROUPED_TILED)
+        assert all(u > 0 for u in us) and us[v] == min(us)
+        assert mxgemm.tune_cache_size() == 1
+        assert mxgemm.grouped_variant(G, totM, N, K, True) == v
+        assert mxgemm.grouped_variant(G, 700, N, K, True) == v          # same nextPow2(totM)
+        H.assert_close(H.bf16_to_f64(D), ref, "grouped after autotune")
+        D2 = torch.full((totM, N), float("nan"), dtype=torch.bfloat16, device=H.DEV)
+        mxgemm.grouped_run(G, dm, dx, dxs, Wp, dws, D2, totM, N, K, b_preshuffled=True)
+        torch.cuda.synchronize()
+        H.assert_close(H.bf16_to_f64(D2), ref, "grouped with the tuned kernel")
+        # the tuner waits on events: refused while the stream is captured
+        lib = mxgemm.lib()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rc = lib.grouped_fp8_gemm_autotune(G, dm.data_ptr(), dx.data_ptr(), dxs.data_ptr(), Wp.data_ptr(),
+                                               dws.data_ptr(), D2.data_ptr(), totM, N, K, 1, 5, None, None,
+                                               torch.cuda.current_stream().cuda_stream)
+        assert rc == -1
+    finally:
+        mxgemm.tune_cache_clear()
