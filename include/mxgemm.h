@@ -147,8 +147,9 @@ int mxgemm_run(int fmtA, int fmtB, int layout,
 enum { MXG_DENSE_TILE256 = 0, MXG_DENSE_TILE64 = 1 };
 int mxgemm_dense_variant(int fmtA, int fmtB, int layout, int64_t M, int64_t N, int64_t K);
 
-/* Host-only check of mxgemm_run's arguments (no device call).  Returns the
- * status mxgemm_run would return before enqueueing anything. */
+/* Host-only check of mxgemm_run's arguments (no device call), for the
+ * operation cited at mxgemm_run.  Returns the status mxgemm_run would return
+ * before enqueueing anything. */
 int mxgemm_validate(int fmtA, int fmtB, int layout,
                     const void *A, const void *sA, const void *B, const void *sB,
                     const void *D, int64_t M, int64_t N, int64_t K);
@@ -183,7 +184,8 @@ int mxgemm_run_fused(int fmtA, int fmtB, int layout,
                      void *D, int64_t M, int64_t N, int64_t K,
                      const void *bias, int activation, hipStream_t stream);
 
-/* Host-only check of mxgemm_run_fused's arguments (no device call). */
+/* Host-only check of mxgemm_run_fused's arguments (no device call), for the
+ * operation cited at mxgemm_run_fused; same return as that call's checks. */
 int mxgemm_validate_fused(int fmtA, int fmtB, int layout,
                           const void *A, const void *sA, const void *B, const void *sB,
                           const void *D, int64_t M, int64_t N, int64_t K,
@@ -318,9 +320,19 @@ int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K
                              hipStream_t stream);
 
 /*
- * grouped_fp8_preshuffle_b: plain E4M3 weights [G, N, K] -> WQ_out of the
- * same byte size, consumable by grouped_fp8_gemm_run with b_preshuffled = 1.
- * N and K must be multiples of 128.
+ * grouped_fp8_preshuffle_b -- the one-time weight swizzle that callers run at
+ * load time so that the grouped GEMM reads its B operand in the order its
+ * matrix-core K-loop consumes it ("Add FlyDSL grouped groupwise FP8 GEMM for
+ * ROCm", PR body: the preshuffled sibling op and its weight swizzle).
+ *
+ * WQ      device E4M3 [G, N, K] row-major (K contiguous), 16-byte aligned.
+ * WQ_out  device, caller-allocated, the same G*N*K bytes, 16-byte aligned;
+ *         each group's [N, K] block becomes the preshuffled block that
+ *         grouped_fp8_gemm_run reads with b_preshuffled = 1.  Must not
+ *         overlap WQ.
+ * Errors: MXG_ERR_INVALID_ARG (G outside 1..MXG_GROUPED_MAX_G, negative
+ * size, null pointer), MXG_ERR_UNSUPPORTED (N or K not a multiple of 128,
+ * the weight scale-block size), MXG_ERR_MISALIGNED.  N or K = 0: no-op.
  */
 int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out,
                              int64_t N, int64_t K, hipStream_t stream);
@@ -417,7 +429,9 @@ int grouped_fp8_quantize_weight(int G, const float *w, void *codes, float *w_sca
 /*
  * mxgemm_mfma_ceiling -- a measurement aid, not part of the GEMM path: one
  * workgroup per compute unit, eight waves each running 32 independent chains
- * of the scaled 16x16x128 matrix-core instruction for `iters` iterations
+ * of the scaled 16x16x128 matrix-core instruction that the GEMMs are built on
+ * ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", Architecture support)
+ * for `iters` iterations
  * (2 * 16 * 16 * 128 FLOP per instruction), E4M3 operands for an FP8 fmt and
  * E2M1 for MXG_MXFP4_E2M1, neutral scales.  Its time gives the throughput the
  * instruction sustains on this device with nothing else running.  clk: device
