@@ -60,6 +60,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // workgroup's wait-barrier-compute chain overlaps the other's.
 constexpr int GS_OCC = 2;
 
+// The 256 x 256 grouped kernel leaves a partial last round of tiles to the
+// streaming kernel when those tiles' 128 x 64 pieces take at most this many
+// rounds of it (grouped_split_end).
+constexpr int GROUPED_TAIL_ROUNDS = 2;
+
 // Compute units of the current device: the grid size of the persistent dense
 // kernel (one workgroup per compute unit).  Queried once per device.
 int cu_count() {
@@ -313,7 +318,7 @@ int launch_grouped(int variant, int G, const int64_t *m_sizes, const void *XQ, c
                        stream, m_sizes, G, (uint16_t *)D, totM, N);
     return launch_status();
   }
-  GroupedArgs a;
+  GroupedArgs a = {};
   a.m_sizes = m_sizes;
   a.XQ = (const uint8_t *)XQ;
   a.WQ = (const uint8_t *)WQ;
@@ -357,7 +362,19 @@ int launch_grouped(int variant, int G, const int64_t *m_sizes, const void *XQ, c
     const int64_t tiles = (int64_t)d.tiles_m * d.tiles_n;
     if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
     const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
+    // With at most `grid` tiles there is one round and no tail to split off.
+    const bool tail = tiles > (int64_t)grid;
+    const unsigned tail_grid = (unsigned)(GS_OCC * cu_count());
+    d.tail_grid = (int)tail_grid;
+    d.tail_rounds = tail ? GROUPED_TAIL_ROUNDS : 0;
     hipLaunchKernelGGL(pick_grouped_dense(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
+    if (tail) {
+      a.tiles_n = (int)(N / 64);
+      a.tiles_nb = d.tiles_n;
+      a.main_grid = (int)grid;
+      a.tail_rounds = GROUPED_TAIL_ROUNDS;
+      hipLaunchKernelGGL(pick_grouped_tail(pre), dim3(tail_grid), dim3(256), 0, stream, a);
+    }
   }
   return launch_status();
 }
@@ -386,70 +403,70 @@ struct GroupedTile {
   int8_t log2m, pre, variant;
 };
 const GroupedTile GROUPED_TILES[] = {
-    {1280, 8192, 7, 0, 0},   //   27.0   42.1  103.6 us
-    {1280, 8192, 7, 1, 0},   //   27.0   42.3  104.2 us
-    {1280, 8192, 8, 0, 0},   //   27.6   42.4  105.8 us
-    {1280, 8192, 8, 1, 0},   //   27.1   42.9  106.9 us
-    {1280, 8192, 9, 0, 0},   //   31.9   43.2  122.7 us
-    {1280, 8192, 9, 1, 0},   //   31.9   43.7  123.3 us
-    {1280, 8192, 10, 0, 0},   //   34.4   44.3  128.9 us
-    {1280, 8192, 10, 1, 0},   //   35.0   45.2  130.2 us
-    {1280, 8192, 11, 0, 2},   //   56.6   53.6  120.8 us
-    {1280, 8192, 11, 1, 2},   //   57.4   55.2  123.5 us
-    {1280, 8192, 12, 0, 2},   //   99.0   93.7  133.5 us
-    {1280, 8192, 12, 1, 2},   //  101.9   95.7  134.3 us
-    {1280, 8192, 13, 0, 1},   //  211.2  191.1  141.3 us
-    {1280, 8192, 13, 1, 1},   //  208.4  179.1  146.0 us
-    {1280, 8192, 14, 0, 1},   //  409.6  361.4  265.3 us
-    {1280, 8192, 14, 1, 1},   //  408.8  352.6  267.0 us
-    {2048, 7168, 7, 0, 0},   //   25.1   38.3   92.5 us
-    {2048, 7168, 7, 1, 0},   //   25.3   39.1   94.4 us
-    {2048, 7168, 8, 0, 0},   //   26.0   38.7   95.8 us
-    {2048, 7168, 8, 1, 0},   //   26.2   39.2   97.6 us
-    {2048, 7168, 9, 0, 0},   //   30.7   39.7  113.3 us
-    {2048, 7168, 9, 1, 0},   //   31.5   40.6  115.0 us
-    {2048, 7168, 10, 0, 2},   //   49.7   47.1  123.1 us
-    {2048, 7168, 10, 1, 2},   //   50.2   48.6  124.3 us
-    {2048, 7168, 11, 0, 0},   //   77.5   83.6  117.0 us
-    {2048, 7168, 11, 1, 0},   //   76.4   82.5  116.4 us
-    {2048, 7168, 12, 0, 2},   //  131.6  126.9  133.0 us
-    {2048, 7168, 12, 1, 2},   //  134.8  127.6  131.9 us
-    {2048, 7168, 13, 0, 1},   //  290.3  264.4  232.4 us
-    {2048, 7168, 13, 1, 1},   //  291.0  258.6  231.8 us
-    {2048, 7168, 14, 0, 1},   //  565.5  506.9  349.4 us
-    {2048, 7168, 14, 1, 1},   //  563.4  496.6  346.4 us
-    {4096, 4096, 7, 0, 0},   //   22.2   29.0   59.6 us
-    {4096, 4096, 7, 1, 0},   //   22.4   29.6   60.4 us
-    {4096, 4096, 8, 0, 0},   //   22.6   28.9   61.8 us
-    {4096, 4096, 8, 1, 0},   //   22.6   30.0   63.8 us
-    {4096, 4096, 9, 0, 2},   //   37.1   31.4   79.4 us
-    {4096, 4096, 9, 1, 2},   //   37.5   32.2   81.2 us
-    {4096, 4096, 10, 0, 0},   //   47.4   50.6   90.9 us
-    {4096, 4096, 10, 1, 0},   //   47.4   50.9   90.9 us
-    {4096, 4096, 11, 0, 0},   //   81.8   87.7   84.7 us
-    {4096, 4096, 11, 1, 0},   //   82.1   88.4   84.5 us
-    {4096, 4096, 12, 0, 2},   //  157.7  144.3  151.9 us
-    {4096, 4096, 12, 1, 2},   //  161.1  142.2  151.0 us
-    {4096, 4096, 13, 0, 1},   //  337.2  301.1  233.3 us
-    {4096, 4096, 13, 1, 1},   //  345.7  290.5  231.0 us
-    {4096, 4096, 14, 0, 1},   //  664.2  558.7  384.0 us
-    {4096, 4096, 14, 1, 1},   //  659.7  565.7  376.5 us
-    {7168, 2304, 7, 0, 0},   //   25.3   32.8   40.7 us
-    {7168, 2304, 7, 1, 0},   //   25.1   33.7   41.7 us
-    {7168, 2304, 8, 0, 0},   //   25.6   33.1   43.1 us
-    {7168, 2304, 8, 1, 0},   //   25.6   34.0   44.3 us
-    {7168, 2304, 9, 0, 0},   //   35.3   35.7   61.0 us
-    {7168, 2304, 9, 1, 0},   //   35.9   36.8   62.6 us
-    {7168, 2304, 10, 0, 2},   //   50.0   48.4   70.2 us
-    {7168, 2304, 10, 1, 2},   //   49.2   48.1   70.3 us
-    {7168, 2304, 11, 0, 2},   //   91.1   89.2  106.0 us
-    {7168, 2304, 11, 1, 2},   //   91.0   90.6  106.3 us
-    {7168, 2304, 12, 0, 1},   //  177.2  146.6  140.0 us
-    {7168, 2304, 12, 1, 1},   //  175.8  160.0  139.5 us
-    {7168, 2304, 13, 0, 1},   //  363.6  318.0  213.3 us
-    {7168, 2304, 13, 1, 1},   //  353.9  315.4  212.6 us
-    {7168, 2304, 14, 0, 1},   //  693.1  611.4  400.2 us
-    {7168, 2304, 14, 1, 1},   //  686.1  597.0  390.9 us
+    {1280, 8192, 7, 0, 0},   //   27.2   42.6  102.7 us
+    {1280, 8192, 7, 1, 0},   //   26.0   41.5  101.2 us
+    {1280, 8192, 8, 0, 0},   //   27.8   42.9  105.0 us
+    {1280, 8192, 8, 1, 0},   //   26.3   41.6  103.3 us
+    {1280, 8192, 9, 0, 0},   //   33.2   44.2  121.7 us
+    {1280, 8192, 9, 1, 0},   //   31.5   42.9  120.2 us
+    {1280, 8192, 10, 0, 0},   //   34.8   45.7  128.9 us
+    {1280, 8192, 10, 1, 0},   //   33.6   44.7  127.1 us
+    {1280, 8192, 11, 0, 2},   //   57.4   55.4  123.5 us
+    {1280, 8192, 11, 1, 2},   //   54.3   54.1  120.0 us
+    {1280, 8192, 12, 0, 0},   //   99.2  101.6  133.1 us
+    {1280, 8192, 12, 1, 2},   //   96.2   91.0  127.1 us
+    {1280, 8192, 13, 0, 1},   //  205.0  182.8  135.2 us
+    {1280, 8192, 13, 1, 1},   //  191.2  167.8  129.6 us
+    {1280, 8192, 14, 0, 1},   //  401.5  327.3  237.0 us
+    {1280, 8192, 14, 1, 1},   //  381.7  312.2  223.0 us
+    {2048, 7168, 7, 0, 0},   //   25.5   39.0   92.7 us
+    {2048, 7168, 7, 1, 0},   //   25.1   38.3   90.8 us
+    {2048, 7168, 8, 0, 0},   //   26.0   39.3   95.2 us
+    {2048, 7168, 8, 1, 0},   //   25.9   38.0   92.9 us
+    {2048, 7168, 9, 0, 0},   //   31.4   41.1  113.5 us
+    {2048, 7168, 9, 1, 0},   //   30.5   39.9  111.3 us
+    {2048, 7168, 10, 0, 2},   //   50.3   48.0  122.0 us
+    {2048, 7168, 10, 1, 2},   //   48.2   47.0  119.1 us
+    {2048, 7168, 11, 0, 0},   //   76.9   84.7  113.7 us
+    {2048, 7168, 11, 1, 0},   //   72.8   79.7  110.4 us
+    {2048, 7168, 12, 0, 1},   //  131.2  135.3  130.4 us
+    {2048, 7168, 12, 1, 2},   //  123.6  123.0  128.5 us
+    {2048, 7168, 13, 0, 1},   //  284.3  247.7  170.2 us
+    {2048, 7168, 13, 1, 1},   //  256.4  232.5  160.1 us
+    {2048, 7168, 14, 0, 1},   //  555.0  459.7  292.3 us
+    {2048, 7168, 14, 1, 1},   //  513.9  442.7  283.4 us
+    {4096, 4096, 7, 0, 0},   //   22.0   29.0   60.3 us
+    {4096, 4096, 7, 1, 0},   //   22.0   28.8   59.1 us
+    {4096, 4096, 8, 0, 0},   //   22.4   29.2   63.4 us
+    {4096, 4096, 8, 1, 0},   //   22.3   29.2   61.7 us
+    {4096, 4096, 9, 0, 2},   //   37.3   32.0   82.1 us
+    {4096, 4096, 9, 1, 2},   //   36.9   31.7   79.1 us
+    {4096, 4096, 10, 0, 0},   //   48.1   52.3   91.2 us
+    {4096, 4096, 10, 1, 0},   //   45.8   49.3   87.7 us
+    {4096, 4096, 11, 0, 0},   //   79.9   92.1   84.3 us
+    {4096, 4096, 11, 1, 0},   //   75.7   84.7   80.6 us
+    {4096, 4096, 12, 0, 1},   //  157.1  142.7  130.8 us
+    {4096, 4096, 12, 1, 2},   //  142.2  123.2  123.5 us
+    {4096, 4096, 13, 0, 1},   //  331.4  260.9  180.7 us
+    {4096, 4096, 13, 1, 1},   //  291.4  245.4  166.2 us
+    {4096, 4096, 14, 0, 1},   //  641.1  484.7  303.2 us
+    {4096, 4096, 14, 1, 1},   //  568.2  476.6  294.5 us
+    {7168, 2304, 7, 0, 0},   //   25.2   33.2   40.9 us
+    {7168, 2304, 7, 1, 0},   //   24.8   33.0   40.9 us
+    {7168, 2304, 8, 0, 0},   //   25.4   33.3   43.4 us
+    {7168, 2304, 8, 1, 0},   //   25.2   33.4   43.2 us
+    {7168, 2304, 9, 0, 0},   //   35.7   36.0   63.7 us
+    {7168, 2304, 9, 1, 0},   //   35.2   36.2   62.0 us
+    {7168, 2304, 10, 0, 2},   //   49.6   47.8   73.4 us
+    {7168, 2304, 10, 1, 2},   //   47.7   46.7   70.9 us
+    {7168, 2304, 11, 0, 0},   //   89.9   93.1   99.6 us
+    {7168, 2304, 11, 1, 0},   //   85.6   85.9   95.4 us
+    {7168, 2304, 12, 0, 1},   //  171.9  145.9  125.9 us
+    {7168, 2304, 12, 1, 1},   //  158.0  134.8  120.4 us
+    {7168, 2304, 13, 0, 1},   //  348.7  280.8  185.6 us
+    {7168, 2304, 13, 1, 1},   //  297.0  261.1  176.3 us
+    {7168, 2304, 14, 0, 1},   //  679.4  541.2  310.7 us
+    {7168, 2304, 14, 1, 1},   //  607.5  518.1  307.0 us
 };
 
 int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
@@ -470,10 +487,12 @@ int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
 //    compute unit walking all tile steps evenly;
 //  - persistent 256 x 256 tiles on the dense pipeline (matrix-core regime):
 //    one tile per compute unit per round, ~1.67 us per 128-K step plus
-//    ~20 us per round (pipeline start, epilogue);
+//    ~20 us per round (pipeline start, epilogue); a partial last round that
+//    goes to the streaming kernel (grouped_split_end) ~1.15 us per 128-K
+//    step plus ~5 us per round of its 128 x 64 pieces;
 // each at least the weights' bytes at ~5 TB/s.  The constants are fitted to
-// the table's measurements; at 50 of its 64 points the estimate picks the
-// table's kernel, and at the other 14 one within 18% of it.
+// the table's measurements; at 49 of its 64 points the estimate picks the
+// table's kernel, and at the other 15 one within 17% of it.
 namespace {
 // Autotuned winners of the grouped GEMM, keyed as "Add FlyDSL grouped
 // groupwise FP8 GEMM for ROCm" (Tile selection) keys its persisted cache:
@@ -516,7 +535,14 @@ extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t 
   const double t64 = std::max(0.6 * (double)(cdiv(totM, 64) + G - 1) * tiles_n * nst / slots, wmin);
   const double t128 = std::max(1.0 * (double)(cdiv(totM, 128) + G - 1) * tiles_n * nst / slots, wmin);
   const double tiles_d = (double)(cdiv(totM, DBM) + G - 1) * (double)cdiv(N, DBN);
-  const double t_d = std::max(std::ceil(tiles_d / cus) * (1.67 * nst + 20.0), wmin);
+  const double round_d = 1.67 * nst + 20.0;
+  const double full = std::floor(tiles_d / cus), r = tiles_d - full * cus;
+  double t_d = full * round_d;
+  if (r > 0) {
+    const double pr = std::ceil(8.0 * r / slots);     // streaming rounds of the tail's pieces
+    t_d += (full >= 1 && pr <= GROUPED_TAIL_ROUNDS) ? pr * (1.15 * nst + 5.0) : round_d;
+  }
+  t_d = std::max(t_d, wmin);
   if (t64 <= t128 && t64 <= t_d) return MXG_GROUPED_STREAM64;
   return t128 <= t_d ? MXG_GROUPED_STREAM128 : MXG_GROUPED_TILED;
 }

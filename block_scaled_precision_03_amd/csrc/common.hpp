@@ -13,7 +13,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
 typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
@@ -33,17 +32,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nb
 __device__ inline uint32_t clamp_records(int64_t remaining) {
   if (remaining <= 0) return 0;
   return remaining > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)remaining;
-}
-
-// 16 bytes per lane from global (via the buffer resource) straight into LDS:
-// lane L's data lands at lds_base + 16*L.  lds_base must be wave-uniform.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, (int)voff, 0, 0, 0);
-}
-
-// 4 bytes per lane into LDS at lds_base + 4*L.
-__device__ inline void dma4(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 4, (int)voff, 0, 0, 0);
 }
 
 // The same DMA issued as inline assembly, invisible to the compiler's
@@ -200,11 +188,5 @@ __device__ inline float activate(int act, float z) {
 }
 
 __device__ inline uint32_t lds_load_u32(const void *p) { return *(const lds_u32_t *)p; }
-__device__ inline void lds_store8(void *p, v2i v) { *(__attribute__((address_space(3))) v2i *)p = v; }
-
-// Wait for this wave's outstanding vector-memory loads (including LDS DMA).
-// s_waitcnt simm16 on gfx9: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8];
-// 0x0F70 = vmcnt(0) with expcnt/lgkmcnt left at their maxima.
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace mxg

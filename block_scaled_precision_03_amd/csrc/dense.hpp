@@ -42,6 +42,7 @@ struct DenseArgs {
   int tiles_m, tiles_n;
   const int64_t *m_sizes;         // groupwise only
   int G;                          // groupwise only
+  int tail_grid, tail_rounds;     // groupwise only: see grouped_split_end
   const uint16_t *bias;           // fused epilogue: BF16 [N] or null
   int act;                        // fused epilogue: ACT_*
 };
@@ -53,12 +54,8 @@ struct TileId {
   int g;
 };
 
-constexpr int DBM = 256, DBN = 256, DNW = 4;
+constexpr int DBM = 256, DBN = 256;
 constexpr int DNW8 = 8;           // waves of the pipelined dense kernel
-constexpr int DSTAGE = (DBM + DBN) * 128;
-
-// ---------------------------------------------------------------------------
-// Global -> LDS stage loaders.  Each issues R*128/1024 wave-wide 1 KiB DMAs.
 
 // LDS placement of staged tiles, chosen for gfx950's LDS, which serves a
 // wave's read in phases over 64 four-byte banks (256 B):
@@ -90,123 +87,14 @@ __device__ constexpr int tswz(int kk) { return (kk & 7) | ((kk & 16) >> 1); }
 // tiles, see rdt4_pair), so the phase's 32 reads hit 32 distinct bank pairs.
 __device__ constexpr int fswz(int kk) { return (kk >> 1) & 7; }
 
-// K-contiguous operand rows [r0, r0+R) x bytes [128*st, 128*st+128).
-template <int R, int NW = DNW>
-__device__ inline void load_nt(const uint8_t *X, int64_t total, int64_t r0, int64_t KB,
-                               int st, uint8_t *lds, int w, int lane) {
-  const int64_t base = r0 * KB + (int64_t)st * 128;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, clamp_records(total - base));
-  constexpr int PER_W = R / 8 / NW;
-#pragma unroll
-  for (int j = 0; j < PER_W; ++j) {
-    const int blk = w * PER_W + j;
-    const int r = blk * 8 + (lane >> 3);
-    const uint32_t voff = (uint32_t)r * (uint32_t)KB + (uint32_t)(((lane & 7) ^ kswz(r)) << 4);
-    dma16(rs, lds + blk * 1024, voff);
-  }
-}
-
-// Preshuffled B (layout documented in preshuffle.hpp): per stage, each of the
-// R/64 column groups contributes 8 KiB (FP8: k-step st; FP4: the two 4 KiB
-// chunks of k-steps 2st and 2st+1, adjacent in memory), copied linearly; in
-// LDS column group c sits at c*8192.
-template <int R, int NW, bool FP4 = false>
-__device__ inline void load_ps(const uint8_t *X, int64_t total, int64_t cg0, int64_t nks,
-                               int st, uint8_t *lds, int w, int lane) {
-  constexpr int CGB = FP4 ? 4096 : 8192;
-  const int64_t ks0 = FP4 ? 2 * (int64_t)st : (int64_t)st;
-  const int64_t base = (cg0 * nks + ks0) * CGB;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, clamp_records(total - base));
-  constexpr int PER_W = (R / 64) * 8 / NW;
-#pragma unroll
-  for (int j = 0; j < PER_W; ++j) {
-    const int idx = w * PER_W + j;
-    const int c = idx >> 3, sub = idx & 7;
-    const uint32_t voff = (uint32_t)(c * nks) * (uint32_t)CGB + sub * 1024 + lane * 16;
-    dma16(rs, lds + idx * 1024, voff);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// LDS -> register fragments for one 16-row tile and one 128-element K step.
-// Matrix-core operand order (gfx950, 8-bit): lane (i = row, q = lane/16) holds
-// k in [16q, 16q+16) then [64+16q, 64+16q+16); 4-bit: k in [32q, 32q+32).
-// The lane's E8M0 scale covers 32-K block q of its row.
-
-__device__ inline v8i frag_nt8(const uint8_t *region, int rloc, int lane) {
-  const int i = lane & 15, q = lane >> 4;
-  const int f = kswz(i);
-  const uint8_t *row = region + (rloc + i) * 128;
-  const v4i lo = lds_read16(row + ((q ^ f) << 4));
-  const v4i hi = lds_read16(row + (((q + 4) ^ f) << 4));
-  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
-
-__device__ inline v8i frag_ps8(const uint8_t *region, int t, int lane) {
-  const v4i lo = lds_read16(region + t * 2048 + lane * 16);
-  const v4i hi = lds_read16(region + t * 2048 + 1024 + lane * 16);
-  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
-
-// FP4: n-tile t of the block, k-step s of the stage.
-__device__ inline v4i frag_ps4(const uint8_t *region, int t, int s, int lane) {
-  return lds_read16(region + (t >> 2) * 8192 + s * 4096 + (t & 3) * 1024 + lane * 16);
-}
-
+// Matrix-core operand order (gfx950) of a 16-row tile and a 128-element K
+// step: 8-bit, lane (i = row, q = lane/16) holds k in [16q, 16q+16) then
+// [64+16q, 64+16q+16); 4-bit, k in [32q, 32q+32) in the low half of the
+// operand register (widen).  The lane's E8M0 scale covers 32-K block q of its
+// row.
 __device__ inline v8i widen(const v4i &v) {
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
-}
-
-// ---------------------------------------------------------------------------
-// Epilogue: FP32 accumulators -> BF16 (RNE) -> LDS -> 16-byte row stores.
-// Wave (wm, wn) owns rows [wm*BM/2, +BM/2) and columns [wn*BN/2, +BN/2) of the
-// block tile; lane (i16, q) holds D[16a + i16][16b + 4q + r], r = 0..3 (the
-// matrix-core result with the B tile as first operand).  In LDS, row m is
-// BN*2 bytes and its 8-byte chunk c sits at position c ^ (m % 16).  Rows at
-// or beyond row_lim and columns at or beyond N are not written.
-template <int BM, int BN, int FM, int FN, int NTHR = 256>
-__device__ inline void store_tile(const v4f (&acc)[FM][FN], float alpha, uint8_t *cs,
-                                  uint16_t *D, int64_t m0, int64_t n0, int64_t row_lim,
-                                  int64_t N, int wm, int wn) {
-  constexpr int ROWB = BN * 2;
-  const int lane = threadIdx.x & 63, i16 = lane & 15, q = lane >> 4;
-  __syncthreads();
-#pragma unroll
-  for (int a = 0; a < FM; ++a) {
-    const int m = wm * (FM * 16) + a * 16 + i16;
-#pragma unroll
-    for (int b = 0; b < FN; ++b) {
-      const int c = (wn * (FN * 16) + b * 16 + 4 * q) >> 2;
-      const v4f v = acc[a][b];
-      const uint32_t lo = pack_bf16x2(v.x * alpha, v.y * alpha);
-      const uint32_t hi = pack_bf16x2(v.z * alpha, v.w * alpha);
-      lds_store8(cs + m * ROWB + ((c ^ (m & 15)) << 3), (v2i){(int)lo, (int)hi});
-    }
-  }
-  __syncthreads();
-  constexpr int PAIRS = BN / 8;                 // 16-byte pairs per row
-  constexpr int RPP = NTHR / PAIRS;             // rows per pass
-  const bool vec_ok = (N & 7) == 0;
-#pragma unroll 4
-  for (int it = 0; it < BM / RPP; ++it) {
-    const int m = it * RPP + (int)threadIdx.x / PAIRS;
-    const int j = (int)threadIdx.x % PAIRS;
-    const int64_t gm = m0 + m, gn = n0 + 8 * j;
-    const int pos = j ^ ((m & 15) >> 1);
-    v4i v = lds_read16(cs + m * ROWB + (pos << 4));
-    if (m & 1) v = (v4i){v.z, v.w, v.x, v.y};
-    if (gm < row_lim) {
-      uint16_t *dst = D + gm * N + gn;
-      if (vec_ok && gn + 8 <= N) {
-        *(v4i *)dst = v;
-      } else {
-        const uint32_t u[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gn + e < N) dst[e] = (uint16_t)(u[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-  }
 }
 
 // vmcnt(n) with expcnt/lgkmcnt left alone (n <= 63).
@@ -1056,18 +944,9 @@ struct DenseLoop {
   }
 };
 
-// The k-th tile of workgroup bid in a persistent grid of P workgroups: it
-// takes virtual tiles bid, bid + P, bid + 2P, ...  Workgroups are dealt to
-// the eight XCDs round-robin, so within each round of P virtual tiles (the
-// ones that run at the same time) those of one XCD (bid % 8 equal) are
-// remapped to a compact band of the tile order.  The tile order walks groups
-// of 8 tile-rows, column by column, so that the 32 tiles an XCD runs at once
-// share 8 A panels and 4 B panels in its L2.
-__device__ inline void persistent_tile(int bid, int k, int P, int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int nb = tiles_m * tiles_n;
-  const int base = k * P;
-  const int size = min(P, nb - base);
-  const int b = base + (((size & 7) == 0) ? (bid & 7) * (size >> 3) + (bid >> 3) : bid);
+// Tile b of the tile order: groups of 8 tile-rows, each walked column by
+// column, so that 32 consecutive tiles share 8 A panels and 4 B panels.
+__device__ inline void tile_in_order(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
   constexpr int GM = 8;
   const int per_group = GM * tiles_n;
   const int g = b / per_group;
@@ -1076,6 +955,20 @@ __device__ inline void persistent_tile(int bid, int k, int P, int tiles_m, int t
   const int in = b - g * per_group;
   tm = first + in % rows;
   tn = in / rows;
+}
+
+// The k-th tile of workgroup bid in a persistent grid of P workgroups: it
+// takes virtual tiles bid, bid + P, bid + 2P, ...  Workgroups are dealt to
+// the eight XCDs round-robin, so within each round of P virtual tiles (the
+// ones that run at the same time) those of one XCD (bid % 8 equal) are
+// remapped to a compact band of the tile order, and the 32 tiles an XCD runs
+// at once share their panels in its L2.
+__device__ inline void persistent_tile(int bid, int k, int P, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int nb = tiles_m * tiles_n;
+  const int base = k * P;
+  const int size = min(P, nb - base);
+  const int b = base + (((size & 7) == 0) ? (bid & 7) * (size >> 3) + (bid >> 3) : bid);
+  tile_in_order(b, tiles_m, tiles_n, tm, tn);
 }
 
 template <int FA, int FB, int SMODE, bool TA, bool TB, bool PSB, bool FUSE = false>

@@ -2,12 +2,12 @@
 // GEMM for ROCm"): for each group g of rows (an expert),
 //   D[r, n] = sum_k dec(XQ[r,k]) xs(r, k/128) * dec(WQ[g,n,k]) ws[g, n/128, k/128].
 //
-// * Tile scheduling: the grid is derived from static shapes only --
-//   (ceil(totM/BM) + G - 1) M-tiles x N/BN N-tiles -- and each workgroup
-//   resolves its group by walking m_sizes on the device (Tile selection;
-//   commit on in-kernel group resolution).  A tile never spans two groups;
-//   tiles past the last group exit.  Every group is clamped to [0, totM) so a
-//   violated sum(m_sizes) == totM precondition cannot reach memory outside D.
+// * Tile scheduling: every grid is derived from static shapes only (a
+//   persistent grid sized by the compute units), and each kernel resolves
+//   its tiles' groups from m_sizes on the device (Tile selection; commit on
+//   in-kernel group resolution).  A tile never spans two groups.  Every
+//   group is clamped to [0, totM) so a violated sum(m_sizes) == totM
+//   precondition cannot reach memory outside D.
 // * Software scaling (Architecture support): each 128-K step runs the scaled
 //   matrix-core instruction with the neutral E8M0 scale into a zeroed
 //   accumulator, then adds that partial times xs(row, kb) * ws(g, n/128, kb)
@@ -17,8 +17,11 @@
 //   k-block kb) sits at i + kb*M_g.
 // * B is either plain [G, N, K] (staged through XOR-swizzled LDS like A) or
 //   preshuffled per group (copied linearly into LDS).
-// This file holds two kernels: grouped_kernel (128 x 128 tiles, one tile per
-// workgroup, for many rows per group) and grouped_stream_kernel (below).
+// This file holds two kernel families: grouped_stream_kernel (BM x 64 tiles,
+// for few rows per group) and grouped_dense_kernel (256 x 256 tiles on the
+// dense kernel's pipeline, for many rows per group), whose last, partial
+// round of tiles the streaming kernel can take over in 128 x 64 pieces
+// (grouped_split_end).
 #pragma once
 #include "../../include/mxgemm.h"
 #include "dense.hpp"
@@ -32,122 +35,24 @@ struct GroupedArgs {
   uint16_t *D;
   int64_t totM, N, K;
   int G, tiles_n;
+  // the streaming kernel as the tail of the 256 x 256 kernel only: that
+  // kernel's 256-column tiles, grid and rule (see grouped_split_end)
+  int tiles_nb, main_grid, tail_rounds;
 };
 
-template <int BM, int BN, bool PSB>
-__global__ __launch_bounds__(256, 1) void grouped_kernel(GroupedArgs p) {
-  constexpr int FM = BM / 32, FN = BN / 32;     // 2x2 waves
-  constexpr int STAGE = (BM + BN) * 128;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
-  const int wm = w >> 1, wn = w & 1;
-  const int i16 = lane & 15;
-  const int tm_flat = blockIdx.x / p.tiles_n;
-  const int tn = blockIdx.x % p.tiles_n;
-
-  // ---- group resolution (uniform across the workgroup)
-  int64_t start = 0, seen = 0, mg = 0, tl = -1;
-  int g = -1;
-  for (int gg = 0; gg < p.G; ++gg) {
-    int64_t s = p.m_sizes[gg];
-    const int64_t room = p.totM - start;
-    s = s < 0 ? 0 : (s > room ? room : s);
-    const int64_t t = (s + BM - 1) / BM;
-    if (tm_flat < seen + t) {
-      g = gg;
-      mg = s;
-      tl = tm_flat - seen;
-      break;
-    }
-    seen += t;
-    start += s;
-  }
-  if (g < 0) return;
-  const int64_t row0 = start + tl * BM;
-  const int64_t row_lim = start + mg;
-  const int64_t n0 = (int64_t)tn * BN;
-  const int64_t K = p.K, N = p.N;
-  const int nst = (int)(K / 128);
-  const int64_t kb_n = K / 128;
-  const uint8_t *Wg = p.WQ + (int64_t)g * N * K;
-  const int64_t wbytes = N * K;
-
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.xs, clamp_records(p.totM * kb_n * 4));
-  const float *wsg = p.ws + (int64_t)g * (N / 128) * kb_n + ((n0 + wn * (BN / 2)) / 128) * kb_n;
-
-  v4f acc[FM][FN];
-#pragma unroll
-  for (int a = 0; a < FM; ++a)
-#pragma unroll
-    for (int b = 0; b < FN; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  float xs_n[FM], ws_n = 0.f;
-  auto load_scales = [&](int st) {
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-      const int64_t local = row0 + wm * (BM / 2) + a * 16 + i16 - start;
-      const int64_t idx = start * kb_n + local + (int64_t)st * mg;
-      xs_n[a] = __uint_as_float(buf_load_u32(rxs, (uint32_t)(idx * 4)));
-    }
-    ws_n = wsg[st];
-  };
-  auto load_stage = [&](int st, uint8_t *buf) {
-    load_nt<BM, 4>(p.XQ, p.totM * K, row0, K, st, buf, w, lane);
-    if constexpr (PSB) load_ps<BN, 4>(Wg, wbytes, n0 / 64, kb_n, st, buf + BM * 128, w, lane);
-    else load_nt<BN, 4>(Wg, wbytes, n0, K, st, buf + BM * 128, w, lane);
-  };
-
-  if (nst > 0) {
-    load_stage(0, smem);
-    load_scales(0);
-  }
-  wait_vmem();
-  __syncthreads();
-
-  for (int st = 0; st < nst; ++st) {
-    const uint8_t *la = smem + (st & 1) * STAGE;
-    const uint8_t *lb = la + BM * 128;
-    float xs_c[FM];
-#pragma unroll
-    for (int a = 0; a < FM; ++a) xs_c[a] = xs_n[a];
-    const float ws_c = ws_n;
-    v8i bf[FN];
-#pragma unroll
-    for (int b = 0; b < FN; ++b) {
-      if constexpr (PSB) bf[b] = frag_ps8(lb, wn * (BN / 32) + b, lane);
-      else bf[b] = frag_nt8(lb, wn * (BN / 2) + b * 16, lane);
-    }
-    if (st + 1 < nst) {
-      load_stage(st + 1, smem + ((st + 1) & 1) * STAGE);
-      load_scales(st + 1);
-    }
-    v8i af = frag_nt8(la, wm * (BM / 2), lane);
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-      v8i af_next;
-      if (a + 1 < FM) af_next = frag_nt8(la, wm * (BM / 2) + (a + 1) * 16, lane);
-      const float sc = xs_c[a] * ws_c;
-#pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        const v4f part = mfma_scaled<F_E4M3, F_E4M3>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f},
-                                                      E8M0_ONE_X4, E8M0_ONE_X4);
-        acc[a][b] += part * sc;
-      }
-      if (a + 1 < FM) af = af_next;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmem();
-    __syncthreads();
-  }
-
-  store_tile<BM, BN, FM, FN>(acc, 1.0f, smem, p.D, row0, n0, row_lim, N, wm, wn);
+// The split of the 256 x 256 grouped kernel's nb tiles (persistent grid of
+// P workgroups, one per compute unit) into [0, end), which it runs in full
+// rounds, and [end, nb), which the streaming kernel (P_tail workgroups)
+// runs after it, each tile cut into 8 pieces of 128 x 64.  A last round of
+// r = nb mod P tiles would leave P - r compute units idle for a whole tile;
+// its 8r pieces take ceil(8r / P_tail) rounds of the streaming kernel, each
+// much shorter than a 256 x 256 tile, so the split is made when that count
+// is at most max_rounds.  Both kernels evaluate this from the same nb.
+__device__ inline int grouped_split_end(int nb, int P, int P_tail, int max_rounds) {
+  const int r = nb % P;
+  if (max_rounds <= 0 || nb <= P || r == 0) return nb;
+  return (8 * r + P_tail - 1) / P_tail <= max_rounds ? nb - r : nb;
 }
-
-}  // namespace mxg
-
-namespace mxg {
 
 // Grouped kernel for few rows per group (the weight-streaming regime: the
 // weights dominate the bytes and HBM, not the matrix cores, sets the time).
@@ -267,9 +172,32 @@ __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable 
   return r;
 }
 
-// BM-row tiles, KS 128-K steps per ring stage, NS ring slots.
-template <bool PSB, int BM, int KS, int NS>
+// Piece t of the tail of the 256 x 256 kernel (tiles [end, nb) of its tile
+// order): tile end + t / 8, row half (t % 8) % 2, column quarter (t % 8) / 2.
+// A half past its group's rows or a quarter past N (the last tile column
+// when N is an odd multiple of 128) is empty: it reads zeros and stores
+// nothing.
+__device__ inline StreamTile tail_piece(const GroupedArgs &p, const GroupTable &gt, int64_t t, int end) {
+  const int v = end + (int)(t >> 3), s = (int)(t & 7);
+  int tm, tn;
+  tile_in_order(v, uni32(gt.mtile[p.G]), p.tiles_nb, tm, tn);
+  const int g = group_of_tile(gt, p.G, tm);
+  StreamTile r;
+  r.g = g;
+  r.start = uni32(gt.rows[g]);
+  r.mg = uni32(gt.rows[g + 1]) - r.start;
+  r.row0 = r.start + (int64_t)(tm - uni32(gt.mtile[g])) * DBM + 128 * (s & 1);
+  r.n0 = (int64_t)tn * DBN + 64 * (s >> 1);
+  if (r.row0 > r.start + r.mg || r.n0 >= p.N) r.row0 = r.start + r.mg;
+  return r;
+}
+
+// BM-row tiles, KS 128-K steps per ring stage, NS ring slots.  TAIL: the
+// kernel runs the tail pieces of the 256 x 256 kernel (BM = 128) in place of
+// its own tiles.
+template <bool PSB, int BM, int KS, int NS, bool TAIL = false>
 __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
+  static_assert(!TAIL || BM == 128, "tail pieces are 128 x 64");
   typedef GroupedStream<BM> S;
   constexpr int FM = S::FM, FN = S::FN, ABLK = S::ABLK;
   constexpr int STAGE = KS * S::STEP;
@@ -286,10 +214,18 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   const int wm = w >> 1, wn = w & 1;
   const int i16 = lane & 15, q = lane >> 4;
 
-  if (w == 0) build_group_table<BM>(p.m_sizes, p.G, p.totM, gt, lane);
+  if (w == 0) build_group_table<TAIL ? DBM : BM>(p.m_sizes, p.G, p.totM, gt, lane);
   __syncthreads();
   const int P = (int)gridDim.x;
-  const int64_t T = (int64_t)uni32(gt.mtile[p.G]) * p.tiles_n;   // real tiles
+  int end = 0;                                      // TAIL: first tile of the tail
+  int64_t T;                                        // real tiles (TAIL: pieces)
+  if constexpr (TAIL) {
+    const int nb = uni32(gt.mtile[p.G]) * p.tiles_nb;
+    end = grouped_split_end(nb, p.main_grid, P, p.tail_rounds);
+    T = (int64_t)(nb - end) * 8;
+  } else {
+    T = (int64_t)uni32(gt.mtile[p.G]) * p.tiles_n;
+  }
   // Workgroup b runs on XCD x = b % 8 (workgroups are dealt to the eight
   // XCDs in turn) as that XCD's r-th, r = b / 8.  Each round of P
   // consecutive tiles (the last round holds T mod P) is cut into eight
@@ -305,6 +241,10 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   if (ntile == 0) return;
   const int64_t off_full = band_start(P) + r, off_last = band_start(last) + r;
   auto tile_of = [&](int64_t i) -> int64_t { return i * P + (i < full ? off_full : off_last); };
+  auto tile_at = [&](int64_t i) -> StreamTile {
+    if constexpr (TAIL) return tail_piece(p, gt, tile_of(i), end);
+    else return stream_tile<BM>(p, gt, tile_of(i));
+  };
   const int64_t K = p.K, N = p.N;
   const int nst = (int)(K / 128);                  // K steps per tile
   const int nsg = (nst + KS - 1) / KS;             // stages per tile
@@ -326,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     int vrows;
   };
   auto make_src = [&](int64_t i) {
-    const StreamTile t = stream_tile<BM>(p, gt, tile_of(i));
+    const StreamTile t = tile_at(i);
     Src s;
     const int64_t abase = t.row0 * K;
     s.ra = rsrc4(p.XQ + abase, clamp_records(p.totM * K - abase));
@@ -447,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     if (++csg == nsg) {
       // Last K step of tile ci: lane (i16, q) holds rows 16a + i16 and
       // columns 16b + 4q .. +3 of the wave's 32 x 32 block.
-      const StreamTile t = stream_tile<BM>(p, gt, tile_of(ci));
+      const StreamTile t = tile_at(ci);
       const int64_t row_lim = t.start + t.mg;
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
@@ -510,8 +450,9 @@ __global__ __launch_bounds__(DNW8 * 64, 1) void grouped_dense_kernel(DenseArgs p
   if (w == 0) build_group_table<DBM>(p.m_sizes, p.G, p.M, gt, lane);
   __syncthreads();
   const int tiles_m = uni32(gt.mtile[p.G]);          // 256-row tiles over all groups
-  const int nb = tiles_m * p.tiles_n;
   const int P = (int)gridDim.x;
+  // tiles [nb, tiles_m * tiles_n) are left to the streaming kernel
+  const int nb = grouped_split_end(tiles_m * p.tiles_n, P, p.tail_grid, p.tail_rounds);
   const int bid = (int)blockIdx.x;
   if (bid >= nb) return;
   const int ntiles = (nb - bid + P - 1) / P;

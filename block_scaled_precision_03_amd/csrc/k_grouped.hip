@@ -11,4 +11,8 @@ grouped_fn pick_grouped_stream(int bm, bool psb) {
   if (bm == 128) return psb ? grouped_stream_kernel<true, 128, 1, 2> : grouped_stream_kernel<false, 128, 1, 2>;
   return nullptr;
 }
+
+grouped_fn pick_grouped_tail(bool psb) {
+  return psb ? grouped_stream_kernel<true, 128, 1, 2, true> : grouped_stream_kernel<false, 128, 1, 2, true>;
+}
 }  // namespace mxg

@@ -45,8 +45,10 @@ dense_fn pick_dense_fp4(int layout, bool psb, bool fuse);
 // k_small.hip: the 64 x 64 NT kernel, every format.
 dense_fn pick_small(int ea, int eb, bool mx, bool psb, bool fuse);
 // k_grouped.hip: the grouped kernels (256 x 256 dense pipeline; persistent
-// streaming with BM-row tiles).
+// streaming with BM-row tiles; the streaming kernel on the dense pipeline's
+// tail pieces).
 dense_fn pick_grouped_dense(bool psb);
 grouped_fn pick_grouped_stream(int bm, bool psb);
+grouped_fn pick_grouped_tail(bool psb);
 
 }  // namespace mxg

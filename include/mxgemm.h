@@ -27,10 +27,12 @@
  *    never allocates, frees or retains caller memory and uses no workspace.
  *  - Calls are stream-ordered and asynchronous: exactly one kernel is
  *    enqueued on `stream` (0 = the null stream) per successful call, with
- *    one exception, mxgemm_quantize_tensor, which enqueues four (its scale
- *    output serves as the amax word between them; see there).  The tuning
- *    call grouped_fp8_gemm_autotune is the one call that waits for the
- *    device (see there).
+ *    two exceptions: mxgemm_quantize_tensor enqueues four (its scale output
+ *    serves as the amax word between them; see there), and
+ *    grouped_fp8_gemm_run enqueues two when it runs MXG_GROUPED_TILED on
+ *    more 256 x 256 tiles than the device has compute units (see
+ *    grouped_fp8_gemm_variant).  The tuning call grouped_fp8_gemm_autotune
+ *    is the one call that waits for the device (see there).
  *  - All argument checks are synchronous and happen before anything is
  *    enqueued; on error nothing is enqueued and outputs are untouched.
  *  - No C++ exception crosses this ABI.  Returns MXG_OK (0) or a negative
@@ -239,12 +241,16 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
  * MXG_GROUPED_STREAM128, the persistent kernel with 64 x 64 or 128 x 64
  * tiles for the weight-streaming regime (few rows per group), or
  * MXG_GROUPED_TILED, the persistent 256 x 256 kernel on the dense pipeline
- * for the matrix-core regime.  A static table keyed on (nextPow2(totM), N,
- * K, b_preshuffled) decides for the shapes it lists ("Add FlyDSL grouped
- * groupwise FP8 GEMM for ROCm", Tile selection: the same key), an estimate
- * of each kernel's time otherwise.  All compute the same function; their
- * results may differ in the last bit of a BF16 output only where their FP32
- * sums do.  Never fails.
+ * for the matrix-core regime (one tile per compute unit per round; when a
+ * last, partial round would leave most compute units idle, its tiles go to
+ * the 128 x 64 streaming kernel, launched after it, as 128 x 64 pieces).  A
+ * static table keyed on (nextPow2(totM), N, K, b_preshuffled) decides for
+ * the shapes it lists ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm",
+ * Tile selection: the same key), an estimate of each kernel's time
+ * otherwise.  All run the same per-element arithmetic (one matrix-core
+ * partial per 128-K block, scaled and added in FP32 in K order), so their
+ * outputs are identical up to the sign of an exactly zero result.  Never
+ * fails.
  */
 enum { MXG_GROUPED_STREAM64 = 0, MXG_GROUPED_TILED = 1, MXG_GROUPED_STREAM128 = 2 };
 int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K, int b_preshuffled);

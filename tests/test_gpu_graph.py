@@ -8,7 +8,8 @@ replay the outputs are overwritten eagerly (NaN or a byte pattern) and the
 device is synchronized, and after it every output must equal the eager
 result bit for bit.  Covered: the persistent and the 64 x 64 dense kernels,
 MX NN/TN, MXFP4 NT/NN, tensor-wise, the fused epilogue, the three grouped
-kernels, the quantizers (the tensor-wise one is four launches) and the
+kernels (and the 256 x 256 one with its tail on the streaming kernel), the
+quantizers (the tensor-wise one is four launches) and the
 preshuffles.
 """
 import numpy as np
@@ -114,7 +115,9 @@ def test_fused_graph_replay():
     _check_graph(lambda: mxgemm.run_fused(*args, bias=bias, activation=mxgemm.ACT_GELU_TANH), [D])
 
 
-GROUPED_SHAPES = [(128, 2048, 1024), (1024, 2048, 7168), (4096, 2048, 4096)]
+# the last: the 256 x 256 kernel followed by the streaming kernel on its
+# partial last round (two launches in the graph)
+GROUPED_SHAPES = [(128, 2048, 1024), (1024, 2048, 7168), (4096, 2048, 4096), (8192, 2048, 7168)]
 
 
 @pytest.mark.parametrize("totM,N,K", GROUPED_SHAPES)

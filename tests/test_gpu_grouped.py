@@ -333,3 +333,89 @@ def test_grouped_autotune_records_the_fastest_and_the_run_uses_it():
         assert rc == -1
     finally:
         mxgemm.tune_cache_clear()
+
+
+def _force_variant(mxgemm, path, G, totM, N, K, variant):
+    """Tune-cache entries (plain and preshuffled) that make grouped_run launch
+    `variant` for this key."""
+    lg = max(0, int(totM - 1).bit_length())
+    with open(path, "w") as f:
+        for pre in (0, 1):
+            f.write("grouped %d %d %d %d %d %d\n" % (G, lg, N, K, pre, variant))
+    mxgemm.tune_cache_clear()
+    mxgemm.tune_cache_load(str(path))
+    assert mxgemm.grouped_variant(G, totM, N, K) == variant
+
+
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_tiled_tail_pieces(preshuffled, tmp_path):
+    """The 256 x 256 kernel's last, partial round goes to the streaming kernel
+    in 128 x 64 pieces.  N = 1152 gives five tile columns, the last one half
+    real, and the groups give 60 row tiles: 300 tiles, of which (on 256
+    compute units) 256 run in one full round and 44 as 352 pieces, among
+    them column quarters past N and the empty half of the last group's
+    82-row last tile.  The result must equal bit for bit those of the 128 x 64
+    and 64 x 64 streaming kernels over the whole problem (the same
+    per-element arithmetic), every row must be written, and sampled entries,
+    the groups' edge rows and every entry of the last group's last 300 rows
+    must match the oracle."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 1152, 1024
+    split = [2000, 0, 3000, 1, 5000, 4690]
+    G = len(split)
+    row_tiles = sum((m + 255) // 256 for m in split)
+    assert row_tiles == 60
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nb = row_tiles * 5
+    if cus == 256:
+        assert nb % cus == 44 and (8 * 44 + 2 * cus - 1) // (2 * cus) <= 2
+    m_sizes, XQ, xs, WQ, ws, totM = _inputs(951, split, N, K)
+    try:
+        _force_variant(mxgemm, tmp_path / "tiled.txt", G, totM, N, K, mxgemm.GROUPED_TILED)
+        D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+        _force_variant(mxgemm, tmp_path / "s128.txt", G, totM, N, K, mxgemm.GROUPED_STREAM128)
+        D128 = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+        _force_variant(mxgemm, tmp_path / "s64.txt", G, totM, N, K, mxgemm.GROUPED_STREAM64)
+        D64 = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    finally:
+        mxgemm.tune_cache_clear()
+    bits = H.bits(D.view(torch.bfloat16))
+    assert not np.any(bits == SENTINEL_BITS)
+    assert np.array_equal(bits, H.bits(D128.view(torch.bfloat16)))
+    assert np.array_equal(bits, H.bits(D64.view(torch.bfloat16)))
+    rng = np.random.default_rng(9)
+    im, inn = _edge_samples(rng, m_sizes, N, 20000)
+    last = np.arange(totM - 300, totM)
+    im = np.concatenate([im, np.repeat(last, N)])
+    inn = np.concatenate([inn, np.tile(np.arange(N), len(last))])
+    ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
+    H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16))[im, inn], ref, "grouped tail pieces")
+
+
+def test_grouped_tiled_tail_pieces_integer_valued_bit_exact(tmp_path):
+    """The split as above with integer-valued codes and power-of-two scales
+    (every partial sum exact in FP32): every entry of the last group, whose
+    rows the tail pieces hold, equals the oracle's bit for bit."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 1152, 1024
+    split = [2000, 0, 3000, 1, 5000, 4690]
+    G = len(split)
+    m_sizes = np.asarray(split, np.int64)
+    totM = int(m_sizes.sum())
+    rng = np.random.default_rng(1152)
+    vals = np.array([0xC0, 0xB8, 0x00, 0x38, 0x40], np.uint8)
+    XQ = vals[rng.integers(0, 5, (totM, K), dtype=np.uint8)]
+    WQ = vals[rng.integers(0, 5, (G, N, K), dtype=np.uint8)]
+    xs = (2.0 ** rng.integers(0, 3, totM * K // 128)).astype(np.float32)
+    ws = (2.0 ** rng.integers(0, 3, (G, N // 128, K // 128))).astype(np.float32)
+    try:
+        _force_variant(mxgemm, tmp_path / "tiled.txt", G, totM, N, K, mxgemm.GROUPED_TILED)
+        D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, True)
+    finally:
+        mxgemm.tune_cache_clear()
+    bits = H.bits(D.view(torch.bfloat16))
+    assert not np.any(bits == SENTINEL_BITS)
+    last = np.arange(totM - split[-1], totM)
+    im, inn = np.repeat(last, N), np.tile(np.arange(N), len(last))
+    ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
+    assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
