@@ -114,11 +114,29 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_current_raw_stream = None
+
+
 def _stream(stream):
+    """The HIP stream handle of `stream`, or torch's current stream on the
+    current device.  After the first call (which goes through the public API
+    and so initializes torch's device state), the current stream is read
+    with torch's raw-handle accessor, which builds no Stream object: a
+    launch-bound call then spends less time here than in the launch."""
+    global _current_raw_stream
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
-    import torch
-    return torch.cuda.current_stream().cuda_stream
+    if _current_raw_stream is None:
+        import torch
+        handle = torch.cuda.current_stream().cuda_stream
+        get_raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        get_dev = getattr(torch._C, "_cuda_getDevice", None)
+        if get_raw is not None and get_dev is not None:
+            _current_raw_stream = lambda: get_raw(get_dev())
+        else:
+            _current_raw_stream = lambda: torch.cuda.current_stream().cuda_stream
+        return handle
+    return _current_raw_stream()
 
 
 def _check(rc, what):

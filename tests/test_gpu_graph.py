@@ -172,3 +172,17 @@ def test_preshuffles_graph_replay():
     sBp = torch.empty(mxgemm.preshuffle_scales_bytes(N, K), dtype=torch.uint8, device=H.DEV)
     _check_graph(lambda: mxgemm.preshuffle_b(E4, NT, B, Bp, N, K), [Bp])
     _check_graph(lambda: mxgemm.preshuffle_scales(sB, sBp, N, K), [sBp])
+
+
+def test_binding_launches_on_the_current_stream():
+    """The binding's default stream is torch's current stream, also inside a
+    `with torch.cuda.stream(...)` block and after it."""
+    mxgemm = _mx()
+    main = torch.cuda.current_stream().cuda_stream
+    assert mxgemm._stream(None) == main
+    assert mxgemm._stream(None) == main
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert mxgemm._stream(None) == side.cuda_stream != main
+    assert mxgemm._stream(None) == main
+    assert mxgemm._stream(side) == side.cuda_stream

@@ -419,3 +419,54 @@ def test_grouped_tiled_tail_pieces_integer_valued_bit_exact(tmp_path):
     im, inn = np.repeat(last, N), np.tile(np.arange(N), len(last))
     ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
     assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
+
+
+def test_grouped_tiled_random_shapes_match_streaming(tmp_path):
+    """Random group counts (1..64) and sizes (some empty), N an odd or even
+    multiple of 128, K from 256 to 1024, rows past the last group, sized so
+    that the 256 x 256 kernel has more tiles than compute units: with its
+    partial last round split off to the streaming kernel or not (the tile
+    count decides; both occur here), its output equals the 128 x 64
+    streaming kernel's over the whole problem bit for bit, and rows outside
+    every group keep the sentinel."""
+    from block_scaled_precision_03_amd import mxgemm
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(4242)
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)   # every E4M3 value but NaN
+    split_seen = {True: 0, False: 0}
+    for case in range(8):
+        G = int(rng.integers(1, 65))
+        N = 128 * int(rng.integers(5, 17))
+        K = 128 * int(rng.integers(2, 9))
+        tiles_n = (N + 255) // 256
+        target = int(rng.integers(cus + 1, 3 * cus)) // tiles_n + G   # 256-row tiles wanted
+        sizes = rng.integers(0, 2 * 256 * target // G + 1, G)
+        sizes[rng.random(G) < 0.2] = 0
+        m_sizes = sizes.astype(np.int64)
+        cover = int(m_sizes.sum())
+        totM = cover + int(rng.integers(0, 300))
+        row_tiles = int(sum((m + 255) // 256 for m in m_sizes))
+        nb = row_tiles * tiles_n
+        grid = min(((totM + 255) // 256 + G - 1) * tiles_n, cus)
+        r = nb % grid
+        split = nb > grid and r > 0 and (8 * r + 2 * cus - 1) // (2 * cus) <= 2
+        if nb <= grid:
+            continue
+        split_seen[split] += 1
+        XQ = codes[rng.integers(0, len(codes), (totM, K))]
+        WQ = codes[rng.integers(0, len(codes), (G, N, K))]
+        xs = (2.0 ** rng.integers(-12, -4, totM * K // 128) * rng.uniform(1, 2, totM * K // 128)).astype(np.float32)
+        ws = (2.0 ** rng.integers(-12, -4, (G, N // 128, K // 128))).astype(np.float32)
+        out = {}
+        for pre in (False, True):
+            try:
+                for v in (mxgemm.GROUPED_TILED, mxgemm.GROUPED_STREAM128):
+                    _force_variant(mxgemm, tmp_path / "v.txt", G, totM, N, K, v)
+                    out[(pre, v)] = H.bits(_run(m_sizes, XQ, xs, WQ, ws, totM, N, K, pre).view(torch.bfloat16))
+            finally:
+                mxgemm.tune_cache_clear()
+            what = "case %d: G=%d totM=%d N=%d K=%d tiles=%d split=%s pre=%s" % (case, G, totM, N, K, nb, split, pre)
+            assert np.array_equal(out[(pre, mxgemm.GROUPED_TILED)], out[(pre, mxgemm.GROUPED_STREAM128)]), what
+            assert np.all(out[(pre, mxgemm.GROUPED_TILED)][cover:] == SENTINEL_BITS), what
+            assert not np.any(out[(pre, mxgemm.GROUPED_TILED)][:cover] == SENTINEL_BITS), what
+    assert split_seen[True] >= 2 and split_seen[False] >= 1, split_seen
