@@ -40,8 +40,8 @@ PEAK_FP8_TFLOPS = 5033.2
 PEAK_MXFP4_TFLOPS = 10066.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_mxfp8_nt_psb_llm_shapes_counters.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_03_amd", "csrc", f)
-                  for f in ("common.hpp", "dense.hpp", "api.hip")]
+CSRC = os.path.join(ROOT, "block_scaled_precision_03_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".hip")))
 C3_CASES = [("fwd", 0, 8192, 11008, 4096), ("dgrad", 1, 8192, 4096, 11008),
             ("wgrad", 2, 11008, 4096, 8192)]
 C2_SHAPES = [(4096, 4096, 4096), (4096, 14336, 4096), (4096, 4096, 14336),
