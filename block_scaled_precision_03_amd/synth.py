@@ -152,6 +152,13 @@ def quant_group_weight(w: np.ndarray):
     return _encode_fp8(y, "e4m3"), s
 
 
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """FP32 data -> BF16 bit patterns (uint16), rounded to nearest even by
+    torch's conversion: the BF16 operands of the BF16 grouped GEMM."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def m_sizes_for(totM: int, G: int, seed: int) -> np.ndarray:
     """Uneven group sizes summing to totM with exactly one empty group."""
     rng = np.random.default_rng(seed)

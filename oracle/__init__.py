@@ -66,6 +66,12 @@ def lib():
         L.oracle_activation.argtypes = [i, d]
         L.oracle_epilogue.restype = i
         L.oracle_epilogue.argtypes = [p, i64, i64, p, i]
+        L.oracle_decode_bf16.restype = d
+        L.oracle_decode_bf16.argtypes = [ctypes.c_uint]
+        L.oracle_grouped_gemm_bf16.restype = i
+        L.oracle_grouped_gemm_bf16.argtypes = [i, p, p, p, i64, i64, i64, p]
+        L.oracle_grouped_entries_bf16.restype = i
+        L.oracle_grouped_entries_bf16.argtypes = [i, p, p, p, i64, i64, i64, p, p, i64, p]
         _lib = L
     return _lib
 
@@ -174,6 +180,40 @@ def grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, idx_m, idx_n):
                                       _ptr(out))
     if rc:
         raise ValueError("oracle_grouped_entries rejected the arguments (%d)" % rc)
+    return out
+
+
+def decode_bf16(bits):
+    """FP64 values of BF16 bit patterns (the oracle's closed-form decoder)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    f = np.vectorize(lambda v: lib().oracle_decode_bf16(int(v)), otypes=[np.float64])
+    return f(b) if b.size else b.astype(np.float64)
+
+
+def grouped_gemm_bf16(m_sizes, X, W, totM, N, K, fill=np.nan):
+    """BF16 grouped GEMM, FP64 [totM, N]: X [totM, K] and W [G, N, K] are BF16
+    bit patterns (uint16); rows in no group keep ``fill``."""
+    ms = _c(m_sizes, np.int64)
+    X = _c(X, np.uint16)
+    W = _c(W, np.uint16)
+    D = np.full((totM, N), fill, dtype=np.float64)
+    rc = lib().oracle_grouped_gemm_bf16(ms.size, _ptr(ms), _ptr(X), _ptr(W), totM, N, K, _ptr(D))
+    if rc:
+        raise ValueError("oracle_grouped_gemm_bf16 rejected the arguments (%d)" % rc)
+    return D
+
+
+def grouped_entries_bf16(m_sizes, X, W, totM, N, K, idx_m, idx_n):
+    ms = _c(m_sizes, np.int64)
+    X = _c(X, np.uint16)
+    W = _c(W, np.uint16)
+    im = _c(idx_m, np.int64)
+    inn = _c(idx_n, np.int64)
+    out = np.empty(im.size, dtype=np.float64)
+    rc = lib().oracle_grouped_entries_bf16(ms.size, _ptr(ms), _ptr(X), _ptr(W), totM, N, K,
+                                           _ptr(im), _ptr(inn), im.size, _ptr(out))
+    if rc:
+        raise ValueError("oracle_grouped_entries_bf16 rejected the arguments (%d)" % rc)
     return out
 
 

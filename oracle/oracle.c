@@ -26,6 +26,8 @@
  *   E5M2: bias 15, IEEE-like: exponent 31 is Inf (m=0) or NaN.
  *   E2M1: bias 1, no Inf/NaN, values {0,.5,1,1.5,2,3,4,6}.
  *   E8M0: 2^(c-127); c=255 is NaN.
+ *   BF16 (operands of the BF16 grouped GEMM): bias 127, 7 fraction bits,
+ *   IEEE-like specials (the upper half of an IEEE binary32).
  *
  * Parity status: every function here is pinned by CPU tests (closed forms,
  * an independent library decoder, exact rational brute force, one-hot and
@@ -569,5 +571,80 @@ int oracle_epilogue(double *D, int64_t M, int64_t N, const uint16_t *bias, int a
             if (bias) z += orc_bf16_value(bias[n]);
             D[m * N + n] = oracle_activation(act, z);
         }
+    return 0;
+}
+
+/* ---- BF16 grouped GEMM ---------------------------------------------------
+ *
+ * "PyTorch on AMD GPUs gains a FlyDSL backend" (Interpretation; the BF16
+ * grouped-GEMM cases of its operator suite): a grouped GEMM over expert
+ * groups of rows that tolerates uneven and empty groups, here with BF16
+ * operands ("Experimental FlyDSL GEMM backend for TE PyTorch", Supported
+ * Data Types, names BF16 among the GEMM input types).  For each group g of
+ * rows [start_g, start_g + m_g):
+ *
+ *     D[r, n] = sum_k x(r, k) * w(g, n, k)
+ *
+ * with x and w the BF16 values, no scales.  Same layout conventions as the
+ * FP8 grouped GEMM above: X [totM, K], W [G, N, K], both K-contiguous.
+ */
+
+/* BF16 from its closed form: sign, 8-bit exponent with bias 127, 7-bit
+ * fraction; exponent 0 is zero or subnormal (f * 2^-133), exponent 255 is
+ * Inf (f = 0) or NaN. */
+double oracle_decode_bf16(unsigned bits)
+{
+    const int s = (bits >> 15) & 1, e = (bits >> 7) & 0xFF, f = bits & 0x7F;
+    double v;
+    if (e == 0xFF) v = f ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)f, -133);
+    else v = ldexp(1.0 + f / 128.0, e - 127);
+    return s ? -v : v;
+}
+
+int oracle_grouped_gemm_bf16(int G, const int64_t *m_sizes, const uint16_t *X, const uint16_t *W,
+                             int64_t totM, int64_t N, int64_t K, double *D)
+{
+    int64_t start = 0;
+    for (int g = 0; g < G; ++g) {
+        int64_t mg = m_sizes[g], i;
+        if (mg < 0 || start + mg > totM) return -2;
+        const uint16_t *Wg = W + (int64_t)g * N * K;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (i = 0; i < mg; ++i) {
+            int64_t r = start + i;
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += oracle_decode_bf16(X[r * K + k]) * oracle_decode_bf16(Wg[n * K + k]);
+                D[r * N + n] = acc;
+            }
+        }
+        start += mg;
+    }
+    return 0;
+}
+
+/* Selected entries; a row in no group yields NaN. */
+int oracle_grouped_entries_bf16(int G, const int64_t *m_sizes, const uint16_t *X, const uint16_t *W,
+                                int64_t totM, int64_t N, int64_t K,
+                                const int64_t *idx_m, const int64_t *idx_n, int64_t count, double *out)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        int64_t r = idx_m[i], n = idx_n[i], start = 0;
+        int g, found = -1;
+        for (g = 0; g < G; ++g) {
+            if (r >= start && r < start + m_sizes[g]) { found = g; break; }
+            start += m_sizes[g];
+        }
+        if (found < 0 || r >= totM) { out[i] = NAN; continue; }
+        const uint16_t *Wg = W + (int64_t)found * N * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += oracle_decode_bf16(X[r * K + k]) * oracle_decode_bf16(Wg[n * K + k]);
+        out[i] = acc;
+    }
     return 0;
 }
