@@ -723,6 +723,74 @@ extern "C" int grouped_fp8_preshuffle_b(int G, const void *WQ, void *WQ_out, int
 }
 
 
+extern "C" int grouped_bf16_gemm_validate(int G, const int64_t *m_sizes, const void *X, const void *W,
+                                          const void *D, int64_t totM, int64_t N, int64_t K,
+                                          int b_preshuffled) {
+  (void)b_preshuffled;
+  if (G < 1 || G > MXG_GROUPED_MAX_G) return MXG_ERR_UNSUPPORTED;
+  if (totM < 0 || N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (!m_sizes) return MXG_ERR_INVALID_ARG;
+  if (N % 64 != 0 || K % 64 != 0) return MXG_ERR_UNSUPPORTED;
+  if (totM >= MAX_DIM || N >= MAX_DIM || 2 * K > MAX_ROW_BYTES) return MXG_ERR_UNSUPPORTED;
+  if (totM == 0 || N == 0) return MXG_OK;
+  if (!D) return MXG_ERR_INVALID_ARG;
+  if (!aligned(D, 16) || !aligned(m_sizes, 8)) return MXG_ERR_MISALIGNED;
+  if (K == 0) return MXG_OK;
+  if (!X || !W) return MXG_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(W, 16)) return MXG_ERR_MISALIGNED;
+  return MXG_OK;
+}
+
+extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *X, const void *W, void *D,
+                                     int64_t totM, int64_t N, int64_t K, int b_preshuffled,
+                                     hipStream_t stream) {
+  const int v = grouped_bf16_gemm_validate(G, m_sizes, X, W, D, totM, N, K, b_preshuffled);
+  if (v != MXG_OK) return v;
+  if (totM == 0 || N == 0) return MXG_OK;
+  if (K == 0) {
+    hipLaunchKernelGGL(grouped_zero_kernel, dim3((unsigned)cdiv(totM * N, 256)), dim3(256), 0,
+                       stream, m_sizes, G, (uint16_t *)D, totM, N);
+    return launch_status();
+  }
+  // 256 x 256 tiles on the dense pipeline, one persistent workgroup per
+  // compute unit, every group's rows cut into 256-row tiles
+  DenseArgs d = {};
+  d.A = (const uint8_t *)X;
+  d.B = (const uint8_t *)W;
+  d.D = (uint16_t *)D;
+  d.M = totM;
+  d.N = N;
+  d.K = K;
+  d.a_bytes = totM * K * 2;
+  d.b_bytes = (int64_t)G * N * K * 2;
+  d.tiles_n = (int)cdiv(N, DBN);
+  d.tiles_m = (int)(cdiv(totM, DBM) + G - 1);      // upper bound; the kernel counts them
+  d.m_sizes = m_sizes;
+  d.G = G;
+  const int64_t tiles = (int64_t)d.tiles_m * d.tiles_n;
+  if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+  const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
+  hipLaunchKernelGGL(pick_grouped_bf16(b_preshuffled != 0), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
+  return launch_status();
+}
+
+extern "C" int grouped_bf16_preshuffle_b(int G, const void *W, void *W_out, int64_t N, int64_t K,
+                                         hipStream_t stream) {
+  if (G < 1 || G > MXG_GROUPED_MAX_G || N < 0 || K < 0) return MXG_ERR_INVALID_ARG;
+  if (N % 64 != 0 || K % 64 != 0) return MXG_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return MXG_OK;
+  if (!W || !W_out) return MXG_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(W_out, 16)) return MXG_ERR_MISALIGNED;
+  // The byte permutation of the 8-bit weights applied to each group's
+  // [N, 2K] bytes: the layout is defined on 128-byte K chunks of 64-row
+  // column groups, which is what the BF16 kernel reads.
+  const int64_t chunks = (int64_t)G * N * (2 * K) / 16;
+  hipLaunchKernelGGL((preshuffle_b_kernel<false, false>), dim3((unsigned)cdiv(chunks, 256)),
+                     dim3(256), 0, stream, (const uint8_t *)W, (uint8_t *)W_out,
+                     (int64_t)G * N, 2 * K, chunks);
+  return launch_status();
+}
+
 extern "C" int mxgemm_mfma_ceiling(int fmt, int64_t iters, void *clk, hipStream_t stream) {
   const FmtInfo f = fmt_info(fmt);
   if (!f.ok || iters < 0 || !clk) return MXG_ERR_INVALID_ARG;

@@ -18,7 +18,7 @@ typedef __attribute__((address_space(3))) v4i lds_v4i;
 typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 
 // Element-format codes understood by the scaled MFMA's cbsz/blgp fields.
-enum : int { F_E4M3 = 0, F_E5M2 = 1, F_E2M1 = 4 };
+enum : int { F_E4M3 = 0, F_E5M2 = 1, F_E2M1 = 4, F_BF16 = 32 };
 
 // Neutral E8M0 scale (2^0) in every byte.
 constexpr int E8M0_ONE_X4 = 0x7F7F7F7F;
@@ -154,6 +154,20 @@ __device__ inline v2i lds_read_tr4(const void *p) {
 template <int FX, int FY>
 __device__ inline v4f mfma_scaled(const v8i &x, const v8i &y, const v4f &c, int sx, int sy) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, sx, 0, sy);
+}
+
+// D += the 16x16x64 BF16 block held as an 8-bit operand fragment holds a
+// 128-byte K chunk: lo half (K elements 8q .. 8q + 7 of a row, q = lane / 16)
+// and hi half (32 + 8q ..) feed two 16x16x32 BF16 matrix-core instructions
+// in K order.  First operand rows = output rows, as mfma_scaled.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ inline v4f mfma_bf16_x2(const v8i &x, const v8i &y, const v4f &c) {
+  const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, x, 0, 1, 2, 3));
+  const bf16x8_t yl = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(y, y, 0, 1, 2, 3));
+  const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, x, 4, 5, 6, 7));
+  const bf16x8_t yh = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(y, y, 4, 5, 6, 7));
+  const v4f r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yl, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, r, 0, 0, 0);
 }
 
 // Two FP32 values -> packed BF16 (lo in bits 0-15), rounded to nearest

@@ -31,7 +31,10 @@ namespace mxg {
 // instruction), tensor-wise (one FP32 per operand, applied in the epilogue),
 // groupwise (the grouped GEMM: FP32 per row and 128-K block of A, per 128 x
 // 128 block of each group's B, applied in software after every 128-K step).
-enum : int { SM_MX = 0, SM_TENSOR = 1, SM_GROUP = 2 };
+// Scale modes: MX (E8M0 per 32 K values), tensor-wise (one FP32 factor per
+// operand), groupwise (FP32 per 1x128 and 128x128 block, grouped GEMM), and
+// grouped without scales (the BF16 grouped GEMM).
+enum : int { SM_MX = 0, SM_TENSOR = 1, SM_GROUP = 2, SM_GNONE = 3 };
 
 struct DenseArgs {
   const uint8_t *A, *B;
@@ -123,6 +126,9 @@ struct DenseLoop {
   static constexpr bool FP4 = (FA == F_E2M1);
   static constexpr bool MX = (SMODE == SM_MX);
   static constexpr bool GROUP = (SMODE == SM_GROUP);
+  static constexpr bool GROUPED = GROUP || SMODE == SM_GNONE;   // B of group g at rows g N
+  static constexpr bool BF = (FA == F_BF16);    // BF16: a 128-byte K chunk is 64 elements
+  static_assert(BF == (FB == F_BF16) && (!BF || (SMODE == SM_GNONE && !TA && !TB)), "BF16 operands");
   static constexpr bool SCALED = MX || GROUP;    // scales staged through LDS
   static constexpr int NW = DNW8;
   static constexpr int KS = FP4 ? 2 : 1;        // 128-element K steps per stage
@@ -177,10 +183,10 @@ struct DenseLoop {
     c.wn = c.w & 3;
     c.i16 = c.lane & 15;
     c.q = c.lane >> 4;
-    c.KB = FP4 ? p.K / 2 : p.K;
+    c.KB = BF ? 2 * p.K : (FP4 ? p.K / 2 : p.K);
     c.nst = (int)(c.KB / 128);
     c.sk32 = p.K / 32;
-    c.nks = p.K / 128;
+    c.nks = BF ? c.KB / 128 : p.K / 128;
     c.ngrp = (p.K + 511) / 512;
     dma_offsets(OPA, c.lane, c.w, c.KB, p.M, c.vo_a);
     dma_offsets(OPB, c.lane, c.w, c.KB, p.N, c.vo_b);
@@ -221,7 +227,7 @@ struct DenseLoop {
     // operand; the resource starts at the tile's first row (plain) or column
     // group (preshuffled), and every offset from there is range-checked.
     int64_t bbase;
-    if constexpr (GROUP) bbase = PSB ? ((int64_t)id.g * p.N + n0) / 64 * c.nks * CGB : ((int64_t)id.g * p.N + n0) * c.KB;
+    if constexpr (GROUPED) bbase = PSB ? ((int64_t)id.g * p.N + n0) / 64 * c.nks * CGB : ((int64_t)id.g * p.N + n0) * c.KB;
     else if constexpr (PSB) bbase = 0;
     else bbase = TB ? (FP4 ? n0 / 2 : n0) : n0 * c.KB;
     t.rb = rsrc4(p.B + bbase, clamp_records(p.b_bytes - bbase));
@@ -319,7 +325,7 @@ struct DenseLoop {
     if constexpr (ALL || PART == 1) load_tile<OPA, 2, 4>(c, t.ra, c.vo_a, c.KB, p.M, st, slot);
     if constexpr (ALL || PART == 2 || PART == 3) {
       constexpr int J0 = (PART == 3) ? 2 : 0, J1 = (PART == 2) ? 2 : 4;
-      if constexpr (PSB && GROUP) {
+      if constexpr (PSB && GROUPED) {
         // column group (4w + j)/8 = w/2, KiB (4w + j)%8 = 4(w%2) + j, from
         // the tile's first column group, range-checked
         const uint32_t add0 = (uint32_t)(((c.w >> 1) * c.nks + st) * CGB) + (uint32_t)(c.w & 1) * 4096u;
@@ -408,7 +414,7 @@ struct DenseLoop {
         dma_asm_v<16, j * 1024>(abase, t.ra, c.vo_a[0], (uint32_t)((v * 8 + j) * 8 * c.KB + 128 * (int64_t)st));
       });
       const uint32_t bbase = slot + B_REG + (uint32_t)v * 8192u;
-      if constexpr (PSB && GROUP) {
+      if constexpr (PSB && GROUPED) {
         // column group v of the tile, range-checked (the last tile of the
         // stack may have fewer than four)
         const uint32_t add0 = (uint32_t)((v * c.nks + st) * CGB);
@@ -817,13 +823,17 @@ struct DenseLoop {
         if (EPI && s == 0) {
           if (e.on) store_rows(c, e, a, acc[a]);
 #pragma unroll
-          for (int b = 0; b < FN; ++b)
-            acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f}, sb[b], sa);
+          for (int b = 0; b < FN; ++b) {
+            if constexpr (BF) acc[a][b] = mfma_bf16_x2(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f});
+            else acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f}, sb[b], sa);
+          }
         } else {
 #pragma unroll
-          for (int b = 0; b < FN; ++b)
+          for (int b = 0; b < FN; ++b) {
             // First operand = B tile: the result lane holds 4 consecutive n.
-            acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb[b], sa);
+            if constexpr (BF) acc[a][b] = mfma_bf16_x2(bf[b], af, acc[a][b]);
+            else acc[a][b] = mfma_scaled<FB, FA>(bf[b], af, acc[a][b], sb[b], sa);
+          }
         }
         if (a + 1 < FM) {
           af = af_next;

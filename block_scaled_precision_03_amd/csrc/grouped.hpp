@@ -439,9 +439,15 @@ namespace mxg {
 //   or preshuffled (the dense kernel's B layout); the last tile of a group
 //   whose N is not a multiple of 256 reads the next group's rows (or zeros
 //   past the end), which no stored output uses.
-template <bool PSB>
+//
+// FMT = F_BF16: the BF16 grouped GEMM ("PyTorch on AMD GPUs gains a FlyDSL
+// backend", Interpretation: grouped GEMM over uneven and empty expert
+// groups) on the same pipeline: BF16 operands (a 128-byte K chunk holds 64
+// elements, two 16x16x32 BF16 matrix-core instructions per fragment pair),
+// no scales, FP32 accumulation, BF16 output.
+template <bool PSB, int FMT = F_E4M3>
 __global__ __launch_bounds__(DNW8 * 64, 1) void grouped_dense_kernel(DenseArgs p) {
-  typedef DenseLoop<F_E4M3, F_E4M3, SM_GROUP, false, false, PSB> L;
+  typedef DenseLoop<FMT, FMT, FMT == F_BF16 ? SM_GNONE : SM_GROUP, false, false, PSB> L;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS_BYTES];
   __shared__ GroupTable gt;
 

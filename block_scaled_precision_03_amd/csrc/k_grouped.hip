@@ -12,6 +12,10 @@ grouped_fn pick_grouped_stream(int bm, bool psb) {
   return nullptr;
 }
 
+dense_fn pick_grouped_bf16(bool psb) {
+  return psb ? grouped_dense_kernel<true, F_BF16> : grouped_dense_kernel<false, F_BF16>;
+}
+
 grouped_fn pick_grouped_tail(bool psb) {
   return psb ? grouped_stream_kernel<true, 128, 1, 2, true> : grouped_stream_kernel<false, 128, 1, 2, true>;
 }

@@ -50,5 +50,6 @@ dense_fn pick_small(int ea, int eb, bool mx, bool psb, bool fuse);
 dense_fn pick_grouped_dense(bool psb);
 grouped_fn pick_grouped_stream(int bm, bool psb);
 grouped_fn pick_grouped_tail(bool psb);
+dense_fn pick_grouped_bf16(bool psb);
 
 }  // namespace mxg

@@ -31,6 +31,7 @@ EXPORTS = (
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
+    "grouped_bf16_gemm_run", "grouped_bf16_gemm_validate", "grouped_bf16_preshuffle_b",
     "mxgemm_quantize_mx", "mxgemm_quantize_tensor", "grouped_fp8_quantize_act", "grouped_fp8_quantize_weight",
 )
 
@@ -82,6 +83,12 @@ _lib.mxgemm_mfma_ceiling.restype = _i
 _lib.mxgemm_mfma_ceiling.argtypes = [_i, _i64, _p, _p]
 _lib.grouped_fp8_preshuffle_b.restype = _i
 _lib.grouped_fp8_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
+_lib.grouped_bf16_gemm_run.restype = _i
+_lib.grouped_bf16_gemm_run.argtypes = [_i, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p]
+_lib.grouped_bf16_gemm_validate.restype = _i
+_lib.grouped_bf16_gemm_validate.argtypes = [_i, _p, _p, _p, _p, _i64, _i64, _i64, _i]
+_lib.grouped_bf16_preshuffle_b.restype = _i
+_lib.grouped_bf16_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
 _lib.mxgemm_quantize_mx.restype = _i
 _lib.mxgemm_quantize_mx.argtypes = [_i, _p, _p, _p, _i64, _i64, _p]
 _lib.mxgemm_quantize_tensor.restype = _i
@@ -244,6 +251,22 @@ def preshuffle_scales(s, s_out, rows, K, stream=None):
 def grouped_preshuffle_b(G, WQ, WQ_out, N, K, stream=None):
     _check(_lib.grouped_fp8_preshuffle_b(G, _ptr(WQ), _ptr(WQ_out), N, K, _stream(stream)),
            "grouped_fp8_preshuffle_b")
+
+
+def grouped_bf16_run(G, m_sizes, X, W, D, totM, N, K, b_preshuffled=False, stream=None):
+    """BF16 grouped GEMM: D[rows of g] = X[rows of g] W[g]^T; see include/mxgemm.h."""
+    _check(_lib.grouped_bf16_gemm_run(G, _ptr(m_sizes), _ptr(X), _ptr(W), _ptr(D), totM, N, K,
+                                      int(bool(b_preshuffled)), _stream(stream)), "grouped_bf16_gemm_run")
+
+
+def grouped_bf16_validate(G, m_sizes, X, W, D, totM, N, K, b_preshuffled=False):
+    return _lib.grouped_bf16_gemm_validate(G, _ptr(m_sizes), _ptr(X), _ptr(W), _ptr(D), totM, N, K,
+                                           int(bool(b_preshuffled)))
+
+
+def grouped_bf16_preshuffle_b(G, W, W_out, N, K, stream=None):
+    _check(_lib.grouped_bf16_preshuffle_b(G, _ptr(W), _ptr(W_out), N, K, _stream(stream)),
+           "grouped_bf16_preshuffle_b")
 
 
 def mfma_ceiling(fmt, iters, clk, stream=None):

@@ -326,6 +326,48 @@ int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K
                              hipStream_t stream);
 
 /*
+ * grouped_bf16_gemm_run -- BF16 grouped GEMM over uneven and empty groups
+ * of rows ("PyTorch on AMD GPUs gains a FlyDSL backend", Interpretation:
+ * grouped GEMM that tolerates uneven and empty expert groups, with BF16
+ * grouped cases in its operator suite; "Experimental FlyDSL GEMM backend for
+ * TE PyTorch", Supported Data Types: BF16 inputs).  For each group g of
+ * rows [start_g, start_g + m_sizes[g]):
+ *     D[r, n] = sum_k x(r, k) * w(g, n, k)
+ * with BF16 operands, FP32 accumulation and one rounding to BF16 (RNE).
+ *
+ * G, m_sizes, totM, D, b_preshuffled: as grouped_fp8_gemm_run (caller
+ *             precondition sum(m_sizes) = totM, rows outside every group
+ *             untouched, empty groups own no rows).
+ * X           BF16 [totM, K] row-major (K contiguous), 16-byte aligned.
+ * W           BF16 [G, N, K] row-major, 16-byte aligned, or (b_preshuffled
+ *             != 0) the output of grouped_bf16_preshuffle_b.
+ * N and K must be multiples of 64 (MXG_ERR_UNSUPPORTED).  K == 0 writes
+ * zeros to every row of every group.  Runs one kernel: 256 x 256 tiles on
+ * the dense pipeline, a group's rows cut into 256-row tiles.
+ * Errors as grouped_fp8_gemm_run.
+ */
+int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *X, const void *W, void *D,
+                          int64_t totM, int64_t N, int64_t K, int b_preshuffled, hipStream_t stream);
+
+/* Host-only check of grouped_bf16_gemm_run's arguments (no device call), for
+ * the operation cited there; same return as that call's checks. */
+int grouped_bf16_gemm_validate(int G, const int64_t *m_sizes, const void *X, const void *W,
+                               const void *D, int64_t totM, int64_t N, int64_t K, int b_preshuffled);
+
+/*
+ * grouped_bf16_preshuffle_b -- the one-time weight swizzle of the BF16
+ * grouped GEMM ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm", PR body:
+ * weights preshuffled once at load time into the matrix-core operand order).
+ * W: BF16 [G, N, K], 16-byte aligned; W_out: caller-allocated, the same
+ * G*N*K*2 bytes, 16-byte aligned, not overlapping W.  N and K multiples of
+ * 64 (MXG_ERR_UNSUPPORTED); MXG_ERR_INVALID_ARG for G outside
+ * 1..MXG_GROUPED_MAX_G, a negative size or a null pointer;
+ * MXG_ERR_MISALIGNED.  N or K = 0: no-op.
+ */
+int grouped_bf16_preshuffle_b(int G, const void *W, void *W_out, int64_t N, int64_t K,
+                              hipStream_t stream);
+
+/*
  * grouped_fp8_preshuffle_b -- the one-time weight swizzle that callers run at
  * load time so that the grouped GEMM reads its B operand in the order its
  * matrix-core K-loop consumes it ("Add FlyDSL grouped groupwise FP8 GEMM for

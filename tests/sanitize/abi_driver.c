@@ -69,6 +69,14 @@ int main(void) {
       got = mxgemm_preshuffle_b((int)a[0], (int)a[1], PTR(a[2]), PTR(a[3]), a[4], a[5], NULL);
     } else if (!strcmp(name, "mxgemm_preshuffle_scales") && na == 4) {
       got = mxgemm_preshuffle_scales(PTR(a[0]), PTR(a[1]), a[2], a[3], NULL);
+    } else if (!strcmp(name, "grouped_bf16_gemm_validate") && na == 9) {
+      got = grouped_bf16_gemm_validate((int)a[0], (const int64_t *)PTR(a[1]), PTR(a[2]), PTR(a[3]),
+                                       PTR(a[4]), a[5], a[6], a[7], (int)a[8]);
+    } else if (!strcmp(name, "grouped_bf16_gemm_run") && na == 9) {
+      got = grouped_bf16_gemm_run((int)a[0], (const int64_t *)PTR(a[1]), PTR(a[2]), PTR(a[3]), PTR(a[4]),
+                                  a[5], a[6], a[7], (int)a[8], NULL);
+    } else if (!strcmp(name, "grouped_bf16_preshuffle_b") && na == 5) {
+      got = grouped_bf16_preshuffle_b((int)a[0], PTR(a[1]), PTR(a[2]), a[3], a[4], NULL);
     } else if (!strcmp(name, "grouped_fp8_preshuffle_b") && na == 5) {
       got = grouped_fp8_preshuffle_b((int)a[0], PTR(a[1]), PTR(a[2]), a[3], a[4], NULL);
     } else if (!strcmp(name, "mxgemm_quantize_mx") && na == 6) {

@@ -106,6 +106,29 @@ def test_grouped_validate(args, expect):
     assert m.grouped_validate(*args) == expect
 
 
+BF16_CASES = [
+    ((8, P, P, P, P, 1024, 2048, 7168, 0), 0),
+    ((8, P, P, P, P, 1024, 192, 320, 1), 0),           # multiples of 64
+    ((0, P, P, P, P, 1024, 2048, 7168, 0), -2),        # G < 1
+    ((2000, P, P, P, P, 1024, 2048, 7168, 0), -2),     # G > max
+    ((8, P, P, P, P, 1024, 2000, 7168, 0), -2),        # N % 64
+    ((8, P, P, P, P, 1024, 2048, 7000, 0), -2),        # K % 64
+    ((8, 0, P, P, P, 1024, 2048, 7168, 0), -1),        # null m_sizes
+    ((8, P, 0, P, P, 1024, 2048, 7168, 0), -1),        # null X
+    ((8, P, P, P, P + 2, 1024, 2048, 7168, 0), -3),    # misaligned D
+    ((8, P, P + 8, P, P, 1024, 2048, 7168, 0), -3),    # misaligned X
+    ((8, P + 4, P, P, P, 1024, 2048, 7168, 0), -3),    # misaligned m_sizes
+    ((8, P, P, P, P, -1, 2048, 7168, 0), -1),          # negative totM
+    ((8, P, P, P, P, 0, 2048, 7168, 1), 0),            # totM = 0
+    ((8, P, 0, 0, P, 1024, 2048, 0, 0), 0),            # K = 0: zeros, no operands read
+]
+
+
+@pytest.mark.parametrize("args,expect", BF16_CASES)
+def test_grouped_bf16_validate(args, expect):
+    assert _mx().lib().grouped_bf16_gemm_validate(*args) == expect
+
+
 def test_preshuffle_sizes():
     m = _mx()
     assert m.preshuffle_b_bytes(0, 4096, 4096) == 4096 * 4096
@@ -124,6 +147,14 @@ REJECT_CALLS = [
     ("mxgemm_preshuffle_b", (0, 0, P, P, 256, 100), -2),
     ("mxgemm_preshuffle_scales", (P, P, 256, 100), -2),
     ("grouped_fp8_preshuffle_b", (8, P, P, 2000, 128), -2),
+    ("grouped_bf16_gemm_run", (8, P, P, P, P, 128, 100, 128, 0), -2),       # N % 64
+    ("grouped_bf16_gemm_run", (0, P, P, P, P, 128, 128, 128, 0), -2),       # G < 1
+    ("grouped_bf16_gemm_run", (8, P, 0, P, P, 128, 128, 128, 0), -1),       # null X
+    ("grouped_bf16_preshuffle_b", (8, P, P, 100, 128), -2),                 # N % 64
+    ("grouped_bf16_preshuffle_b", (8, P, P, 128, 96), -2),                  # K % 64
+    ("grouped_bf16_preshuffle_b", (0, P, P, 128, 128), -1),                 # G < 1
+    ("grouped_bf16_preshuffle_b", (8, P + 2, P, 128, 128), -3),             # misaligned W
+    ("grouped_bf16_preshuffle_b", (8, P, P, 0, 128), 0),                    # N = 0: no-op
     ("mxgemm_quantize_mx", (16, P, P, P, 4, 32), -1),        # tensor-wise fmt
     ("mxgemm_quantize_mx", (0, P, P, P, 4, 48), -2),         # K % 32
     ("mxgemm_quantize_mx", (0, P + 4, P, P, 4, 32), -3),     # misaligned x

@@ -186,3 +186,16 @@ def test_binding_launches_on_the_current_stream():
         assert mxgemm._stream(None) == side.cuda_stream != main
     assert mxgemm._stream(None) == main
     assert mxgemm._stream(side) == side.cuda_stream
+
+
+def test_grouped_bf16_graph_replay():
+    mxgemm = _mx()
+    G, totM, N, K = 8, 2048, 512, 1024
+    m_sizes = synth.m_sizes_for(totM, G, 7301)
+    X = H.dev(synth.bf16_bits(synth.normal(7302, (totM, K))).view(np.int16))
+    W = H.dev(synth.bf16_bits(synth.normal(7303, (G, N, K))).view(np.int16))
+    Wp = torch.empty_like(W)
+    mxgemm.grouped_bf16_preshuffle_b(G, W, Wp, N, K)
+    dm = H.dev(m_sizes)
+    D = H.empty_d(totM, N)
+    _check_graph(lambda: mxgemm.grouped_bf16_run(G, dm, X, Wp, D, totM, N, K, b_preshuffled=True), [D])

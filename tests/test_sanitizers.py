@@ -80,6 +80,9 @@ def _driver_lines():
     for args, expect in test_abi.GROUPED_CASES:
         lines.append(("grouped_fp8_gemm_validate", args, expect))
         lines.append(("grouped_fp8_gemm_run", args, expect if expect != 0 else None))
+    for args, expect in test_abi.BF16_CASES:
+        lines.append(("grouped_bf16_gemm_validate", args, expect))
+        lines.append(("grouped_bf16_gemm_run", args, expect if expect != 0 else None))
     for fn, args, expect in test_abi.REJECT_CALLS:
         lines.append((fn, args, expect))
     for rows, K in ((4096, 4096), (300, 512), (11008, 11008), (-1, 128), (128, 100)):
