@@ -39,6 +39,7 @@ PEAK_MXFP8_TFLOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 FLOP/clk/CU (dense)
 PEAK_FP8_TFLOPS = 5033.2
 PEAK_MXFP4_TFLOPS = 10066.3
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU (dense)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_mxfp8_nt_psb_llm_shapes_counters.txt")
 CSRC = os.path.join(ROOT, "block_scaled_precision_03_amd", "csrc")
 KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".hip")))
@@ -66,7 +67,7 @@ def parse():
     ap.add_argument("--plain-b", action="store_true", help="time with plain (not preshuffled) B")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the tensor-wise FP8 and MXFP4 measurements")
-    ap.add_argument("--profile-leg", choices=("grouped", "mxfp4", "mx_backward", "tensorwise"),
+    ap.add_argument("--profile-leg", choices=("grouped", "grouped_bf16", "mxfp4", "mx_backward", "tensorwise"),
                     help="only launch one leg's kernels, three times per shape (no graphs, no "
                          "cold rotation): the short program a profiler's counter passes run")
     ap.add_argument("--copy-probe", action="store_true",
@@ -302,6 +303,53 @@ def time_calls(torch, call, reps=20, warmup=3):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1000.0 / reps
+
+
+def grouped_bf16_bench(torch, synth, mxgemm, dev, reps=30):
+    """BF16 grouped GEMM at the six grouped shapes (G = 8, the grouped
+    benchmark's m_sizes): us per call warm, plain and preshuffled weights,
+    and cold (weights rotated over > 256 MB), with TFLOP/s against the
+    published dense BF16 peak and the algorithmic bytes' rate."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = []
+    G = 8
+    for si, (totM, N, K) in enumerate(C4_SHAPES):
+        m_sizes = synth.m_sizes_for(totM, G, synth.seed_for(4, 4, si))
+        X = t(synth.bf16_bits(synth.normal(synth.seed_for(8, 1, si), (totM, K))).view(np.int16))
+        Wplain = t(synth.bf16_bits(synth.normal(synth.seed_for(8, 2, si), (G, N, K), 0.02)).view(np.int16))
+        dm = t(m_sizes)
+        copies = max(1, int(np.ceil(300e6 / (Wplain.numel() * 2))) + 1)
+        wps = []
+        for _ in range(copies):
+            wp = torch.empty_like(Wplain)
+            mxgemm.grouped_bf16_preshuffle_b(G, Wplain, wp, N, K)
+            wps.append(wp)
+        D = torch.empty((totM, N), dtype=torch.bfloat16, device=dev)
+        res = {"totM": totM, "N": N, "K": K}
+        for name, W, pre in (("plain", Wplain, False), ("preshuffled", wps[0], True)):
+            res[name + "_us"] = time_calls(torch, lambda: mxgemm.grouped_bf16_run(G, dm, X, W, D, totM, N, K,
+                                                                                 b_preshuffled=pre), reps=reps)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(reps):
+            mxgemm.grouped_bf16_run(G, dm, X, wps[r % copies], D, totM, N, K, b_preshuffled=True)
+        b.record()
+        torch.cuda.synchronize()
+        res["preshuffled_cold_us"] = a.elapsed_time(b) * 1000.0 / reps
+        nonempty = int(np.count_nonzero(m_sizes))
+        algo = 2 * totM * K + 2 * nonempty * N * K + 2 * totM * N
+        best = min(res["plain_us"], res["preshuffled_us"])
+        res["tflops_best_warm"] = 2.0 * totM * N * K / (best * 1e-6) / 1e12
+        res["pct_bf16_peak"] = 100.0 * res["tflops_best_warm"] / PEAK_BF16_TFLOPS
+        res["algo_bytes"] = algo
+        res["gbs_cold"] = algo / (res["preshuffled_cold_us"] * 1e-6) / 1e9
+        out.append(res)
+        log("grouped bf16 %s: plain %.1f us, preshuffled %.1f us (%.0f TFLOP/s, %.1f%% of BF16 peak), cold %.1f us "
+            "(%.0f GB/s)" % ((totM, N, K), res["plain_us"], res["preshuffled_us"], res["tflops_best_warm"],
+                             res["pct_bf16_peak"], res["preshuffled_cold_us"], res["gbs_cold"]))
+        del wps, Wplain, X, D
+        torch.cuda.empty_cache()
+    return out
 
 
 def small_bench(torch, synth, mxgemm, dev):
@@ -624,6 +672,21 @@ def profile_leg(torch, synth, mxgemm, dev, leg, launches=3):
             order.append({"totM": totM, "N": N, "K": K, "G": G,
                           "nonempty_groups": int((m_sizes > 0).sum()),
                           "variant": mxgemm.grouped_variant(G, totM, N, K, True)})
+    elif leg == "grouped_bf16":
+        G = 8
+        for si, (totM, N, K) in enumerate(C4_SHAPES):
+            m_sizes = synth.m_sizes_for(totM, G, synth.seed_for(4, 4, si))
+            X = t(synth.bf16_bits(synth.normal(synth.seed_for(8, 1, si), (totM, K))).view(np.int16))
+            W = t(synth.bf16_bits(synth.normal(synth.seed_for(8, 2, si), (G, N, K), 0.02)).view(np.int16))
+            Wp = torch.empty_like(W)
+            mxgemm.grouped_bf16_preshuffle_b(G, W, Wp, N, K)
+            dm = t(m_sizes)
+            D = torch.empty((totM, N), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(launches):
+                mxgemm.grouped_bf16_run(G, dm, X, Wp, D, totM, N, K, b_preshuffled=True)
+            torch.cuda.synchronize()
+            order.append({"totM": totM, "N": N, "K": K, "G": G, "nonempty_groups": int((m_sizes > 0).sum())})
     elif leg == "mxfp4":
         M = N = K = 8192
         qa, sa = synth.quant_mx(synth.normal(synth.seed_for(5, 1), (M, K)), "e2m1")
@@ -881,6 +944,8 @@ def main():
         result["mxfp4"] = mxfp4_bench(torch, synth, mxgemm, dev)
         log("fused epilogue ...")
         result["fused_epilogue"] = fused_bench(torch, synth, mxgemm, dev)
+        log("BF16 grouped ...")
+        result["grouped_bf16"] = grouped_bf16_bench(torch, synth, mxgemm, dev)
         log("weight preshuffles ...")
         result["preshuffle"] = preshuffle_bench(torch, synth, mxgemm, dev)
         result["mfma_ceiling"] = mfma_ceiling(torch, mxgemm, dev)

@@ -518,6 +518,10 @@ bool valid_variant(int v) {
 }
 }  // namespace
 
+namespace {
+int grouped_model_variant(int G, int64_t totM, int64_t N, int64_t kbytes);
+}  // namespace
+
 extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t K, int b_preshuffled) {
   if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM64;
   {
@@ -527,6 +531,15 @@ extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t 
   }
   const int listed = grouped_table_variant(G, totM, N, K, b_preshuffled);
   if (listed >= 0) return listed;
+  return grouped_model_variant(G, totM, N, K);
+}
+
+namespace {
+// The cost model of the grouped kernel choice (see above), for K given in
+// bytes per row (FP8: K; BF16: 2K): every kernel's step is one 128-byte K
+// chunk, and the weights stream G N kbytes bytes.
+int grouped_model_variant(int G, int64_t totM, int64_t N, int64_t kbytes) {
+  const int64_t K = kbytes;
   const double cus = cu_count(), nst = (double)(K / 128);
   const double wbytes = (double)G * (double)N * (double)K;
   const double wmin = wbytes / 5.0e6;
@@ -546,6 +559,7 @@ extern "C" int grouped_fp8_gemm_variant(int G, int64_t totM, int64_t N, int64_t 
   if (t64 <= t128 && t64 <= t_d) return MXG_GROUPED_STREAM64;
   return t128 <= t_d ? MXG_GROUPED_STREAM128 : MXG_GROUPED_TILED;
 }
+}  // namespace
 
 extern "C" int grouped_fp8_gemm_autotune(int G, const int64_t *m_sizes, const void *XQ, const float *x_scale,
                                          const void *WQ, const float *w_scale, void *D, int64_t totM,
@@ -752,8 +766,29 @@ extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *
                        stream, m_sizes, G, (uint16_t *)D, totM, N);
     return launch_status();
   }
+  const int variant = grouped_bf16_gemm_variant(G, totM, N, K);
+  const bool pre = b_preshuffled != 0;
+  GroupedArgs a = {};
+  a.m_sizes = m_sizes;
+  a.XQ = (const uint8_t *)X;
+  a.WQ = (const uint8_t *)W;
+  a.D = (uint16_t *)D;
+  a.totM = totM;
+  a.N = N;
+  a.K = K;
+  a.G = G;
+  a.tiles_n = (int)(N / 64);
+  if (variant != MXG_GROUPED_TILED) {
+    const int BM = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
+    const int64_t blocks = (cdiv(totM, BM) + G - 1) * a.tiles_n;
+    if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
+    const unsigned P = (unsigned)std::min<int64_t>(blocks, (int64_t)GS_OCC * cu_count());
+    hipLaunchKernelGGL(pick_grouped_stream_bf16(BM, pre), dim3(P), dim3(256), 0, stream, a);
+    return launch_status();
+  }
   // 256 x 256 tiles on the dense pipeline, one persistent workgroup per
-  // compute unit, every group's rows cut into 256-row tiles
+  // compute unit, every group's rows cut into 256-row tiles; a partial last
+  // round goes to the 128 x 64 streaming kernel (grouped_split_end)
   DenseArgs d = {};
   d.A = (const uint8_t *)X;
   d.B = (const uint8_t *)W;
@@ -770,8 +805,23 @@ extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *
   const int64_t tiles = (int64_t)d.tiles_m * d.tiles_n;
   if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
   const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
-  hipLaunchKernelGGL(pick_grouped_bf16(b_preshuffled != 0), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
+  const bool tail = tiles > (int64_t)grid;
+  const unsigned tail_grid = (unsigned)(GS_OCC * cu_count());
+  d.tail_grid = (int)tail_grid;
+  d.tail_rounds = tail ? GROUPED_TAIL_ROUNDS : 0;
+  hipLaunchKernelGGL(pick_grouped_bf16(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
+  if (tail) {
+    a.tiles_nb = d.tiles_n;
+    a.main_grid = (int)grid;
+    a.tail_rounds = GROUPED_TAIL_ROUNDS;
+    hipLaunchKernelGGL(pick_grouped_tail_bf16(pre), dim3(tail_grid), dim3(256), 0, stream, a);
+  }
   return launch_status();
+}
+
+extern "C" int grouped_bf16_gemm_variant(int G, int64_t totM, int64_t N, int64_t K) {
+  if (G < 1 || totM <= 0 || N <= 0 || K <= 0) return MXG_GROUPED_STREAM64;
+  return grouped_model_variant(G, totM, N, 2 * K);
 }
 
 extern "C" int grouped_bf16_preshuffle_b(int G, const void *W, void *W_out, int64_t N, int64_t K,

@@ -195,9 +195,12 @@ __device__ inline StreamTile tail_piece(const GroupedArgs &p, const GroupTable &
 // BM-row tiles, KS 128-K steps per ring stage, NS ring slots.  TAIL: the
 // kernel runs the tail pieces of the 256 x 256 kernel (BM = 128) in place of
 // its own tiles.
-template <bool PSB, int BM, int KS, int NS, bool TAIL = false>
+// FMT = F_BF16: BF16 operands and no scales (a 128-byte K step holds 64
+// values, two 16x16x32 BF16 matrix-core instructions per fragment pair).
+template <bool PSB, int BM, int KS, int NS, bool TAIL = false, int FMT = F_E4M3>
 __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   static_assert(!TAIL || BM == 128, "tail pieces are 128 x 64");
+  constexpr bool BF = (FMT == F_BF16);
   typedef GroupedStream<BM> S;
   constexpr int FM = S::FM, FN = S::FN, ABLK = S::ABLK;
   constexpr int STAGE = KS * S::STEP;
@@ -245,8 +248,8 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     if constexpr (TAIL) return tail_piece(p, gt, tile_of(i), end);
     else return stream_tile<BM>(p, gt, tile_of(i));
   };
-  const int64_t K = p.K, N = p.N;
-  const int nst = (int)(K / 128);                  // K steps per tile
+  const int64_t K = BF ? 2 * p.K : p.K, N = p.N;  // K: bytes per row
+  const int nst = (int)(K / 128);                  // K steps (128 bytes) per tile
   const int nsg = (nst + KS - 1) / KS;             // stages per tile
   const int64_t kb_n = K / 128;
   const int64_t V = ntile * nsg;                   // stages of this workgroup
@@ -314,11 +317,13 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
           dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, vo,
                       (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
       });
-      // activation scales of rows 64h .. 64h + 63 by wave 2h
-      if ((w & 1) == 0 && 32 * w < BM)
-        dma_asm_v<4>(ksc + (uint32_t)(128 * w), live ? rx : rzero, (uint32_t)lane * 4u,
-                     src.xs0 + (uint32_t)(128 * w) + (uint32_t)st * src.mg4);
-      if (w == 1) dma_asm<4>(ksc + (uint32_t)(BM * 4), live ? rw : rzero, 0u, src.ws0 + (uint32_t)st * 4u);
+      if constexpr (!BF) {
+        // activation scales of rows 64h .. 64h + 63 by wave 2h
+        if ((w & 1) == 0 && 32 * w < BM)
+          dma_asm_v<4>(ksc + (uint32_t)(128 * w), live ? rx : rzero, (uint32_t)lane * 4u,
+                       src.xs0 + (uint32_t)(128 * w) + (uint32_t)st * src.mg4);
+        if (w == 1) dma_asm<4>(ksc + (uint32_t)(BM * 4), live ? rw : rzero, 0u, src.ws0 + (uint32_t)st * 4u);
+      }
     });
     if (++iss_sg == nsg) {
       iss_sg = 0;
@@ -370,17 +375,23 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
         const v4i x = lds_read16(lb + ob0 + b * 2048), y = lds_read16(lb + ob1 + b * 2048);
         bf[b] = (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
       }
-      const float wsc = __uint_as_float(lds_load_u32(lsc + BM * 4));
+      float wsc = 1.0f;
+      if constexpr (!BF) wsc = __uint_as_float(lds_load_u32(lsc + BM * 4));
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         const v4i x = lds_read16(la + oa0 + a * 2048), y = lds_read16(la + oa1 + a * 2048);
         const v8i af = (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-        const float sc = __uint_as_float(lds_load_u32(lsc + oxs + a * 64)) * wsc;
+        if constexpr (BF) {
 #pragma unroll
-        for (int b = 0; b < FN; ++b) {
-          const v4f part = mfma_scaled<F_E4M3, F_E4M3>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f},
-                                                        E8M0_ONE_X4, E8M0_ONE_X4);
-          acc[a][b] += part * sc;
+          for (int b = 0; b < FN; ++b) acc[a][b] = mfma_bf16_x2(bf[b], af, acc[a][b]);
+        } else {
+          const float sc = __uint_as_float(lds_load_u32(lsc + oxs + a * 64)) * wsc;
+#pragma unroll
+          for (int b = 0; b < FN; ++b) {
+            const v4f part = mfma_scaled<F_E4M3, F_E4M3>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f},
+                                                          E8M0_ONE_X4, E8M0_ONE_X4);
+            acc[a][b] += part * sc;
+          }
         }
       }
     }

@@ -31,7 +31,8 @@ EXPORTS = (
     "mxgemm_preshuffle_b_bytes", "mxgemm_preshuffle_b",
     "mxgemm_preshuffle_scales_bytes", "mxgemm_preshuffle_scales",
     "grouped_fp8_preshuffle_b", "mxgemm_mfma_ceiling",
-    "grouped_bf16_gemm_run", "grouped_bf16_gemm_validate", "grouped_bf16_preshuffle_b",
+    "grouped_bf16_gemm_run", "grouped_bf16_gemm_validate", "grouped_bf16_gemm_variant",
+    "grouped_bf16_preshuffle_b",
     "mxgemm_quantize_mx", "mxgemm_quantize_tensor", "grouped_fp8_quantize_act", "grouped_fp8_quantize_weight",
 )
 
@@ -87,6 +88,8 @@ _lib.grouped_bf16_gemm_run.restype = _i
 _lib.grouped_bf16_gemm_run.argtypes = [_i, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p]
 _lib.grouped_bf16_gemm_validate.restype = _i
 _lib.grouped_bf16_gemm_validate.argtypes = [_i, _p, _p, _p, _p, _i64, _i64, _i64, _i]
+_lib.grouped_bf16_gemm_variant.restype = _i
+_lib.grouped_bf16_gemm_variant.argtypes = [_i, _i64, _i64, _i64]
 _lib.grouped_bf16_preshuffle_b.restype = _i
 _lib.grouped_bf16_preshuffle_b.argtypes = [_i, _p, _p, _i64, _i64, _p]
 _lib.mxgemm_quantize_mx.restype = _i
@@ -262,6 +265,12 @@ def grouped_bf16_run(G, m_sizes, X, W, D, totM, N, K, b_preshuffled=False, strea
 def grouped_bf16_validate(G, m_sizes, X, W, D, totM, N, K, b_preshuffled=False):
     return _lib.grouped_bf16_gemm_validate(G, _ptr(m_sizes), _ptr(X), _ptr(W), _ptr(D), totM, N, K,
                                            int(bool(b_preshuffled)))
+
+
+def grouped_bf16_variant(G, totM, N, K):
+    """GROUPED_STREAM64, GROUPED_STREAM128 or GROUPED_TILED: the kernel
+    grouped_bf16_run launches for these static shapes."""
+    return _lib.grouped_bf16_gemm_variant(G, totM, N, K)
 
 
 def grouped_bf16_preshuffle_b(G, W, W_out, N, K, stream=None):

@@ -29,9 +29,9 @@
  *    enqueued on `stream` (0 = the null stream) per successful call, with
  *    two exceptions: mxgemm_quantize_tensor enqueues four (its scale output
  *    serves as the amax word between them; see there), and
- *    grouped_fp8_gemm_run enqueues two when it runs MXG_GROUPED_TILED on
- *    more 256 x 256 tiles than the device has compute units (see
- *    grouped_fp8_gemm_variant).  The tuning call grouped_fp8_gemm_autotune
+ *    grouped_fp8_gemm_run and grouped_bf16_gemm_run enqueue two when they
+ *    run MXG_GROUPED_TILED on more 256 x 256 tiles than the device has
+ *    compute units (see grouped_fp8_gemm_variant).  The tuning call grouped_fp8_gemm_autotune
  *    is the one call that waits for the device (see there).
  *  - All argument checks are synchronous and happen before anything is
  *    enqueued; on error nothing is enqueued and outputs are untouched.
@@ -342,12 +342,23 @@ int mxgemm_preshuffle_scales(const void *s, void *s_out, int64_t rows, int64_t K
  * W           BF16 [G, N, K] row-major, 16-byte aligned, or (b_preshuffled
  *             != 0) the output of grouped_bf16_preshuffle_b.
  * N and K must be multiples of 64 (MXG_ERR_UNSUPPORTED).  K == 0 writes
- * zeros to every row of every group.  Runs one kernel: 256 x 256 tiles on
- * the dense pipeline, a group's rows cut into 256-row tiles.
+ * zeros to every row of every group.  The kernel is the one
+ * grouped_bf16_gemm_variant names (the three kernels of the FP8 grouped
+ * GEMM, with BF16 operands; the 256 x 256 one followed, when its last round
+ * is partial, by the streaming kernel on that round's tiles).
  * Errors as grouped_fp8_gemm_run.
  */
 int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *X, const void *W, void *D,
                           int64_t totM, int64_t N, int64_t K, int b_preshuffled, hipStream_t stream);
+
+/* Which kernel grouped_bf16_gemm_run launches for these static shapes
+ * (MXG_GROUPED_*, as grouped_fp8_gemm_variant): the same cost model with
+ * each 128-byte K step holding 64 BF16 values, no static table ("Add FlyDSL
+ * grouped groupwise FP8 GEMM for ROCm", Tile selection: the tile is picked
+ * per shape from static shapes alone).  All three compute the same
+ * per-element sequence (one 64-value partial per 128-byte K step, added in
+ * K order in FP32), so their outputs are identical.  Never fails. */
+int grouped_bf16_gemm_variant(int G, int64_t totM, int64_t N, int64_t K);
 
 /* Host-only check of grouped_bf16_gemm_run's arguments (no device call), for
  * the operation cited there; same return as that call's checks. */

@@ -53,8 +53,9 @@ SPLITS = [
 @pytest.mark.parametrize("preshuffled", [False, True])
 @pytest.mark.parametrize("split", SPLITS)
 def test_bf16_grouped_splits(split, preshuffled):
-    """N = 192 (one 256-column tile, 64 columns past N), K = 320 (five
-    64-element stages): every entry against the oracle, every row written."""
+    """N = 192 (three 64-column tiles; one 256-column tile with 64 columns
+    past N where the 256 x 256 kernel runs), K = 320 (five 64-value K
+    steps): every entry against the oracle, every row written."""
     N, K = 192, 320
     m_sizes, X, W, totM = _inputs(811, split, N, K)
     D = _run(m_sizes, X, W, totM, N, K, preshuffled)
@@ -83,17 +84,43 @@ def _integer_inputs(rng, m_sizes, N, K):
     return X, W, totM
 
 
+# (m_sizes, N, K, kernel): one configuration per kernel the call can run
+EXACT_CASES = [
+    ([30, 0, 47, 1, 60], 576, 1024, "stream64"),
+    ([300, 0, 517, 1, 700], 576, 1024, "stream128"),
+    ([1500, 0, 1077, 2100, 1, 700, 2500, 314], 2048, 1024, "tiled"),
+]
+
+
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_bf16_grouped_integer_valued_bit_exact(preshuffled):
+@pytest.mark.parametrize("m_sizes,N,K,kernel", EXACT_CASES)
+def test_bf16_grouped_integer_valued_bit_exact(m_sizes, N, K, kernel, preshuffled):
     """Values in {0, +-0.5, +-1, +-2}: every FP32 partial sum is exact, so
     each output is the oracle's exact sum rounded once to BF16, bit for bit,
-    over several row and column tiles with ragged groups."""
-    m_sizes = np.array([300, 0, 517, 1, 700], np.int64)
-    N, K = 576, 1024
+    on each of the three kernels (the 256 x 256 one here with 288 tiles: a
+    full round and a last round of 32 tiles handed to the streaming kernel
+    on 256 compute units), ragged groups over several tiles.  The streaming
+    shapes compare every entry, the 256 x 256 one every entry of 600 rows
+    (every group's first and last among them)."""
+    from block_scaled_precision_03_amd import mxgemm
+    m_sizes = np.array(m_sizes, np.int64)
     X, W, totM = _integer_inputs(np.random.default_rng(99), m_sizes, N, K)
+    names = {mxgemm.GROUPED_STREAM64: "stream64", mxgemm.GROUPED_STREAM128: "stream128",
+             mxgemm.GROUPED_TILED: "tiled"}
+    assert names[mxgemm.grouped_bf16_variant(len(m_sizes), totM, N, K)] == kernel
     D = _run(m_sizes, X, W, totM, N, K, preshuffled)
-    ref = oracle.grouped_gemm_bf16(m_sizes, X, W, totM, N, K)
-    assert np.array_equal(H.bits(D.view(torch.bfloat16)), oracle.bf16_rne(ref))
+    bits = H.bits(D.view(torch.bfloat16))
+    if kernel != "tiled":
+        ref = oracle.grouped_gemm_bf16(m_sizes, X, W, totM, N, K)
+        assert np.array_equal(bits, oracle.bf16_rne(ref))
+        return
+    starts = np.concatenate([[0], np.cumsum(m_sizes)])
+    edge = [r for g in range(len(m_sizes)) if m_sizes[g] for r in (starts[g], starts[g + 1] - 1)]
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(5).integers(0, totM, 600 - len(edge))]))
+    im, inn = np.repeat(rows, N), np.tile(np.arange(N), len(rows))
+    ref = oracle.grouped_entries_bf16(m_sizes, X, W, totM, N, K, im, inn)
+    assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
+    assert not np.any(bits == SENTINEL_BITS)
 
 
 def test_bf16_grouped_preshuffled_equals_plain():
