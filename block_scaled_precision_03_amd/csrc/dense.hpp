@@ -30,10 +30,8 @@ namespace mxg {
 // Scale modes: MX (E8M0 per 32 K values, applied by the matrix-core
 // instruction), tensor-wise (one FP32 per operand, applied in the epilogue),
 // groupwise (the grouped GEMM: FP32 per row and 128-K block of A, per 128 x
-// 128 block of each group's B, applied in software after every 128-K step).
-// Scale modes: MX (E8M0 per 32 K values), tensor-wise (one FP32 factor per
-// operand), groupwise (FP32 per 1x128 and 128x128 block, grouped GEMM), and
-// grouped without scales (the BF16 grouped GEMM).
+// 128 block of each group's B, applied in software after every 128-K step),
+// and none with the grouped GEMM's addressing (the BF16 grouped GEMM).
 enum : int { SM_MX = 0, SM_TENSOR = 1, SM_GROUP = 2, SM_GNONE = 3 };
 
 struct DenseArgs {
