@@ -377,20 +377,56 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
       }
       float wsc = 1.0f;
       if constexpr (!BF) wsc = __uint_as_float(lds_load_u32(lsc + BM * 4));
-#pragma unroll
-      for (int a = 0; a < FM; ++a) {
+      auto read_af = [&](int a) -> v8i {
         const v4i x = lds_read16(la + oa0 + a * 2048), y = lds_read16(la + oa1 + a * 2048);
-        const v8i af = (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-        if constexpr (BF) {
+        return (v8i){x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+      };
+      if constexpr (BF) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+          const v8i af = read_af(a);
 #pragma unroll
           for (int b = 0; b < FN; ++b) acc[a][b] = mfma_bf16_x2(bf[b], af, acc[a][b]);
-        } else {
-          const float sc = __uint_as_float(lds_load_u32(lsc + oxs + a * 64)) * wsc;
+        }
+      } else {
+        // As the 256 x 256 kernel: row tile a's partial products go to one
+        // of two register sets while tile a - 1's are scaled and added, one
+        // matrix-core instruction followed by four FMAs, and tile a + 1's A
+        // fragment and scale are read ahead.
+        v4f part[2][FN];
+        float scp[2];
+        v8i af = read_af(0);
+        float scn = __uint_as_float(lds_load_u32(lsc + oxs)) * wsc;
 #pragma unroll
-          for (int b = 0; b < FN; ++b) {
-            const v4f part = mfma_scaled<F_E4M3, F_E4M3>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f},
-                                                          E8M0_ONE_X4, E8M0_ONE_X4);
-            acc[a][b] += part * sc;
+        for (int a = 0; a <= FM; ++a) {
+          v8i af_next;
+          float sc_next = 0.0f;
+          if (a + 1 < FM) {
+            af_next = read_af(a + 1);
+            sc_next = __uint_as_float(lds_load_u32(lsc + oxs + (a + 1) * 64)) * wsc;
+          }
+          if (a < FM) {
+            scp[a & 1] = scn;
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+              part[a & 1][b] = mfma_scaled<F_E4M3, F_E4M3>(bf[b], af, (v4f){0.f, 0.f, 0.f, 0.f},
+                                                            E8M0_ONE_X4, E8M0_ONE_X4);
+          }
+          if (a > 0) {
+#pragma unroll
+            for (int b = 0; b < FN; ++b) acc[a - 1][b] += part[(a - 1) & 1][b] * scp[(a - 1) & 1];
+          }
+          if (a > 0 && a < FM) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (a + 1 < FM) {
+            af = af_next;
+            scn = sc_next;
           }
         }
       }
