@@ -1,8 +1,10 @@
 // C ABI of the gfx950 block-scaled GEMM library: argument validation, tile
 // and grid selection from static shapes, and kernel launch.  The host never
 // reads device memory; every call enqueues one kernel on the caller's
-// stream (the tensor-wise quantizer four, see mxgemm_quantize_tensor) or
-// returns an error before enqueueing anything.
+// stream (the tensor-wise quantizer four, see mxgemm_quantize_tensor; a
+// grouped GEMM on 256 x 256 tiles two when the last round of its tiles
+// goes to the streaming kernel) or returns an error before enqueueing
+// anything.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <algorithm>

@@ -21,7 +21,8 @@
 // for few rows per group) and grouped_dense_kernel (256 x 256 tiles on the
 // dense kernel's pipeline, for many rows per group), whose last, partial
 // round of tiles the streaming kernel can take over in 128 x 64 pieces
-// (grouped_split_end).
+// (grouped_split_end).  Both families also run the BF16 grouped GEMM
+// (FMT = F_BF16: BF16 operands, no scales).
 #pragma once
 #include "../../include/mxgemm.h"
 #include "dense.hpp"
