@@ -277,7 +277,7 @@ def grouped_bench(torch, synth, mxgemm, dev, reps=50):
         res["algo_bytes"] = hbm
         res["gbs_cold"] = hbm / (res["preshuffled_cold_us"] * 1e-6) / 1e9
         out.append(res)
-        res["kernel"] = ["persistent 64x64", "persistent 256x256 (dense pipeline)", "persistent 128x64"][mxgemm.grouped_variant(G, totM, N, K)]
+        res["kernel"] = ["persistent 64x64", "persistent 256x256 (dense pipeline)", "persistent 128x128"][mxgemm.grouped_variant(G, totM, N, K)]
         log("grouped %s: plain %.1f us, preshuffled %.1f us, graph replay median %.1f us (p10 %.1f, p90 %.1f%s), "
             "10-call graph %.1f us/call, cold %.1f us (%.0f GB/s) [%s]" % (
                 (totM, N, K), res["plain_us"], res["preshuffled_us"], res["graph_replay_us"]["median"],

@@ -57,8 +57,8 @@ int launch_status() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The persistent grouped kernels run GS_OCC workgroups per compute unit (74
-// and 59 KiB of LDS with the group table: 64-row tiles with two 128-K steps
-// per ring stage, 128-row tiles with one; two ring slots), so that one
+// KiB of LDS each with the group table: 64 x 64 tiles with two 128-K steps
+// per ring stage, 128 x 128 tiles with one; two ring slots), so that one
 // workgroup's wait-barrier-compute chain overlaps the other's.
 constexpr int GS_OCC = 2;
 
@@ -331,8 +331,9 @@ int launch_grouped(int variant, int G, const int64_t *m_sizes, const void *XQ, c
   a.N = N;
   a.K = K;
   a.G = G;
+  // streaming tiles: 64 x 64 or 128 x 128 (N % 128 == 0)
   const int BM = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
-  const int BN = variant == MXG_GROUPED_TILED ? 128 : 64;
+  const int BN = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
   a.tiles_n = (int)(N / BN);
   const int64_t blocks = (cdiv(totM, BM) + G - 1) * a.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
@@ -398,77 +399,81 @@ namespace {
 // (nextPow2(totM), N, K, b_preshuffled), here for G = 8 (the pages' G).
 // Each entry is the fastest of the three kernels measured on MI355X at
 // totM = 2^log2m with the benchmark's kind of m_sizes (one empty group,
-// uneven cuts); the times after each entry are 64 x 64 streaming,
-// 128 x 64 streaming and 256 x 256 dense-pipeline, in that order.
+// uneven cuts), by the sum of its warm time (the same weights every call)
+// and its cold time (weight copies totalling more than the 256 MB
+// last-level cache rotated between calls: a layer whose weights are not
+// cached); the times after each entry are warm / cold us of the 64 x 64
+// streaming, 128 x 128 streaming and 256 x 256 dense-pipeline kernels, in
+// that order.
 struct GroupedTile {
   int32_t N, K;
   int8_t log2m, pre, variant;
 };
 const GroupedTile GROUPED_TILES[] = {
-    {1280, 8192, 7, 0, 0},   //   27.2   42.6  102.7 us
-    {1280, 8192, 7, 1, 0},   //   26.0   41.5  101.2 us
-    {1280, 8192, 8, 0, 0},   //   27.8   42.9  105.0 us
-    {1280, 8192, 8, 1, 0},   //   26.3   41.6  103.3 us
-    {1280, 8192, 9, 0, 0},   //   33.2   44.2  121.7 us
-    {1280, 8192, 9, 1, 0},   //   31.5   42.9  120.2 us
-    {1280, 8192, 10, 0, 0},   //   34.8   45.7  128.9 us
-    {1280, 8192, 10, 1, 0},   //   33.6   44.7  127.1 us
-    {1280, 8192, 11, 0, 2},   //   57.4   55.4  123.5 us
-    {1280, 8192, 11, 1, 2},   //   54.3   54.1  120.0 us
-    {1280, 8192, 12, 0, 0},   //   99.2  101.6  133.1 us
-    {1280, 8192, 12, 1, 2},   //   96.2   91.0  127.1 us
-    {1280, 8192, 13, 0, 1},   //  205.0  182.8  135.2 us
-    {1280, 8192, 13, 1, 1},   //  191.2  167.8  129.6 us
-    {1280, 8192, 14, 0, 1},   //  401.5  327.3  237.0 us
-    {1280, 8192, 14, 1, 1},   //  381.7  312.2  223.0 us
-    {2048, 7168, 7, 0, 0},   //   25.5   39.0   92.7 us
-    {2048, 7168, 7, 1, 0},   //   25.1   38.3   90.8 us
-    {2048, 7168, 8, 0, 0},   //   26.0   39.3   95.2 us
-    {2048, 7168, 8, 1, 0},   //   25.9   38.0   92.9 us
-    {2048, 7168, 9, 0, 0},   //   31.4   41.1  113.5 us
-    {2048, 7168, 9, 1, 0},   //   30.5   39.9  111.3 us
-    {2048, 7168, 10, 0, 2},   //   50.3   48.0  122.0 us
-    {2048, 7168, 10, 1, 2},   //   48.2   47.0  119.1 us
-    {2048, 7168, 11, 0, 0},   //   76.9   84.7  113.7 us
-    {2048, 7168, 11, 1, 0},   //   72.8   79.7  110.4 us
-    {2048, 7168, 12, 0, 1},   //  131.2  135.3  130.4 us
-    {2048, 7168, 12, 1, 2},   //  123.6  123.0  128.5 us
-    {2048, 7168, 13, 0, 1},   //  284.3  247.7  170.2 us
-    {2048, 7168, 13, 1, 1},   //  256.4  232.5  160.1 us
-    {2048, 7168, 14, 0, 1},   //  555.0  459.7  292.3 us
-    {2048, 7168, 14, 1, 1},   //  513.9  442.7  283.4 us
-    {4096, 4096, 7, 0, 0},   //   22.0   29.0   60.3 us
-    {4096, 4096, 7, 1, 0},   //   22.0   28.8   59.1 us
-    {4096, 4096, 8, 0, 0},   //   22.4   29.2   63.4 us
-    {4096, 4096, 8, 1, 0},   //   22.3   29.2   61.7 us
-    {4096, 4096, 9, 0, 2},   //   37.3   32.0   82.1 us
-    {4096, 4096, 9, 1, 2},   //   36.9   31.7   79.1 us
-    {4096, 4096, 10, 0, 0},   //   48.1   52.3   91.2 us
-    {4096, 4096, 10, 1, 0},   //   45.8   49.3   87.7 us
-    {4096, 4096, 11, 0, 0},   //   79.9   92.1   84.3 us
-    {4096, 4096, 11, 1, 0},   //   75.7   84.7   80.6 us
-    {4096, 4096, 12, 0, 1},   //  157.1  142.7  130.8 us
-    {4096, 4096, 12, 1, 2},   //  142.2  123.2  123.5 us
-    {4096, 4096, 13, 0, 1},   //  331.4  260.9  180.7 us
-    {4096, 4096, 13, 1, 1},   //  291.4  245.4  166.2 us
-    {4096, 4096, 14, 0, 1},   //  641.1  484.7  303.2 us
-    {4096, 4096, 14, 1, 1},   //  568.2  476.6  294.5 us
-    {7168, 2304, 7, 0, 0},   //   25.2   33.2   40.9 us
-    {7168, 2304, 7, 1, 0},   //   24.8   33.0   40.9 us
-    {7168, 2304, 8, 0, 0},   //   25.4   33.3   43.4 us
-    {7168, 2304, 8, 1, 0},   //   25.2   33.4   43.2 us
-    {7168, 2304, 9, 0, 0},   //   35.7   36.0   63.7 us
-    {7168, 2304, 9, 1, 0},   //   35.2   36.2   62.0 us
-    {7168, 2304, 10, 0, 2},   //   49.6   47.8   73.4 us
-    {7168, 2304, 10, 1, 2},   //   47.7   46.7   70.9 us
-    {7168, 2304, 11, 0, 0},   //   89.9   93.1   99.6 us
-    {7168, 2304, 11, 1, 0},   //   85.6   85.9   95.4 us
-    {7168, 2304, 12, 0, 1},   //  171.9  145.9  125.9 us
-    {7168, 2304, 12, 1, 1},   //  158.0  134.8  120.4 us
-    {7168, 2304, 13, 0, 1},   //  348.7  280.8  185.6 us
-    {7168, 2304, 13, 1, 1},   //  297.0  261.1  176.3 us
-    {7168, 2304, 14, 0, 1},   //  679.4  541.2  310.7 us
-    {7168, 2304, 14, 1, 1},   //  607.5  518.1  307.0 us
+    {1280, 8192, 7, 0, 0},   //   26.4 /  34.8    49.4 /  60.3    91.4 /  94.0 us
+    {1280, 8192, 7, 1, 0},   //   25.9 /  33.7    49.9 /  57.4    91.2 /  92.5 us
+    {1280, 8192, 8, 0, 0},   //   27.4 /  37.1    50.3 /  61.5    94.0 /  97.8 us
+    {1280, 8192, 8, 1, 0},   //   26.3 /  34.4    50.1 /  57.5    93.0 /  95.8 us
+    {1280, 8192, 9, 0, 0},   //   32.7 /  36.2    51.5 /  62.4   110.1 / 114.0 us
+    {1280, 8192, 9, 1, 0},   //   31.7 /  34.8    51.0 /  58.2   109.7 / 112.8 us
+    {1280, 8192, 10, 0, 0},   //   34.9 /  43.4    52.9 /  62.6   116.4 / 120.7 us
+    {1280, 8192, 10, 1, 0},   //   34.2 /  40.9    51.8 /  59.0   115.4 / 119.4 us
+    {1280, 8192, 11, 0, 2},   //   56.8 /  71.6    55.4 /  63.4   109.8 / 113.0 us
+    {1280, 8192, 11, 1, 2},   //   53.5 /  65.3    52.8 /  58.9   107.5 / 111.2 us
+    {1280, 8192, 12, 0, 2},   //  101.6 / 109.5    74.0 /  78.5   115.3 / 116.9 us
+    {1280, 8192, 12, 1, 2},   //   93.5 / 100.7    67.9 /  73.3   111.8 / 116.8 us
+    {1280, 8192, 13, 0, 1},   //  202.0 / 214.3   125.5 / 138.8   118.4 / 118.7 us
+    {1280, 8192, 13, 1, 1},   //  189.1 / 203.3   123.2 / 131.3   118.3 / 118.7 us
+    {1280, 8192, 14, 0, 1},   //  387.7 / 378.9   222.8 / 224.1   218.8 / 227.8 us
+    {1280, 8192, 14, 1, 2},   //  381.1 / 370.6   218.7 / 221.2   216.4 / 225.0 us
+    {2048, 7168, 7, 0, 0},   //   25.1 /  33.6    44.8 /  54.8    81.3 /  86.0 us
+    {2048, 7168, 7, 1, 0},   //   24.7 /  31.0    44.4 /  52.3    80.9 /  83.4 us
+    {2048, 7168, 8, 0, 0},   //   25.8 /  34.5    45.5 /  55.5    84.7 /  90.6 us
+    {2048, 7168, 8, 1, 0},   //   25.5 /  31.9    44.8 /  53.0    83.9 /  86.7 us
+    {2048, 7168, 9, 0, 0},   //   31.0 /  38.6    47.7 /  56.8   101.1 / 108.5 us
+    {2048, 7168, 9, 1, 0},   //   30.2 /  36.3    46.1 /  54.0   100.6 / 105.1 us
+    {2048, 7168, 10, 0, 2},   //   49.6 /  65.3    48.6 /  57.7   110.6 / 117.8 us
+    {2048, 7168, 10, 1, 2},   //   47.8 /  61.1    47.1 /  54.3   108.1 / 113.9 us
+    {2048, 7168, 11, 0, 2},   //   75.6 /  93.0    66.0 /  72.7    99.8 / 106.0 us
+    {2048, 7168, 11, 1, 2},   //   69.3 /  83.7    59.0 /  66.8    96.6 / 101.7 us
+    {2048, 7168, 12, 0, 2},   //  138.6 / 148.7   102.0 / 114.8   110.7 / 114.0 us
+    {2048, 7168, 12, 1, 2},   //  115.4 / 135.2    98.2 / 109.1   112.6 / 113.0 us
+    {2048, 7168, 13, 0, 1},   //  270.1 / 282.7   165.5 / 182.2   154.3 / 167.4 us
+    {2048, 7168, 13, 1, 1},   //  254.7 / 270.1   162.1 / 176.3   153.9 / 163.5 us
+    {2048, 7168, 14, 0, 1},   //  523.7 / 527.8   292.6 / 304.3   282.4 / 284.0 us
+    {2048, 7168, 14, 1, 1},   //  514.3 / 514.5   277.9 / 296.8   276.0 / 279.2 us
+    {4096, 4096, 7, 0, 0},   //   21.8 /  31.4    29.9 /  37.5    53.1 /  54.8 us
+    {4096, 4096, 7, 1, 0},   //   21.8 /  25.6    28.4 /  33.4    51.2 /  53.8 us
+    {4096, 4096, 8, 0, 0},   //   22.4 /  31.2    31.1 /  38.2    56.3 /  58.8 us
+    {4096, 4096, 8, 1, 0},   //   22.3 /  26.5    29.7 /  34.1    53.8 /  56.4 us
+    {4096, 4096, 9, 0, 2},   //   37.1 /  45.2    32.0 /  39.8    73.8 /  76.6 us
+    {4096, 4096, 9, 1, 2},   //   34.8 /  41.6    31.3 /  35.1    70.6 /  74.7 us
+    {4096, 4096, 10, 0, 2},   //   46.8 /  61.6    44.3 /  48.8    83.4 /  84.9 us
+    {4096, 4096, 10, 1, 2},   //   44.0 /  56.1    39.6 /  44.7    79.5 /  83.9 us
+    {4096, 4096, 11, 0, 2},   //   80.1 /  96.7    65.0 /  74.6    74.7 /  76.6 us
+    {4096, 4096, 11, 1, 2},   //   73.3 /  89.0    63.9 /  68.6    73.5 /  74.1 us
+    {4096, 4096, 12, 0, 2},   //  157.9 / 162.2    98.2 / 106.9   117.1 / 122.6 us
+    {4096, 4096, 12, 1, 2},   //  134.9 / 149.3    93.7 / 103.5   117.0 / 121.7 us
+    {4096, 4096, 13, 0, 1},   //  306.5 / 315.0   180.4 / 189.8   166.1 / 172.0 us
+    {4096, 4096, 13, 1, 1},   //  286.5 / 301.8   174.1 / 183.1   164.8 / 172.3 us
+    {4096, 4096, 14, 0, 1},   //  589.7 / 599.6   339.2 / 352.9   295.6 / 310.1 us
+    {4096, 4096, 14, 1, 1},   //  568.0 / 587.2   337.6 / 336.1   289.2 / 309.9 us
+    {7168, 2304, 7, 0, 2},   //   24.9 /  30.0    25.4 /  27.9    39.3 /  40.2 us
+    {7168, 2304, 7, 1, 2},   //   25.2 /  29.2    23.9 /  26.9    36.6 /  38.5 us
+    {7168, 2304, 8, 0, 2},   //   24.8 /  29.8    24.7 /  28.4    39.3 /  41.4 us
+    {7168, 2304, 8, 1, 2},   //   24.8 /  29.3    24.2 /  27.4    37.9 /  40.4 us
+    {7168, 2304, 9, 0, 2},   //   34.3 /  40.1    29.6 /  33.6    57.2 /  59.6 us
+    {7168, 2304, 9, 1, 2},   //   33.5 /  39.5    27.8 /  31.4    56.6 /  58.4 us
+    {7168, 2304, 10, 0, 2},   //   48.3 /  59.5    40.8 /  50.3    66.8 /  69.2 us
+    {7168, 2304, 10, 1, 2},   //   45.4 /  56.2    39.3 /  47.3    65.8 /  68.0 us
+    {7168, 2304, 11, 0, 2},   //   90.2 /  99.5    63.0 /  67.6    90.5 /  97.3 us
+    {7168, 2304, 11, 1, 2},   //   84.9 /  92.2    59.3 /  64.8    88.6 /  95.3 us
+    {7168, 2304, 12, 0, 2},   //  171.9 / 170.8   100.5 / 104.3   112.9 / 118.1 us
+    {7168, 2304, 12, 1, 2},   //  156.1 / 164.9    97.3 / 104.7   113.5 / 118.4 us
+    {7168, 2304, 13, 0, 1},   //  320.3 / 323.3   190.2 / 194.8   180.0 / 181.4 us
+    {7168, 2304, 13, 1, 1},   //  298.8 / 317.3   187.4 / 192.4   180.5 / 180.5 us
+    {7168, 2304, 14, 0, 1},   //  631.0 / 619.4   370.1 / 367.8   308.6 / 307.0 us
+    {7168, 2304, 14, 1, 1},   //  612.4 / 616.4   365.2 / 374.4   312.5 / 309.5 us
 };
 
 int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
@@ -484,17 +489,19 @@ int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
 // Kernel choice from the static shapes (the host never reads m_sizes): the
 // static table above when it lists the shape, else the estimated time of
 // each kernel from upper bounds of the tile counts.
-//  - persistent, 64 x 64 or 128 x 64 tiles (weight streaming): ~0.6 or
-//    ~1.0 us per 128-K tile step per workgroup, GS_OCC workgroups per
-//    compute unit walking all tile steps evenly;
+//  - persistent, 64 x 64 or 128 x 128 tiles (weight streaming): ~0.8 or
+//    ~1.7 us per 128-K tile step per workgroup, GS_OCC workgroups per
+//    compute unit walking all tile steps evenly (the 128 x 128 kernel at
+//    least ~1.1 us per K step: a tile's time when its workgroup has the
+//    compute unit to itself);
 //  - persistent 256 x 256 tiles on the dense pipeline (matrix-core regime):
 //    one tile per compute unit per round, ~1.67 us per 128-K step plus
 //    ~20 us per round (pipeline start, epilogue); a partial last round that
 //    goes to the streaming kernel (grouped_split_end) ~1.15 us per 128-K
 //    step plus ~5 us per round of its 128 x 64 pieces;
 // each at least the weights' bytes at ~5 TB/s.  The constants are fitted to
-// the table's measurements; at 49 of its 64 points the estimate picks the
-// table's kernel, and at the other 15 one within 17% of it.
+// the table's warm-plus-cold times; at 57 of its 64 points the estimate
+// picks the table's kernel, and at the other 7 one within 11% of it.
 namespace {
 // Autotuned winners of the grouped GEMM, keyed as "Add FlyDSL grouped
 // groupwise FP8 GEMM for ROCm" (Tile selection) keys its persisted cache:
@@ -545,10 +552,10 @@ int grouped_model_variant(int G, int64_t totM, int64_t N, int64_t kbytes) {
   const double cus = cu_count(), nst = (double)(K / 128);
   const double wbytes = (double)G * (double)N * (double)K;
   const double wmin = wbytes / 5.0e6;
-  const double tiles_n = (double)(N / 64);
   const double slots = (double)GS_OCC * cus;
-  const double t64 = std::max(0.6 * (double)(cdiv(totM, 64) + G - 1) * tiles_n * nst / slots, wmin);
-  const double t128 = std::max(1.0 * (double)(cdiv(totM, 128) + G - 1) * tiles_n * nst / slots, wmin);
+  const double t64 = std::max(0.8 * (double)(cdiv(totM, 64) + G - 1) * (double)(N / 64) * nst / slots, wmin);
+  const double t128 = std::max(std::max(1.7 * (double)(cdiv(totM, 128) + G - 1) * (double)(N / 128) * nst / slots,
+                                        1.1 * nst), wmin);
   const double tiles_d = (double)(cdiv(totM, DBM) + G - 1) * (double)cdiv(N, DBN);
   const double round_d = 1.67 * nst + 20.0;
   const double full = std::floor(tiles_d / cus), r = tiles_d - full * cus;
@@ -779,13 +786,15 @@ extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *
   a.N = N;
   a.K = K;
   a.G = G;
-  a.tiles_n = (int)(N / 64);
   if (variant != MXG_GROUPED_TILED) {
+    // 64 x 64 or 128 x 128 tiles (128 x 64 when N is an odd multiple of 64)
     const int BM = variant == MXG_GROUPED_STREAM64 ? 64 : 128;
+    const int BN = BM == 128 && N % 128 == 0 ? 128 : 64;
+    a.tiles_n = (int)(N / BN);
     const int64_t blocks = (cdiv(totM, BM) + G - 1) * a.tiles_n;
     if (blocks > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
     const unsigned P = (unsigned)std::min<int64_t>(blocks, (int64_t)GS_OCC * cu_count());
-    hipLaunchKernelGGL(pick_grouped_stream_bf16(BM, pre), dim3(P), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(pick_grouped_stream_bf16(BM, BN, pre), dim3(P), dim3(256), 0, stream, a);
     return launch_status();
   }
   // 256 x 256 tiles on the dense pipeline, one persistent workgroup per
@@ -813,6 +822,7 @@ extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *
   d.tail_rounds = tail ? GROUPED_TAIL_ROUNDS : 0;
   hipLaunchKernelGGL(pick_grouped_bf16(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
   if (tail) {
+    a.tiles_n = (int)(N / 64);
     a.tiles_nb = d.tiles_n;
     a.main_grid = (int)grid;
     a.tail_rounds = GROUPED_TAIL_ROUNDS;

@@ -17,7 +17,7 @@
 //   k-block kb) sits at i + kb*M_g.
 // * B is either plain [G, N, K] (staged through XOR-swizzled LDS like A) or
 //   preshuffled per group (copied linearly into LDS).
-// This file holds two kernel families: grouped_stream_kernel (BM x 64 tiles,
+// This file holds two kernel families: grouped_stream_kernel (BM x BN tiles,
 // for few rows per group) and grouped_dense_kernel (256 x 256 tiles on the
 // dense kernel's pipeline, for many rows per group), whose last, partial
 // round of tiles the streaming kernel can take over in 128 x 64 pieces
@@ -58,7 +58,9 @@ __device__ inline int grouped_split_end(int nb, int P, int P_tail, int max_round
 // Grouped kernel for few rows per group (the weight-streaming regime: the
 // weights dominate the bytes and HBM, not the matrix cores, sets the time).
 //
-// * BM x 64 output tiles (BM = 64 or 128).  The real tiles (groups with rows
+// * BM x BN output tiles (64 x 64, or 128 x 128 where a group's rows are
+//   read by many column tiles: each 128-row A block is then streamed half
+//   as often as with 128 x 64 tiles).  The real tiles (groups with rows
 //   only, none spanning two groups) are numbered group by group, N-tile
 //   major and M-tile minor, so that consecutive tiles share one weight tile.
 //   Each workgroup finds a tile's group by binary search in a table of the
@@ -74,19 +76,20 @@ __device__ inline int grouped_split_end(int nb, int P, int P_tail, int max_round
 //   The ring runs across tile boundaries, so a workgroup's stream never
 //   drains between its tiles; the second workgroup on the compute unit
 //   covers this one's wait-barrier-compute chain.
-// * Per K step, four waves (2 x 2, (BM/2) x 32 each) run the scaled
+// * Per K step, four waves (2 x 2, (BM/2) x (BN/2) each) run the scaled
 //   matrix-core instruction with the neutral E8M0 scale into a zeroed
 //   accumulator and add the partial times xs(row, kb) * ws(g, n/128, kb) in
 //   FP32.  A tile's result is stored as BF16 straight from the accumulators.
 // * 8-row blocks of A past the tile's group read nothing (empty range).
-template <int BM_>
+template <int BM_, int BN_>
 struct GroupedStream {
-  static constexpr int BM = BM_, BN = 64;
-  static constexpr int FM = BM / 32, FN = 2;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int FM = BM / 32, FN = BN / 32;
   static constexpr int AB = BM * 128, BB = BN * 128;
   static constexpr int SC = BM * 4 + 256;           // xs (BM floats) + ws (64 copies)
   static constexpr int STEP = AB + BB + SC;         // one 128-K step
   static constexpr int ABLK = BM / 32;              // A DMAs per wave and K step
+  static constexpr int BBLK = BN / 32;              // B DMAs per wave and K step
 };
 
 // Group table of a workgroup, in LDS: rows[g] = first row of group g (groups
@@ -156,7 +159,7 @@ struct StreamTile {
   int g;
 };
 
-template <int BM>
+template <int BM, int BN>
 __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable &gt, int64_t t) {
   const int32_t u = (int32_t)(t / p.tiles_n);        // BM-row tile index over all groups
   const int g = group_of_tile(gt, p.G, u);
@@ -169,7 +172,7 @@ __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable 
   r.start = r0;
   r.mg = uni32(gt.rows[g + 1]) - r0;
   r.row0 = r.start + tm * BM;
-  r.n0 = tn * 64;
+  r.n0 = tn * BN;
   return r;
 }
 
@@ -193,22 +196,22 @@ __device__ inline StreamTile tail_piece(const GroupedArgs &p, const GroupTable &
   return r;
 }
 
-// BM-row tiles, KS 128-K steps per ring stage, NS ring slots.  TAIL: the
-// kernel runs the tail pieces of the 256 x 256 kernel (BM = 128) in place of
-// its own tiles.
+// BM x BN tiles, KS 128-K steps per ring stage, NS ring slots.  TAIL: the
+// kernel runs the tail pieces of the 256 x 256 kernel (128 x 64) in place
+// of its own tiles.
 // FMT = F_BF16: BF16 operands and no scales (a 128-byte K step holds 64
 // values, two 16x16x32 BF16 matrix-core instructions per fragment pair).
-template <bool PSB, int BM, int KS, int NS, bool TAIL = false, int FMT = F_E4M3>
+template <bool PSB, int BM, int BN, int KS, int NS, bool TAIL = false, int FMT = F_E4M3>
 __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
-  static_assert(!TAIL || BM == 128, "tail pieces are 128 x 64");
+  static_assert(!TAIL || (BM == 128 && BN == 64), "tail pieces are 128 x 64");
   constexpr bool BF = (FMT == F_BF16);
-  typedef GroupedStream<BM> S;
-  constexpr int FM = S::FM, FN = S::FN, ABLK = S::ABLK;
+  typedef GroupedStream<BM, BN> S;
+  constexpr int FM = S::FM, FN = S::FN, ABLK = S::ABLK, BBLK = S::BBLK;
   constexpr int STAGE = KS * S::STEP;
-  // DMAs per stage and wave: ABLK for A and two for B per K step, plus one
+  // DMAs per stage and wave: ABLK for A and BBLK for B per K step, plus one
   // per K step for the activation scales (waves 0 and, with 128 rows, 2) or
   // the weight block scale (wave 1).
-  constexpr int OPS_LO = (ABLK + 2) * KS, OPS_HI = (ABLK + 3) * KS;
+  constexpr int OPS_LO = (ABLK + BBLK) * KS, OPS_HI = (ABLK + BBLK + 1) * KS;
   static_assert(OPS_HI * (NS - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   __shared__ GroupTable gt;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   auto tile_of = [&](int64_t i) -> int64_t { return i * P + (i < full ? off_full : off_last); };
   auto tile_at = [&](int64_t i) -> StreamTile {
     if constexpr (TAIL) return tail_piece(p, gt, tile_of(i), end);
-    else return stream_tile<BM>(p, gt, tile_of(i));
+    else return stream_tile<BM, BN>(p, gt, tile_of(i));
   };
   const int64_t K = BF ? 2 * p.K : p.K, N = p.N;  // K: bytes per row
   const int nst = (int)(K / 128);                  // K steps (128 bytes) per tile
@@ -308,12 +311,17 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
         dma_asm_v<16>(ka + (uint32_t)blk * 1024u, r, vo, (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
       });
       const u32x4 rb = live ? src.rb : rzero;
-      static_for<0, 2>([&](auto jc) {
+      static_for<0, BBLK>([&](auto jc) {
         constexpr int jj = decltype(jc)::value;
-        const int blk = 2 * w + jj;
-        if constexpr (PSB)
+        const int blk = BBLK * w + jj;
+        // preshuffled: 1 KiB block blk % 8 of 64-column group blk / 8, whose
+        // K steps lie 64 K bytes after the previous group's
+        if constexpr (PSB && BN == 64)
           dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, (uint32_t)lane * 16u,
                       (uint32_t)(st * 8192 + blk * 1024));
+        else if constexpr (PSB)
+          dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, (uint32_t)lane * 16u,
+                      (uint32_t)((blk >> 3) * 64 * K + st * 8192 + (blk & 7) * 1024));
         else
           dma_asm<16>(kb + (uint32_t)blk * 1024u, rb, vo,
                       (uint32_t)(blk * 8 * K + 128 * (int64_t)st));
@@ -351,9 +359,9 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   const int f = kswz(i16);
   const uint32_t oa0 = (uint32_t)((wm * (BM / 2) + i16) * 128 + ((q ^ f) << 4));
   const uint32_t oa1 = (uint32_t)((wm * (BM / 2) + i16) * 128 + (((q + 4) ^ f) << 4));
-  const uint32_t ob0 = PSB ? (uint32_t)(wn * 2 * 2048 + lane * 16)
-                           : (uint32_t)((wn * 32 + i16) * 128 + ((q ^ f) << 4));
-  const uint32_t ob1 = PSB ? ob0 + 1024u : (uint32_t)((wn * 32 + i16) * 128 + (((q + 4) ^ f) << 4));
+  const uint32_t ob0 = PSB ? (uint32_t)(wn * (BN / 2) * 128 + lane * 16)
+                           : (uint32_t)((wn * (BN / 2) + i16) * 128 + ((q ^ f) << 4));
+  const uint32_t ob1 = PSB ? ob0 + 1024u : (uint32_t)((wn * (BN / 2) + i16) * 128 + (((q + 4) ^ f) << 4));
   const uint32_t oxs = (uint32_t)((wm * (BM / 2) + i16) * 4);
 
   for (int s = 0; s < NS - 1; ++s) issue(s);
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     }
     if (++csg == nsg) {
       // Last K step of tile ci: lane (i16, q) holds rows 16a + i16 and
-      // columns 16b + 4q .. +3 of the wave's 32 x 32 block.
+      // columns 16b + 4q .. +3 of the wave's (BM/2) x (BN/2) block.
       const StreamTile t = tile_at(ci);
       const int64_t row_lim = t.start + t.mg;
 #pragma unroll
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
           const v4f r = acc[a][b];
           const uint32_t lo = pack_bf16x2(r.x, r.y), hi = pack_bf16x2(r.z, r.w);
           if (row < row_lim)
-            *(v2i *)(p.D + row * N + t.n0 + wn * 32 + b * 16 + 4 * q) = (v2i){(int)lo, (int)hi};
+            *(v2i *)(p.D + row * N + t.n0 + wn * (BN / 2) + b * 16 + 4 * q) = (v2i){(int)lo, (int)hi};
           acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
         }
       }

@@ -52,7 +52,7 @@ grouped_fn pick_grouped_stream(int bm, bool psb);
 grouped_fn pick_grouped_tail(bool psb);
 // The BF16 grouped GEMM on the same three kernels.
 dense_fn pick_grouped_bf16(bool psb);
-grouped_fn pick_grouped_stream_bf16(int bm, bool psb);
+grouped_fn pick_grouped_stream_bf16(int bm, int bn, bool psb);
 grouped_fn pick_grouped_tail_bf16(bool psb);
 
 }  // namespace mxg

@@ -238,7 +238,7 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
  * grouped_fp8_gemm_variant: which kernel grouped_fp8_gemm_run launches for
  * these static shapes (and b_preshuffled) on the current device (the
  * choice never depends on m_sizes' contents): MXG_GROUPED_STREAM64 or
- * MXG_GROUPED_STREAM128, the persistent kernel with 64 x 64 or 128 x 64
+ * MXG_GROUPED_STREAM128, the persistent kernel with 64 x 64 or 128 x 128
  * tiles for the weight-streaming regime (few rows per group), or
  * MXG_GROUPED_TILED, the persistent 256 x 256 kernel on the dense pipeline
  * for the matrix-core regime (one tile per compute unit per round; when a

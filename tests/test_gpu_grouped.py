@@ -45,6 +45,17 @@ def _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled):
     return D
 
 
+def _run_forced(tmp_path, variant, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled):
+    """_run with grouped_run made to launch `variant` (tune-cache entries for
+    this key), whichever kernel the table or the estimate would pick."""
+    from block_scaled_precision_03_amd import mxgemm
+    _force_variant(mxgemm, tmp_path / "forced.txt", len(m_sizes), totM, N, K, variant)
+    try:
+        return _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    finally:
+        mxgemm.tune_cache_clear()
+
+
 SPLITS = [
     [37, 0, 150, 3, 64, 1, 99, 30],    # uneven, one empty, not tile aligned
     [0, 0, 300, 0],                    # all rows in one group
@@ -149,7 +160,7 @@ def _edge_samples(rng, m_sizes, N, count):
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_tiled_kernel(preshuffled):
+def test_grouped_tiled_kernel(preshuffled, tmp_path):
     """Shapes for which the matrix-core kernel (256 x 256 tiles on the dense
     pipeline) runs: uneven groups, one empty, none tile aligned, 38 K steps.
     Every row written; sampled entries and every group's edge rows."""
@@ -157,8 +168,7 @@ def test_grouped_tiled_kernel(preshuffled):
     N, K = 2048, 4864
     split = [1500, 0, 1077, 2100, 1, 700, 2500, 314]
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(921, split, N, K)
-    assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_TILED
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_TILED, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
     im, inn = _edge_samples(np.random.default_rng(7), m_sizes, N, 20000)
     ref = oracle.grouped_entries(m_sizes, XQ, xs, WQ, ws, totM, N, K, im, inn)
@@ -167,26 +177,27 @@ def test_grouped_tiled_kernel(preshuffled):
 
 def test_grouped_small_shapes_take_the_streaming_kernels():
     """The parity cases above with few rows run the persistent 64 x 64
-    kernel (the 128 x 64 one has its own test below), and so do the
-    benchmark's 128-row shapes."""
+    kernel (the 128 x 128 one has its own test below), and so does the
+    benchmark's 128 x 2048 x 7168 call (at 128 x 7168 x 2304 the table lists
+    the 128 x 128 kernel, faster there warm and cold)."""
     from block_scaled_precision_03_amd import mxgemm
     got = {mxgemm.grouped_variant(len(split), int(sum(split)), 256, 640) for split in SPLITS}
     assert got == {mxgemm.GROUPED_STREAM64}
     assert mxgemm.grouped_variant(8, 128, 2048, 7168) == mxgemm.GROUPED_STREAM64
-    assert mxgemm.grouped_variant(8, 128, 7168, 2304) == mxgemm.GROUPED_STREAM64
+    assert mxgemm.grouped_variant(8, 128, 2048, 7168, False) == mxgemm.GROUPED_STREAM64
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_stream128_kernel(preshuffled):
-    """Shapes for which the persistent kernel runs with 128 x 64 tiles: uneven
-    groups (one empty, none tile aligned), sampled entries and every group's
-    first and last rows against the oracle, every row written."""
+def test_grouped_stream128_kernel(preshuffled, tmp_path):
+    """The persistent kernel with 128 x 128 tiles: uneven groups (one empty,
+    none tile aligned) and five tile columns (the preshuffled weights' 64-
+    column groups in pairs), sampled entries and every group's first and
+    last rows against the oracle, every row written."""
     from block_scaled_precision_03_amd import mxgemm
-    N, K = 512, 2048
+    N, K = 640, 2048
     split = [700, 0, 1, 1157, 129, 1013]
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(941, split, N, K)
-    assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_STREAM128
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_STREAM128, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     d = H.bf16_to_f64(D.view(torch.bfloat16))
     assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
     rng = np.random.default_rng(5)
@@ -200,7 +211,7 @@ def test_grouped_stream128_kernel(preshuffled):
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_many_groups_several_rounds(preshuffled):
+def test_grouped_many_groups_several_rounds(preshuffled, tmp_path):
     """200 small groups (some empty): the persistent 64 x 64 kernel walks more
     real tiles than it has workgroups (on 256 compute units three whole
     rounds of 512 and a last round of 314 tiles, which do not split evenly
@@ -212,19 +223,18 @@ def test_grouped_many_groups_several_rounds(preshuffled):
     split = rng.integers(0, 41, G)
     split[::17] = 0
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(960, split, N, K)
-    assert mxgemm.grouped_variant(G, totM, N, K) == mxgemm.GROUPED_STREAM64
     real_tiles = int(sum((m + 63) // 64 for m in split)) * (N // 64)
     P = min(((totM + 63) // 64 + G - 1) * (N // 64),
             2 * torch.cuda.get_device_properties(0).multi_processor_count)
     assert real_tiles // P >= 2 and (real_tiles % P) % 8 != 0
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_STREAM64, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
     ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
     H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped, 200 groups")
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_tiled_half_last_column_tile(preshuffled):
+def test_grouped_tiled_half_last_column_tile(preshuffled, tmp_path):
     """The matrix-core kernel's 256-column tiles with N = 1152 (the last tile
     of each group holds 128 real columns; its weight rows and block scales
     past N belong to the next group, or lie past the end for the last one),
@@ -235,8 +245,7 @@ def test_grouped_tiled_half_last_column_tile(preshuffled):
     N, K = 1152, 2048
     split = [1900, 0, 1077, 2100, 1, 700, 2500, 2622]
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(931, split, N, K, totM=11000)
-    assert mxgemm.grouped_variant(len(split), totM, N, K) == mxgemm.GROUPED_TILED
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_TILED, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     cover = int(sum(split))
     bits = H.bits(D.view(torch.bfloat16))
     assert np.all(bits[cover:] == SENTINEL_BITS)
@@ -251,7 +260,7 @@ def test_grouped_tiled_half_last_column_tile(preshuffled):
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_1024_groups_streaming(preshuffled):
+def test_grouped_1024_groups_streaming(preshuffled, tmp_path):
     """MXG_GROUPED_MAX_G = 1024 groups of 0..8 rows: the persistent 64 x 64
     kernel's group table spans sixteen 64-group chunks.  Every entry against
     the oracle, every row written."""
@@ -259,15 +268,14 @@ def test_grouped_1024_groups_streaming(preshuffled):
     G, N, K = 1024, 256, 256
     split = np.random.default_rng(1024).integers(0, 9, G)
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(970, split, N, K)
-    assert mxgemm.grouped_variant(G, totM, N, K) == mxgemm.GROUPED_STREAM64
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_STREAM64, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
     ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
     H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped, 1024 groups")
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_1024_groups_tiled(preshuffled):
+def test_grouped_1024_groups_tiled(preshuffled, tmp_path):
     """MXG_GROUPED_MAX_G = 1024 groups of 0..512 rows (every seventh empty)
     on the matrix-core kernel: its group table and binary search over all of
     them, eight rounds of persistent tiles.  Integer-valued codes with
@@ -280,13 +288,12 @@ def test_grouped_1024_groups_tiled(preshuffled):
     split[::7] = 0
     m_sizes = split.astype(np.int64)
     totM = int(m_sizes.sum())
-    assert mxgemm.grouped_variant(G, totM, N, K) == mxgemm.GROUPED_TILED
     vals = np.array([0xC0, 0xB8, 0x00, 0x38, 0x40], np.uint8)
     XQ = vals[rng.integers(0, 5, (totM, K), dtype=np.uint8)]
     WQ = vals[rng.integers(0, 5, (G, N, K), dtype=np.uint8)]
     xs = (2.0 ** rng.integers(0, 3, totM * K // 128)).astype(np.float32)
     ws = (2.0 ** rng.integers(0, 3, (G, N // 128, K // 128))).astype(np.float32)
-    D = _run(m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_TILED, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     bits = H.bits(D.view(torch.bfloat16))
     assert not np.any(bits == SENTINEL_BITS)
     im, inn = _edge_samples(np.random.default_rng(6), m_sizes, N, 20000)
@@ -354,7 +361,7 @@ def test_grouped_tiled_tail_pieces(preshuffled, tmp_path):
     real, and the groups give 60 row tiles: 300 tiles, of which (on 256
     compute units) 256 run in one full round and 44 as 352 pieces, among
     them column quarters past N and the empty half of the last group's
-    82-row last tile.  The result must equal bit for bit those of the 128 x 64
+    82-row last tile.  The result must equal bit for bit those of the 128 x 128
     and 64 x 64 streaming kernels over the whole problem (the same
     per-element arithmetic), every row must be written, and sampled entries,
     the groups' edge rows and every entry of the last group's last 300 rows
@@ -426,7 +433,7 @@ def test_grouped_tiled_random_shapes_match_streaming(tmp_path):
     multiple of 128, K from 256 to 1024, rows past the last group, sized so
     that the 256 x 256 kernel has more tiles than compute units: with its
     partial last round split off to the streaming kernel or not (the tile
-    count decides; both occur here), its output equals the 128 x 64
+    count decides; both occur here), its output equals the 128 x 128
     streaming kernel's over the whole problem bit for bit, and rows outside
     every group keep the sentinel."""
     from block_scaled_precision_03_amd import mxgemm

@@ -84,11 +84,14 @@ def _integer_inputs(rng, m_sizes, N, K):
     return X, W, totM
 
 
-# (m_sizes, N, K, kernel): one configuration per kernel the call can run
+# (m_sizes, N, K, kernel): one configuration per kernel the call can run;
+# the 128-row streaming kernel runs 128 x 128 tiles (N = 1152: nine tile
+# columns) and, where N is an odd multiple of 64 (1216), 128 x 64 tiles
 EXACT_CASES = [
     ([30, 0, 47, 1, 60], 576, 1024, "stream64"),
-    ([300, 0, 517, 1, 700], 576, 1024, "stream128"),
-    ([1500, 0, 1077, 2100, 1, 700, 2500, 314], 2048, 1024, "tiled"),
+    ([1200, 0, 1017, 1, 900, 1400], 1152, 256, "stream128"),
+    ([1200, 0, 1017, 1, 900, 1400], 1216, 128, "stream128"),
+    ([1500, 0, 1077, 2100, 1, 700, 2500, 314], 2048, 4096, "tiled"),
 ]
 
 
@@ -100,7 +103,7 @@ def test_bf16_grouped_integer_valued_bit_exact(m_sizes, N, K, kernel, preshuffle
     on each of the three kernels (the 256 x 256 one here with 288 tiles: a
     full round and a last round of 32 tiles handed to the streaming kernel
     on 256 compute units), ragged groups over several tiles.  The streaming
-    shapes compare every entry, the 256 x 256 one every entry of 600 rows
+    shapes compare every entry, the 256 x 256 one every entry of 300 rows
     (every group's first and last among them)."""
     from block_scaled_precision_03_amd import mxgemm
     m_sizes = np.array(m_sizes, np.int64)
@@ -116,7 +119,7 @@ def test_bf16_grouped_integer_valued_bit_exact(m_sizes, N, K, kernel, preshuffle
         return
     starts = np.concatenate([[0], np.cumsum(m_sizes)])
     edge = [r for g in range(len(m_sizes)) if m_sizes[g] for r in (starts[g], starts[g + 1] - 1)]
-    rows = np.unique(np.concatenate([edge, np.random.default_rng(5).integers(0, totM, 600 - len(edge))]))
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(5).integers(0, totM, 300 - len(edge))]))
     im, inn = np.repeat(rows, N), np.tile(np.arange(N), len(rows))
     ref = oracle.grouped_entries_bf16(m_sizes, X, W, totM, N, K, im, inn)
     assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
