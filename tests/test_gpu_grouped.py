@@ -260,15 +260,17 @@ def test_grouped_tiled_half_last_column_tile(preshuffled, tmp_path):
 
 
 @pytest.mark.parametrize("preshuffled", [False, True])
-def test_grouped_1024_groups_streaming(preshuffled, tmp_path):
-    """MXG_GROUPED_MAX_G = 1024 groups of 0..8 rows: the persistent 64 x 64
-    kernel's group table spans sixteen 64-group chunks.  Every entry against
-    the oracle, every row written."""
+@pytest.mark.parametrize("variant", ["stream64", "stream128"])
+def test_grouped_1024_groups_streaming(preshuffled, variant, tmp_path):
+    """MXG_GROUPED_MAX_G = 1024 groups of 0..8 rows on each streaming kernel
+    (64 x 64 and 128 x 128 tiles): the group table spans sixteen 64-group
+    chunks.  Every entry against the oracle, every row written."""
     from block_scaled_precision_03_amd import mxgemm
     G, N, K = 1024, 256, 256
     split = np.random.default_rng(1024).integers(0, 9, G)
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(970, split, N, K)
-    D = _run_forced(tmp_path, mxgemm.GROUPED_STREAM64, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    v = mxgemm.GROUPED_STREAM64 if variant == "stream64" else mxgemm.GROUPED_STREAM128
+    D = _run_forced(tmp_path, v, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
     assert not np.any(H.bits(D.view(torch.bfloat16)) == SENTINEL_BITS)
     ref = oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K)
     H.assert_close(H.bf16_to_f64(D.view(torch.bfloat16)), ref, "grouped, 1024 groups")
