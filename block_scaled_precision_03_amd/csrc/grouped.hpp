@@ -20,8 +20,8 @@
 // This file holds two kernel families: grouped_stream_kernel (BM x BN tiles,
 // for few rows per group) and grouped_dense_kernel (256 x 256 tiles on the
 // dense kernel's pipeline, for many rows per group), whose last, partial
-// round of tiles the streaming kernel can take over in 128 x 64 pieces
-// (grouped_split_end).  Both families also run the BF16 grouped GEMM
+// round of tiles the streaming kernel can take over in 128 x 64 or 64 x 64
+// pieces (grouped_split_end).  Both families also run the BF16 grouped GEMM
 // (FMT = F_BF16: BF16 operands, no scales).
 #pragma once
 #include "../../include/mxgemm.h"
@@ -44,15 +44,20 @@ struct GroupedArgs {
 // The split of the 256 x 256 grouped kernel's nb tiles (persistent grid of
 // P workgroups, one per compute unit) into [0, end), which it runs in full
 // rounds, and [end, nb), which the streaming kernel (P_tail workgroups)
-// runs after it, each tile cut into 8 pieces of 128 x 64.  A last round of
+// runs after it, each tile cut into 8 pieces of 128 x 64, or into 16 of
+// 64 x 64 when those 16 r fill at most one round of the streaming kernel
+// (then twice as many of its workgroups share the work).  A last round of
 // r = nb mod P tiles would leave P - r compute units idle for a whole tile;
-// its 8r pieces take ceil(8r / P_tail) rounds of the streaming kernel, each
+// its pieces take ceil(pieces / P_tail) rounds of the streaming kernel, each
 // much shorter than a 256 x 256 tile, so the split is made when that count
 // is at most max_rounds.  Both kernels evaluate this from the same nb.
+__device__ inline int grouped_tail_pieces(int r, int P_tail) { return 16 * r <= P_tail ? 16 : 8; }
+
 __device__ inline int grouped_split_end(int nb, int P, int P_tail, int max_rounds) {
   const int r = nb % P;
   if (max_rounds <= 0 || nb <= P || r == 0) return nb;
-  return (8 * r + P_tail - 1) / P_tail <= max_rounds ? nb - r : nb;
+  const int pieces = grouped_tail_pieces(r, P_tail) * r;
+  return (pieces + P_tail - 1) / P_tail <= max_rounds ? nb - r : nb;
 }
 
 // Grouped kernel for few rows per group (the weight-streaming regime: the
@@ -153,9 +158,10 @@ __device__ inline int group_of_tile(const GroupTable &gt, int G, int32_t u) {
 }
 
 // Real tile t (t < mtile[G] * tiles_n): tiles are numbered group by group,
-// N-tile major, M-tile minor within a group.
+// N-tile major, M-tile minor within a group.  Group g's rows are
+// [start, start + mg); the tile's are [row0, min(row0 + BM, lim)).
 struct StreamTile {
-  int64_t start, mg, row0, n0;
+  int64_t start, mg, row0, n0, lim;
   int g;
 };
 
@@ -173,16 +179,20 @@ __device__ inline StreamTile stream_tile(const GroupedArgs &p, const GroupTable 
   r.mg = uni32(gt.rows[g + 1]) - r0;
   r.row0 = r.start + tm * BM;
   r.n0 = tn * BN;
+  r.lim = r.start + r.mg;
   return r;
 }
 
 // Piece t of the tail of the 256 x 256 kernel (tiles [end, nb) of its tile
-// order): tile end + t / 8, row half (t % 8) % 2, column quarter (t % 8) / 2.
-// A half past its group's rows or a quarter past N (the last tile column
-// when N is an odd multiple of 128) is empty: it reads zeros and stores
-// nothing.
-__device__ inline StreamTile tail_piece(const GroupedArgs &p, const GroupTable &gt, int64_t t, int end) {
-  const int v = end + (int)(t >> 3), s = (int)(t & 7);
+// order), `pieces` (8 or 16) per tile: tile end + t / pieces, and with h =
+// pieces / 4 row parts of 256 / h rows, row part (t % pieces) % h and
+// column quarter (t % pieces) / h.  A part past its group's rows or a
+// quarter past N (the last tile column when N is an odd multiple of 128) is
+// empty: it reads zeros and stores nothing.
+__device__ inline StreamTile tail_piece(const GroupedArgs &p, const GroupTable &gt, int64_t t, int end,
+                                        int pieces) {
+  const int v = end + (int)(t / pieces), s = (int)(t % pieces);
+  const int h = pieces >> 2, rows = DBM / h;
   int tm, tn;
   tile_in_order(v, uni32(gt.mtile[p.G]), p.tiles_nb, tm, tn);
   const int g = group_of_tile(gt, p.G, tm);
@@ -190,15 +200,17 @@ __device__ inline StreamTile tail_piece(const GroupedArgs &p, const GroupTable &
   r.g = g;
   r.start = uni32(gt.rows[g]);
   r.mg = uni32(gt.rows[g + 1]) - r.start;
-  r.row0 = r.start + (int64_t)(tm - uni32(gt.mtile[g])) * DBM + 128 * (s & 1);
-  r.n0 = (int64_t)tn * DBN + 64 * (s >> 1);
+  r.row0 = r.start + (int64_t)(tm - uni32(gt.mtile[g])) * DBM + (int64_t)rows * (s % h);
+  r.n0 = (int64_t)tn * DBN + 64 * (s / h);
   if (r.row0 > r.start + r.mg || r.n0 >= p.N) r.row0 = r.start + r.mg;
+  r.lim = min(r.start + r.mg, r.row0 + rows);
   return r;
 }
 
 // BM x BN tiles, KS 128-K steps per ring stage, NS ring slots.  TAIL: the
-// kernel runs the tail pieces of the 256 x 256 kernel (128 x 64) in place
-// of its own tiles.
+// kernel (128 x 64) runs the tail pieces of the 256 x 256 kernel in place
+// of its own tiles (a 64 x 64 piece leaves the tile's lower 64 rows
+// empty).
 // FMT = F_BF16: BF16 operands and no scales (a 128-byte K step holds 64
 // values, two 16x16x32 BF16 matrix-core instructions per fragment pair).
 template <bool PSB, int BM, int BN, int KS, int NS, bool TAIL = false, int FMT = F_E4M3>
@@ -225,11 +237,13 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   __syncthreads();
   const int P = (int)gridDim.x;
   int end = 0;                                      // TAIL: first tile of the tail
+  int pieces = 8;                                   // TAIL: pieces per tile
   int64_t T;                                        // real tiles (TAIL: pieces)
   if constexpr (TAIL) {
     const int nb = uni32(gt.mtile[p.G]) * p.tiles_nb;
     end = grouped_split_end(nb, p.main_grid, P, p.tail_rounds);
-    T = (int64_t)(nb - end) * 8;
+    pieces = grouped_tail_pieces(nb - end, P);
+    T = (int64_t)(nb - end) * pieces;
   } else {
     T = (int64_t)uni32(gt.mtile[p.G]) * p.tiles_n;
   }
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
   const int64_t off_full = band_start(P) + r, off_last = band_start(last) + r;
   auto tile_of = [&](int64_t i) -> int64_t { return i * P + (i < full ? off_full : off_last); };
   auto tile_at = [&](int64_t i) -> StreamTile {
-    if constexpr (TAIL) return tail_piece(p, gt, tile_of(i), end);
+    if constexpr (TAIL) return tail_piece(p, gt, tile_of(i), end, pieces);
     else return stream_tile<BM, BN>(p, gt, tile_of(i));
   };
   const int64_t K = BF ? 2 * p.K : p.K, N = p.N;  // K: bytes per row
@@ -282,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
     s.xs0 = (uint32_t)((t.start * kb_n + (t.row0 - t.start)) * 4);
     s.ws0 = (uint32_t)((((int64_t)t.g * (N / 128) + t.n0 / 128) * kb_n) * 4);
     s.mg4 = (uint32_t)(t.mg * 4);
-    const int64_t left = t.start + t.mg - t.row0;
+    const int64_t left = t.lim - t.row0;
     s.vrows = (int)(left < BM ? left : BM);
     return s;
   };
@@ -444,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedArgs p) {
       // Last K step of tile ci: lane (i16, q) holds rows 16a + i16 and
       // columns 16b + 4q .. +3 of the wave's (BM/2) x (BN/2) block.
       const StreamTile t = tile_at(ci);
-      const int64_t row_lim = t.start + t.mg;
+      const int64_t row_lim = t.lim;
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         const int64_t row = t.row0 + wm * (BM / 2) + a * 16 + i16;
