@@ -63,8 +63,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int GS_OCC = 2;
 
 // The 256 x 256 grouped kernel leaves a partial last round of tiles to the
-// streaming kernel when those tiles' 128 x 64 pieces take at most this many
-// rounds of it (grouped_split_end).
+// streaming kernel when those tiles' pieces (128 x 64, or 64 x 64 when they
+// fit one round) take at most this many rounds of it (grouped_split_end).
 constexpr int GROUPED_TAIL_ROUNDS = 2;
 
 // Compute units of the current device: the grid size of the persistent dense
@@ -799,7 +799,7 @@ extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *
   }
   // 256 x 256 tiles on the dense pipeline, one persistent workgroup per
   // compute unit, every group's rows cut into 256-row tiles; a partial last
-  // round goes to the 128 x 64 streaming kernel (grouped_split_end)
+  // round goes to the streaming kernel in pieces (grouped_split_end)
   DenseArgs d = {};
   d.A = (const uint8_t *)X;
   d.B = (const uint8_t *)W;

@@ -243,7 +243,7 @@ int grouped_fp8_gemm_validate(int G, const int64_t *m_sizes,
  * MXG_GROUPED_TILED, the persistent 256 x 256 kernel on the dense pipeline
  * for the matrix-core regime (one tile per compute unit per round; when a
  * last, partial round would leave most compute units idle, its tiles go to
- * the 128 x 64 streaming kernel, launched after it, as 128 x 64 pieces).  A
+ * the streaming kernel, launched after it, as 128 x 64 or 64 x 64 pieces).  A
  * static table keyed on (nextPow2(totM), N, K, b_preshuffled) decides for
  * the shapes it lists ("Add FlyDSL grouped groupwise FP8 GEMM for ROCm",
  * Tile selection: the same key), an estimate of each kernel's time
