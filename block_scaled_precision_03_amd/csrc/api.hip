@@ -65,6 +65,9 @@ constexpr int GS_OCC = 2;
 // The 256 x 256 grouped kernel leaves a partial last round of tiles to the
 // streaming kernel when those tiles' pieces (128 x 64, or 64 x 64 when they
 // fit one round) take at most this many rounds of it (grouped_split_end).
+// That kernel runs with two 128-K steps per ring stage (99 KiB of LDS), one
+// workgroup per compute unit: half the waits and barriers per K step of the
+// one-step ring, whose two workgroups per unit took no less time per piece.
 constexpr int GROUPED_TAIL_ROUNDS = 2;
 
 // Compute units of the current device: the grid size of the persistent dense
@@ -367,7 +370,7 @@ int launch_grouped(int variant, int G, const int64_t *m_sizes, const void *XQ, c
     const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
     // With at most `grid` tiles there is one round and no tail to split off.
     const bool tail = tiles > (int64_t)grid;
-    const unsigned tail_grid = (unsigned)(GS_OCC * cu_count());
+    const unsigned tail_grid = (unsigned)cu_count();
     d.tail_grid = (int)tail_grid;
     d.tail_rounds = tail ? GROUPED_TAIL_ROUNDS : 0;
     hipLaunchKernelGGL(pick_grouped_dense(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);
@@ -410,70 +413,70 @@ struct GroupedTile {
   int8_t log2m, pre, variant;
 };
 const GroupedTile GROUPED_TILES[] = {
-    {1280, 8192, 7, 0, 0},   //   26.4 /  34.8    49.4 /  60.3    91.4 /  94.0 us
-    {1280, 8192, 7, 1, 0},   //   25.9 /  33.7    49.9 /  57.4    91.2 /  92.5 us
-    {1280, 8192, 8, 0, 0},   //   27.4 /  37.1    50.3 /  61.5    94.0 /  97.8 us
-    {1280, 8192, 8, 1, 0},   //   26.3 /  34.4    50.1 /  57.5    93.0 /  95.8 us
-    {1280, 8192, 9, 0, 0},   //   32.7 /  36.2    51.5 /  62.4   110.1 / 114.0 us
-    {1280, 8192, 9, 1, 0},   //   31.7 /  34.8    51.0 /  58.2   109.7 / 112.8 us
-    {1280, 8192, 10, 0, 0},   //   34.9 /  43.4    52.9 /  62.6   116.4 / 120.7 us
-    {1280, 8192, 10, 1, 0},   //   34.2 /  40.9    51.8 /  59.0   115.4 / 119.4 us
-    {1280, 8192, 11, 0, 2},   //   56.8 /  71.6    55.4 /  63.4   109.8 / 113.0 us
-    {1280, 8192, 11, 1, 2},   //   53.5 /  65.3    52.8 /  58.9   107.5 / 111.2 us
-    {1280, 8192, 12, 0, 2},   //  101.6 / 109.5    74.0 /  78.5   115.3 / 116.9 us
-    {1280, 8192, 12, 1, 2},   //   93.5 / 100.7    67.9 /  73.3   111.8 / 116.8 us
-    {1280, 8192, 13, 0, 1},   //  202.0 / 214.3   125.5 / 138.8   118.4 / 118.7 us
-    {1280, 8192, 13, 1, 1},   //  189.1 / 203.3   123.2 / 131.3   118.3 / 118.7 us
-    {1280, 8192, 14, 0, 1},   //  387.7 / 378.9   222.8 / 224.1   218.8 / 227.8 us
-    {1280, 8192, 14, 1, 2},   //  381.1 / 370.6   218.7 / 221.2   216.4 / 225.0 us
-    {2048, 7168, 7, 0, 0},   //   25.1 /  33.6    44.8 /  54.8    81.3 /  86.0 us
-    {2048, 7168, 7, 1, 0},   //   24.7 /  31.0    44.4 /  52.3    80.9 /  83.4 us
-    {2048, 7168, 8, 0, 0},   //   25.8 /  34.5    45.5 /  55.5    84.7 /  90.6 us
-    {2048, 7168, 8, 1, 0},   //   25.5 /  31.9    44.8 /  53.0    83.9 /  86.7 us
-    {2048, 7168, 9, 0, 0},   //   31.0 /  38.6    47.7 /  56.8   101.1 / 108.5 us
-    {2048, 7168, 9, 1, 0},   //   30.2 /  36.3    46.1 /  54.0   100.6 / 105.1 us
-    {2048, 7168, 10, 0, 2},   //   49.6 /  65.3    48.6 /  57.7   110.6 / 117.8 us
-    {2048, 7168, 10, 1, 2},   //   47.8 /  61.1    47.1 /  54.3   108.1 / 113.9 us
-    {2048, 7168, 11, 0, 2},   //   75.6 /  93.0    66.0 /  72.7    99.8 / 106.0 us
-    {2048, 7168, 11, 1, 2},   //   69.3 /  83.7    59.0 /  66.8    96.6 / 101.7 us
-    {2048, 7168, 12, 0, 2},   //  138.6 / 148.7   102.0 / 114.8   110.7 / 114.0 us
-    {2048, 7168, 12, 1, 2},   //  115.4 / 135.2    98.2 / 109.1   112.6 / 113.0 us
-    {2048, 7168, 13, 0, 1},   //  270.1 / 282.7   165.5 / 182.2   154.3 / 167.4 us
-    {2048, 7168, 13, 1, 1},   //  254.7 / 270.1   162.1 / 176.3   153.9 / 163.5 us
-    {2048, 7168, 14, 0, 1},   //  523.7 / 527.8   292.6 / 304.3   282.4 / 284.0 us
-    {2048, 7168, 14, 1, 1},   //  514.3 / 514.5   277.9 / 296.8   276.0 / 279.2 us
-    {4096, 4096, 7, 0, 0},   //   21.8 /  31.4    29.9 /  37.5    53.1 /  54.8 us
-    {4096, 4096, 7, 1, 0},   //   21.8 /  25.6    28.4 /  33.4    51.2 /  53.8 us
-    {4096, 4096, 8, 0, 0},   //   22.4 /  31.2    31.1 /  38.2    56.3 /  58.8 us
-    {4096, 4096, 8, 1, 0},   //   22.3 /  26.5    29.7 /  34.1    53.8 /  56.4 us
-    {4096, 4096, 9, 0, 2},   //   37.1 /  45.2    32.0 /  39.8    73.8 /  76.6 us
-    {4096, 4096, 9, 1, 2},   //   34.8 /  41.6    31.3 /  35.1    70.6 /  74.7 us
-    {4096, 4096, 10, 0, 2},   //   46.8 /  61.6    44.3 /  48.8    83.4 /  84.9 us
-    {4096, 4096, 10, 1, 2},   //   44.0 /  56.1    39.6 /  44.7    79.5 /  83.9 us
-    {4096, 4096, 11, 0, 2},   //   80.1 /  96.7    65.0 /  74.6    74.7 /  76.6 us
-    {4096, 4096, 11, 1, 2},   //   73.3 /  89.0    63.9 /  68.6    73.5 /  74.1 us
-    {4096, 4096, 12, 0, 2},   //  157.9 / 162.2    98.2 / 106.9   117.1 / 122.6 us
-    {4096, 4096, 12, 1, 2},   //  134.9 / 149.3    93.7 / 103.5   117.0 / 121.7 us
-    {4096, 4096, 13, 0, 1},   //  306.5 / 315.0   180.4 / 189.8   166.1 / 172.0 us
-    {4096, 4096, 13, 1, 1},   //  286.5 / 301.8   174.1 / 183.1   164.8 / 172.3 us
-    {4096, 4096, 14, 0, 1},   //  589.7 / 599.6   339.2 / 352.9   295.6 / 310.1 us
-    {4096, 4096, 14, 1, 1},   //  568.0 / 587.2   337.6 / 336.1   289.2 / 309.9 us
-    {7168, 2304, 7, 0, 2},   //   24.9 /  30.0    25.4 /  27.9    39.3 /  40.2 us
-    {7168, 2304, 7, 1, 2},   //   25.2 /  29.2    23.9 /  26.9    36.6 /  38.5 us
-    {7168, 2304, 8, 0, 2},   //   24.8 /  29.8    24.7 /  28.4    39.3 /  41.4 us
-    {7168, 2304, 8, 1, 2},   //   24.8 /  29.3    24.2 /  27.4    37.9 /  40.4 us
-    {7168, 2304, 9, 0, 2},   //   34.3 /  40.1    29.6 /  33.6    57.2 /  59.6 us
-    {7168, 2304, 9, 1, 2},   //   33.5 /  39.5    27.8 /  31.4    56.6 /  58.4 us
-    {7168, 2304, 10, 0, 2},   //   48.3 /  59.5    40.8 /  50.3    66.8 /  69.2 us
-    {7168, 2304, 10, 1, 2},   //   45.4 /  56.2    39.3 /  47.3    65.8 /  68.0 us
-    {7168, 2304, 11, 0, 2},   //   90.2 /  99.5    63.0 /  67.6    90.5 /  97.3 us
-    {7168, 2304, 11, 1, 2},   //   84.9 /  92.2    59.3 /  64.8    88.6 /  95.3 us
-    {7168, 2304, 12, 0, 2},   //  171.9 / 170.8   100.5 / 104.3   112.9 / 118.1 us
-    {7168, 2304, 12, 1, 2},   //  156.1 / 164.9    97.3 / 104.7   113.5 / 118.4 us
-    {7168, 2304, 13, 0, 1},   //  320.3 / 323.3   190.2 / 194.8   180.0 / 181.4 us
-    {7168, 2304, 13, 1, 1},   //  298.8 / 317.3   187.4 / 192.4   180.5 / 180.5 us
-    {7168, 2304, 14, 0, 1},   //  631.0 / 619.4   370.1 / 367.8   308.6 / 307.0 us
-    {7168, 2304, 14, 1, 1},   //  612.4 / 616.4   365.2 / 374.4   312.5 / 309.5 us
+    {1280, 8192, 7, 0, 0},   //   26.8 /  34.6    49.7 /  60.6    91.1 /  93.0 us
+    {1280, 8192, 7, 1, 0},   //   26.3 /  33.9    49.9 /  57.5    91.3 /  93.4 us
+    {1280, 8192, 8, 0, 0},   //   27.5 /  36.9    50.4 /  61.5    93.2 /  97.1 us
+    {1280, 8192, 8, 1, 0},   //   26.7 /  34.9    50.2 /  57.9    93.1 /  96.2 us
+    {1280, 8192, 9, 0, 0},   //   33.3 /  36.4    51.5 /  62.0   109.9 / 114.4 us
+    {1280, 8192, 9, 1, 0},   //   32.4 /  35.1    51.3 /  58.5   110.2 / 113.5 us
+    {1280, 8192, 10, 0, 0},   //   34.6 /  42.6    52.4 /  62.4   115.2 / 120.2 us
+    {1280, 8192, 10, 1, 0},   //   34.3 /  41.1    52.4 /  59.8   115.3 / 120.5 us
+    {1280, 8192, 11, 0, 2},   //   56.5 /  71.9    56.4 /  64.2   108.4 / 112.0 us
+    {1280, 8192, 11, 1, 2},   //   53.5 /  65.7    52.8 /  59.4   107.6 / 111.9 us
+    {1280, 8192, 12, 0, 2},   //  100.0 / 108.4    75.0 /  79.2   114.6 / 117.0 us
+    {1280, 8192, 12, 1, 2},   //   92.1 / 100.1    66.0 /  72.5   112.3 / 116.1 us
+    {1280, 8192, 13, 0, 1},   //  203.3 / 214.5   124.5 / 138.4   115.6 / 116.6 us
+    {1280, 8192, 13, 1, 1},   //  187.7 / 203.4   120.2 / 130.3   111.6 / 114.6 us
+    {1280, 8192, 14, 0, 1},   //  389.7 / 381.1   218.9 / 223.0   219.3 / 220.3 us
+    {1280, 8192, 14, 1, 2},   //  380.6 / 370.0   215.5 / 219.8   219.7 / 220.0 us
+    {2048, 7168, 7, 0, 0},   //   25.5 /  33.9    44.8 /  55.2    80.4 /  86.0 us
+    {2048, 7168, 7, 1, 0},   //   25.2 /  31.4    44.5 /  52.8    81.7 /  83.3 us
+    {2048, 7168, 8, 0, 0},   //   25.9 /  34.7    45.5 /  55.8    83.1 /  90.6 us
+    {2048, 7168, 8, 1, 0},   //   25.7 /  32.2    44.8 /  53.3    84.6 /  87.6 us
+    {2048, 7168, 9, 0, 0},   //   31.7 /  38.6    48.4 /  56.7   101.3 / 108.8 us
+    {2048, 7168, 9, 1, 0},   //   30.5 /  36.3    46.7 /  54.2   101.1 / 106.0 us
+    {2048, 7168, 10, 0, 2},   //   49.9 /  64.9    49.0 /  57.5   109.1 / 117.2 us
+    {2048, 7168, 10, 1, 2},   //   48.0 /  60.9    47.3 /  54.1   108.8 / 114.0 us
+    {2048, 7168, 11, 0, 2},   //   75.3 /  93.1    66.4 /  73.5   100.7 / 106.5 us
+    {2048, 7168, 11, 1, 2},   //   68.6 /  84.8    59.0 /  67.0    97.2 / 102.8 us
+    {2048, 7168, 12, 0, 2},   //  133.6 / 149.6   102.0 / 115.4   112.8 / 114.9 us
+    {2048, 7168, 12, 1, 2},   //  116.6 / 137.1    98.2 / 108.8   108.1 / 111.2 us
+    {2048, 7168, 13, 0, 1},   //  270.3 / 284.3   162.0 / 181.0   154.4 / 155.7 us
+    {2048, 7168, 13, 1, 1},   //  255.6 / 271.4   158.3 / 172.2   152.8 / 153.7 us
+    {2048, 7168, 14, 0, 1},   //  523.3 / 527.4   291.3 / 303.3   272.4 / 273.0 us
+    {2048, 7168, 14, 1, 1},   //  515.6 / 515.6   283.2 / 292.5   268.5 / 270.2 us
+    {4096, 4096, 7, 0, 0},   //   22.0 /  30.9    30.8 /  38.4    54.6 /  55.7 us
+    {4096, 4096, 7, 1, 0},   //   22.0 /  25.5    29.1 /  33.7    52.3 /  54.1 us
+    {4096, 4096, 8, 0, 0},   //   22.3 /  31.4    31.3 /  38.2    55.8 /  58.4 us
+    {4096, 4096, 8, 1, 0},   //   22.2 /  27.1    29.2 /  34.0    53.8 /  56.7 us
+    {4096, 4096, 9, 0, 2},   //   37.5 /  44.5    33.2 /  40.0    74.9 /  77.1 us
+    {4096, 4096, 9, 1, 2},   //   35.6 /  41.8    31.6 /  35.6    72.1 /  74.9 us
+    {4096, 4096, 10, 0, 2},   //   47.5 /  62.2    43.3 /  48.8    83.1 /  84.6 us
+    {4096, 4096, 10, 1, 2},   //   43.8 /  56.8    39.4 /  45.1    80.0 /  83.8 us
+    {4096, 4096, 11, 0, 2},   //   78.4 /  96.1    67.0 /  75.1    76.4 /  77.5 us
+    {4096, 4096, 11, 1, 2},   //   72.8 /  85.6    61.8 /  67.5    72.1 /  73.3 us
+    {4096, 4096, 12, 0, 2},   //  156.7 / 162.5    98.6 / 107.3   133.3 / 132.2 us
+    {4096, 4096, 12, 1, 2},   //  130.3 / 149.3    91.4 / 100.4   129.3 / 130.4 us
+    {4096, 4096, 13, 0, 1},   //  304.7 / 315.8   178.5 / 189.2   178.2 / 180.7 us
+    {4096, 4096, 13, 1, 2},   //  286.9 / 301.5   170.8 / 187.2   177.7 / 180.6 us
+    {4096, 4096, 14, 0, 1},   //  590.2 / 599.0   344.6 / 351.9   304.9 / 317.6 us
+    {4096, 4096, 14, 1, 1},   //  567.7 / 587.2   334.6 / 344.7   302.0 / 316.1 us
+    {7168, 2304, 7, 0, 2},   //   25.0 /  30.3    25.6 /  28.0    37.7 /  40.0 us
+    {7168, 2304, 7, 1, 2},   //   24.6 /  29.5    23.9 /  26.7    36.4 /  38.9 us
+    {7168, 2304, 8, 0, 2},   //   24.9 /  30.0    24.9 /  28.5    39.8 /  41.6 us
+    {7168, 2304, 8, 1, 2},   //   25.0 /  29.6    24.3 /  27.6    38.2 /  40.3 us
+    {7168, 2304, 9, 0, 2},   //   34.2 /  40.5    30.2 /  32.4    57.2 /  59.6 us
+    {7168, 2304, 9, 1, 2},   //   33.1 /  38.9    27.2 /  31.5    56.0 /  58.3 us
+    {7168, 2304, 10, 0, 2},   //   48.5 /  62.0    42.3 /  50.7    68.0 /  69.5 us
+    {7168, 2304, 10, 1, 2},   //   45.6 /  55.6    38.8 /  47.5    65.3 /  67.7 us
+    {7168, 2304, 11, 0, 2},   //   89.2 /  98.0    63.1 /  67.2    98.6 /  98.3 us
+    {7168, 2304, 11, 1, 2},   //   79.6 /  89.9    56.8 /  62.5    96.1 /  96.7 us
+    {7168, 2304, 12, 0, 2},   //  172.5 / 169.4    98.5 / 104.4   120.3 / 120.7 us
+    {7168, 2304, 12, 1, 2},   //  144.5 / 161.2    93.1 / 100.4   118.1 / 119.8 us
+    {7168, 2304, 13, 0, 1},   //  319.2 / 321.7   187.3 / 194.5   168.2 / 171.4 us
+    {7168, 2304, 13, 1, 1},   //  294.3 / 317.1   184.9 / 191.4   167.8 / 171.1 us
+    {7168, 2304, 14, 0, 1},   //  622.5 / 618.1   365.4 / 370.1   299.2 / 305.3 us
+    {7168, 2304, 14, 1, 1},   //  611.1 / 615.0   360.3 / 365.7   299.5 / 303.7 us
 };
 
 int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
@@ -490,18 +493,18 @@ int grouped_table_variant(int G, int64_t totM, int64_t N, int64_t K, int pre) {
 // static table above when it lists the shape, else the estimated time of
 // each kernel from upper bounds of the tile counts.
 //  - persistent, 64 x 64 or 128 x 128 tiles (weight streaming): ~0.8 or
-//    ~1.7 us per 128-K tile step per workgroup, GS_OCC workgroups per
+//    ~1.6 us per 128-K tile step per workgroup, GS_OCC workgroups per
 //    compute unit walking all tile steps evenly (the 128 x 128 kernel at
 //    least ~1.1 us per K step: a tile's time when its workgroup has the
 //    compute unit to itself);
 //  - persistent 256 x 256 tiles on the dense pipeline (matrix-core regime):
 //    one tile per compute unit per round, ~1.67 us per 128-K step plus
 //    ~20 us per round (pipeline start, epilogue); a partial last round that
-//    goes to the streaming kernel (grouped_split_end) ~1.15 us per 128-K
-//    step plus ~5 us per round of its 128 x 64 pieces;
+//    goes to the streaming kernel (grouped_split_end) ~0.55 us per 128-K
+//    step plus ~5 us per round of its pieces (one per compute unit);
 // each at least the weights' bytes at ~5 TB/s.  The constants are fitted to
-// the table's warm-plus-cold times; at 57 of its 64 points the estimate
-// picks the table's kernel, and at the other 7 one within 11% of it.
+// the table's warm-plus-cold times; at 58 of its 64 points the estimate
+// picks the table's kernel, and at the other 6 one within 12% of it.
 namespace {
 // Autotuned winners of the grouped GEMM, keyed as "Add FlyDSL grouped
 // groupwise FP8 GEMM for ROCm" (Tile selection) keys its persisted cache:
@@ -554,15 +557,16 @@ int grouped_model_variant(int G, int64_t totM, int64_t N, int64_t kbytes) {
   const double wmin = wbytes / 5.0e6;
   const double slots = (double)GS_OCC * cus;
   const double t64 = std::max(0.8 * (double)(cdiv(totM, 64) + G - 1) * (double)(N / 64) * nst / slots, wmin);
-  const double t128 = std::max(std::max(1.7 * (double)(cdiv(totM, 128) + G - 1) * (double)(N / 128) * nst / slots,
+  const double t128 = std::max(std::max(1.6 * (double)(cdiv(totM, 128) + G - 1) * (double)(N / 128) * nst / slots,
                                         1.1 * nst), wmin);
   const double tiles_d = (double)(cdiv(totM, DBM) + G - 1) * (double)cdiv(N, DBN);
   const double round_d = 1.67 * nst + 20.0;
   const double full = std::floor(tiles_d / cus), r = tiles_d - full * cus;
   double t_d = full * round_d;
   if (r > 0) {
-    const double pr = std::ceil(8.0 * r / slots);     // streaming rounds of the tail's pieces
-    t_d += (full >= 1 && pr <= GROUPED_TAIL_ROUNDS) ? pr * (1.15 * nst + 5.0) : round_d;
+    const double pieces = (16.0 * r <= cus ? 16.0 : 8.0) * r;   // grouped_tail_pieces
+    const double pr = std::ceil(pieces / cus);                   // streaming rounds of them
+    t_d += (full >= 1 && pr <= GROUPED_TAIL_ROUNDS) ? pr * (0.55 * nst + 5.0) : round_d;
   }
   t_d = std::max(t_d, wmin);
   if (t64 <= t128 && t64 <= t_d) return MXG_GROUPED_STREAM64;
@@ -817,7 +821,7 @@ extern "C" int grouped_bf16_gemm_run(int G, const int64_t *m_sizes, const void *
   if (tiles > 0x7FFFFFFF) return MXG_ERR_UNSUPPORTED;
   const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
   const bool tail = tiles > (int64_t)grid;
-  const unsigned tail_grid = (unsigned)(GS_OCC * cu_count());
+  const unsigned tail_grid = (unsigned)cu_count();
   d.tail_grid = (int)tail_grid;
   d.tail_rounds = tail ? GROUPED_TAIL_ROUNDS : 0;
   hipLaunchKernelGGL(pick_grouped_bf16(pre), dim3(grid), dim3(DNW8 * 64), 0, stream, d);

@@ -27,10 +27,10 @@ grouped_fn pick_grouped_stream_bf16(int bm, int bn, bool psb) {
 }
 
 grouped_fn pick_grouped_tail_bf16(bool psb) {
-  return psb ? grouped_stream_kernel<true, 128, 64, 1, 2, true, F_BF16> : grouped_stream_kernel<false, 128, 64, 1, 2, true, F_BF16>;
+  return psb ? grouped_stream_kernel<true, 128, 64, 2, 2, true, F_BF16> : grouped_stream_kernel<false, 128, 64, 2, 2, true, F_BF16>;
 }
 
 grouped_fn pick_grouped_tail(bool psb) {
-  return psb ? grouped_stream_kernel<true, 128, 64, 1, 2, true> : grouped_stream_kernel<false, 128, 64, 1, 2, true>;
+  return psb ? grouped_stream_kernel<true, 128, 64, 2, 2, true> : grouped_stream_kernel<false, 128, 64, 2, 2, true>;
 }
 }  // namespace mxg

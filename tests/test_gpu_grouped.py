@@ -377,7 +377,8 @@ def test_grouped_tiled_tail_pieces(preshuffled, tmp_path):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nb = row_tiles * 5
     if cus == 256:
-        assert nb % cus == 44 and (8 * 44 + 2 * cus - 1) // (2 * cus) <= 2
+        pieces = (16 if 16 * 44 <= cus else 8) * 44      # the tail kernel: one workgroup per CU
+        assert nb % cus == 44 and (pieces + cus - 1) // cus <= 2
     m_sizes, XQ, xs, WQ, ws, totM = _inputs(951, split, N, K)
     try:
         _force_variant(mxgemm, tmp_path / "tiled.txt", G, totM, N, K, mxgemm.GROUPED_TILED)
@@ -458,7 +459,8 @@ def test_grouped_tiled_random_shapes_match_streaming(tmp_path):
         nb = row_tiles * tiles_n
         grid = min(((totM + 255) // 256 + G - 1) * tiles_n, cus)
         r = nb % grid
-        split = nb > grid and r > 0 and (8 * r + 2 * cus - 1) // (2 * cus) <= 2
+        pieces = (16 if 16 * r <= cus else 8) * r
+        split = nb > grid and r > 0 and (pieces + cus - 1) // cus <= 2
         if nb <= grid:
             continue
         split_seen[split] += 1
