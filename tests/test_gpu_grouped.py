@@ -431,6 +431,43 @@ def test_grouped_tiled_tail_pieces_integer_valued_bit_exact(tmp_path):
     assert np.array_equal(bits[im, inn], oracle.bf16_rne(ref))
 
 
+@pytest.mark.parametrize("preshuffled", [False, True])
+def test_grouped_tiled_tail_64_row_pieces_bit_exact(preshuffled, tmp_path):
+    """A last round of 12 tiles of the 256 x 256 kernel (on 256 compute
+    units; N = 256, 268 row tiles): sixteen 64 x 64 pieces per tile, the
+    lower half of each tail tile empty, groups ending inside a piece and one
+    single-row group.  Integer-valued codes and power-of-two scales (every
+    partial sum exact in FP32): every entry equals the oracle's bit for
+    bit, and every row is written."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 256, 256
+    split = [20000, 1, 0, 30030, 17800]
+    G = len(split)
+    m_sizes = np.asarray(split, np.int64)
+    totM = int(m_sizes.sum())
+    row_tiles = sum((m + 255) // 256 for m in split)
+    assert row_tiles == 268
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:
+        r = row_tiles % cus
+        assert r == 12 and 16 * r <= cus      # the tail grid is one workgroup per CU
+    rng = np.random.default_rng(268)
+    vals = np.array([0xC0, 0xB8, 0x00, 0x38, 0x40], np.uint8)
+    XQ = vals[rng.integers(0, 5, (totM, K), dtype=np.uint8)]
+    WQ = vals[rng.integers(0, 5, (G, N, K), dtype=np.uint8)]
+    xs = (2.0 ** rng.integers(0, 3, totM * K // 128)).astype(np.float32)
+    ws = (2.0 ** rng.integers(0, 3, (G, N // 128, K // 128))).astype(np.float32)
+    D = _run_forced(tmp_path, mxgemm.GROUPED_TILED, m_sizes, XQ, xs, WQ, ws, totM, N, K, preshuffled)
+    bits = H.bits(D.view(torch.bfloat16))
+    assert not np.any(bits == SENTINEL_BITS)
+    if "tail64" not in _ORACLE_CACHE:         # the same inputs for both weight layouts
+        _ORACLE_CACHE["tail64"] = oracle.bf16_rne(oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K))
+    assert np.array_equal(bits, _ORACLE_CACHE["tail64"])
+
+
+_ORACLE_CACHE = {}
+
+
 def test_grouped_tiled_random_shapes_match_streaming(tmp_path):
     """Random group counts (1..64) and sizes (some empty), N an odd or even
     multiple of 128, K from 256 to 1024, rows past the last group, sized so
