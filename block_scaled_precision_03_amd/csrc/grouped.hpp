@@ -70,7 +70,8 @@ __device__ inline int grouped_split_end(int nb, int P, int P_tail, int max_round
 //   major and M-tile minor, so that consecutive tiles share one weight tile.
 //   Each workgroup finds a tile's group by binary search in a table of the
 //   groups' first rows and first tiles that wave 0 builds in LDS once.
-// * Persistent grid of P workgroups, two per compute unit: each walks one
+// * Persistent grid of P workgroups, two per compute unit (one for the
+//   tail of the 256 x 256 kernel, with two K steps per stage): each walks one
 //   tile of every round of P consecutive tiles; within a round each XCD (one
 //   L2) takes a contiguous band of tiles, the eight bands as even as the
 //   round allows, so tiles that read the same weights at the same time
