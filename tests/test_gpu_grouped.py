@@ -468,6 +468,37 @@ def test_grouped_tiled_tail_64_row_pieces_bit_exact(preshuffled, tmp_path):
 _ORACLE_CACHE = {}
 
 
+@pytest.mark.parametrize("variant", ["stream64", "stream128", "tiled"])
+def test_grouped_single_k_step_every_kernel(variant, tmp_path):
+    """K = 128, one K step, on each kernel: the 64 x 64 kernel's two-step
+    stages and the tail kernel's hold one live step and one that reads
+    zeros.  N = 384 (the 256 x 256 kernel's last column tile half real),
+    uneven groups (one empty, one single row); on 256 compute units the
+    256 x 256 kernel has 276 tiles and hands a last round of 20 to the tail
+    kernel.  Integer-valued codes and power-of-two scales: every entry
+    equals the oracle's bit for bit, every row written."""
+    from block_scaled_precision_03_amd import mxgemm
+    N, K = 384, 128
+    split = [10000, 0, 1, 14000, 10500]
+    G = len(split)
+    m_sizes = np.asarray(split, np.int64)
+    totM = int(m_sizes.sum())
+    rng = np.random.default_rng(128)
+    vals = np.array([0xC0, 0xB8, 0x00, 0x38, 0x40], np.uint8)
+    XQ = vals[rng.integers(0, 5, (totM, K), dtype=np.uint8)]
+    WQ = vals[rng.integers(0, 5, (G, N, K), dtype=np.uint8)]
+    xs = (2.0 ** rng.integers(0, 3, totM * K // 128)).astype(np.float32)
+    ws = (2.0 ** rng.integers(0, 3, (G, N // 128, K // 128))).astype(np.float32)
+    v = {"stream64": mxgemm.GROUPED_STREAM64, "stream128": mxgemm.GROUPED_STREAM128,
+         "tiled": mxgemm.GROUPED_TILED}[variant]
+    D = _run_forced(tmp_path, v, m_sizes, XQ, xs, WQ, ws, totM, N, K, True)
+    bits = H.bits(D.view(torch.bfloat16))
+    assert not np.any(bits == SENTINEL_BITS)
+    if "k1" not in _ORACLE_CACHE:             # the same inputs for every kernel
+        _ORACLE_CACHE["k1"] = oracle.bf16_rne(oracle.grouped_gemm(m_sizes, XQ, xs, WQ, ws, totM, N, K))
+    assert np.array_equal(bits, _ORACLE_CACHE["k1"])
+
+
 def test_grouped_tiled_random_shapes_match_streaming(tmp_path):
     """Random group counts (1..64) and sizes (some empty), N an odd or even
     multiple of 128, K from 256 to 1024, rows past the last group, sized so
