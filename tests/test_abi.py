@@ -283,3 +283,35 @@ def test_tune_cache_io_errors(tmp_path):
     assert lib.mxgemm_tune_cache_load(str(tmp_path / "missing.txt").encode()) == -5
     assert lib.mxgemm_tune_cache_save(str(tmp_path / "no_dir" / "x.txt").encode()) == -5
     assert m.status_string(-5)
+
+
+def _tile_table():
+    """The static grouped tile table of the library source: (N, K, log2m,
+    preshuffled, variant, {variant: warm + cold us}) per entry."""
+    src = open(os.path.join(ROOT, "block_scaled_precision_03_amd", "csrc", "api.hip")).read()
+    body = src[src.index("GROUPED_TILES[] = {"):]
+    body = body[:body.index("};")]
+    rows = []
+    for m in re.finditer(r"\{(\d+), (\d+), (\d+), (\d+), (\d+)\},\s*//\s*([\d.]+) /\s*([\d.]+)\s+([\d.]+) /\s*([\d.]+)"
+                         r"\s+([\d.]+) /\s*([\d.]+) us", body):
+        N, K, lg, pre, v = (int(x) for x in m.groups()[:5])
+        w64, c64, w128, c128, wt, ct = (float(x) for x in m.groups()[5:])
+        # the times are listed 64 x 64, 128 x 128, 256 x 256; variant ids 0, 2, 1
+        rows.append((N, K, lg, pre, v, {0: w64 + c64, 2: w128 + c128, 1: wt + ct}))
+    return rows, body.count("},")
+
+
+def test_grouped_tile_table_entries_pick_the_least_warm_plus_cold_time():
+    """Every entry of the static table names the kernel with the least warm
+    plus cold time among the three times recorded beside it, covers both
+    weight layouts of each (N, K, log2m) key once, and the library answers
+    with it."""
+    rows, count = _tile_table()
+    assert len(rows) == count == 64
+    keys = {(N, K, lg, pre) for N, K, lg, pre, _, _ in rows}
+    assert len(keys) == 64
+    for N, K, lg, pre, v, cost in rows:
+        assert v == min(cost, key=cost.get), (N, K, lg, pre)
+    m = _mx()
+    for N, K, lg, pre, v, _ in rows:
+        assert m.grouped_variant(8, 1 << lg, N, K, bool(pre)) == v, (N, K, lg, pre)
